@@ -1,0 +1,401 @@
+/*
+ * sgmv_oracle.c -- plain fp64 CPU oracle for SGMV expand-slice.
+ *
+ * TEST INFRASTRUCTURE ONLY (see sgmv_oracle.h).  Nothing here is tuned:
+ * the computation is the definition written out as loops, parallel over
+ * output rows only (rows are independent).  Build without fast-math and
+ * with -ffp-contract=off.
+ *
+ * Definition followed (wiki page "Implementation: Predibase Lorax SGMV
+ * Expand Slice Kernel"):
+ *   - Description: for segment b and token m, row start_b + m of the output
+ *     slice is updated with input[start_b + m] times lora_B[idx[b]].
+ *   - I/O Contract, Inputs: lora_B is (lora_num, slice_size, rank), so the
+ *     contraction runs over rank: y[n] = sum_k x[k] * B[a][n][k];
+ *     b_seq_start_loc gives each segment's first row, seq_len_tensor its
+ *     length; lora index -1 means no LoRA is applied (rows untouched);
+ *     add_inputs=false (default) overwrites, true accumulates.
+ *   - Description / Signature (CAST_TYPE, "mixed-precision type casting"):
+ *     float32 inputs are rounded to the 16-bit weight type before the
+ *     products.
+ * Readings where the page is silent are listed beside the code below.
+ */
+#include "sgmv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------------- */
+/* IEEE 754 binary formats: exponent field width and trailing significand  */
+/* width.  bfloat16 keeps binary32's exponent with a 7-bit significand.     */
+/* ---------------------------------------------------------------------- */
+static int format_of(int dtype, int* ebits, int* mbits) {
+  switch (dtype) {
+    case ORC_F16:  *ebits = 5; *mbits = 10; return 1;
+    case ORC_BF16: *ebits = 8; *mbits = 7;  return 1;
+    case ORC_F32:  *ebits = 8; *mbits = 23; return 1;
+    default: return 0;
+  }
+}
+
+double orc_decode(int dtype, uint32_t bits) {
+  int eb, mb;
+  if (!format_of(dtype, &eb, &mb)) return NAN;
+  const int bias = (1 << (eb - 1)) - 1;
+  const uint32_t emask = (1u << eb) - 1u;
+  const uint32_t sign = (bits >> (eb + mb)) & 1u;
+  const uint32_t e = (bits >> mb) & emask;
+  const uint32_t m = bits & ((1u << mb) - 1u);
+  double mag;
+  if (e == emask) {
+    mag = m ? NAN : INFINITY;
+  } else if (e == 0) {
+    /* subnormal: 0.m * 2^(1 - bias) */
+    mag = ldexp((double)m, 1 - bias - mb);
+  } else {
+    /* normal: 1.m * 2^(e - bias) */
+    mag = ldexp((double)((1u << mb) + m), (int)e - bias - mb);
+  }
+  return sign ? -mag : mag;
+}
+
+uint32_t orc_encode(int dtype, double v) {
+  int eb, mb;
+  if (!format_of(dtype, &eb, &mb)) return 0;
+  const int bias = (1 << (eb - 1)) - 1;
+  const uint32_t emask = (1u << eb) - 1u;
+  const uint32_t sbit = (signbit(v) ? 1u : 0u) << (eb + mb);
+  if (isnan(v)) return sbit | (emask << mb) | (1u << (mb - 1));
+  const double a = fabs(v);
+  if (isinf(a)) return sbit | (emask << mb);
+  if (a == 0.0) return sbit;
+
+  const int emin = 1 - bias;          /* exponent of the smallest normal   */
+  int e2;
+  (void)frexp(a, &e2);                /* a = f * 2^e2, 0.5 <= f < 1         */
+  const int ea = e2 - 1;              /* floor(log2(a))                     */
+  /* Spacing of the representable values around a: 2^(max(ea, emin) - mb). */
+  const int qexp = (ea < emin ? emin : ea) - mb;
+  const double scaled = ldexp(a, -qexp);   /* exact (power-of-two scaling)  */
+  double r = floor(scaled);
+  const double frac = scaled - r;          /* exact: scaled < 2^(mb + 1)    */
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;  /* ties to even */
+  uint64_t ri = (uint64_t)r;
+
+  uint32_t field, mant;
+  if (ea < emin) {
+    /* Subnormal range; rounding up to 2^mb reaches the smallest normal. */
+    if (ri == (1ull << mb)) { field = 1; mant = 0; }
+    else { field = 0; mant = (uint32_t)ri; }
+  } else {
+    int eu = ea;
+    if (ri == (2ull << mb)) { eu += 1; ri = 1ull << mb; }   /* carry into next binade */
+    if (eu > bias) return sbit | (emask << mb);            /* overflow -> infinity   */
+    field = (uint32_t)(eu + bias);
+    mant = (uint32_t)(ri - (1ull << mb));
+  }
+  return sbit | (field << mb) | mant;
+}
+
+void orc_decode_array(int dtype, const uint32_t* bits, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_decode(dtype, bits[i]);
+}
+
+void orc_encode_array(int dtype, const double* v, uint32_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_encode(dtype, v[i]);
+}
+
+static uint32_t load_bits(int dtype, const void* base, int64_t i) {
+  if (dtype == ORC_F32) {
+    uint32_t b;
+    memcpy(&b, (const char*)base + 4 * i, 4);
+    return b;
+  }
+  uint16_t h;
+  memcpy(&h, (const char*)base + 2 * i, 2);
+  return h;
+}
+
+static void store_bits(int dtype, void* base, int64_t i, uint32_t bits) {
+  if (dtype == ORC_F32) {
+    memcpy((char*)base + 4 * i, &bits, 4);
+  } else {
+    uint16_t h = (uint16_t)bits;
+    memcpy((char*)base + 2 * i, &h, 2);
+  }
+}
+
+int orc_threads(int threads) {
+#ifdef _OPENMP
+  return threads > 0 ? threads : omp_get_max_threads();
+#else
+  (void)threads;
+  return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------------- */
+/* Argument checks and the row -> segment map.                             */
+/* ---------------------------------------------------------------------- */
+static int check_args(const orc_slice* s, int ns, int64_t K, int64_t L, int out_dtype,
+                      int64_t T, int64_t H, int64_t out_stride, int64_t batches) {
+  int eb, mb;
+  if (!s || ns < 1 || K < 1 || L < 0 || T < 0 || H < 0 || out_stride < H || batches < 0)
+    return ORC_BAD_ARGUMENT;
+  if (!format_of(out_dtype, &eb, &mb)) return ORC_BAD_ARGUMENT;
+  for (int i = 0; i < ns; ++i) {
+    /* Weights are float16 or bfloat16; inputs are the weight type or
+     * float32 (I/O Contract, Inputs).  A 16-bit input of the other 16-bit
+     * type is not a case the page describes and is rejected. */
+    if (s[i].w_dtype != ORC_F16 && s[i].w_dtype != ORC_BF16) return ORC_BAD_ARGUMENT;
+    if (s[i].x_dtype != s[i].w_dtype && s[i].x_dtype != ORC_F32) return ORC_BAD_ARGUMENT;
+    if (s[i].N < 0 || s[i].offset < 0 || s[i].offset + s[i].N > H) return ORC_BAD_ARGUMENT;
+    if (s[i].x_stride < K) return ORC_BAD_ARGUMENT;
+    for (int j = 0; j < i; ++j) {
+      if (s[i].N == 0 || s[j].N == 0) continue;
+      if (s[i].offset < s[j].offset + s[j].N && s[j].offset < s[i].offset + s[i].N)
+        return ORC_BAD_ARGUMENT;  /* overlapping column windows */
+    }
+  }
+  return ORC_OK;
+}
+
+/* owner[t] = segment that writes row t, or -1.  A segment is active when its
+ * adapter index is not -1 and its length is positive.  Active segments must
+ * lie inside [0, T) and be pairwise disjoint. */
+static int build_owner(int64_t T, int64_t L, const int64_t* start, const int64_t* lens,
+                       const int64_t* idx, int64_t batches, int64_t** owner_out) {
+  int64_t* owner = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+  if (!owner) return ORC_NO_MEMORY;
+  for (int64_t t = 0; t < T; ++t) owner[t] = -1;
+  for (int64_t b = 0; b < batches; ++b) {
+    if (lens[b] < 0) { free(owner); return ORC_BAD_SEGMENT; }
+    if (idx[b] < -1 || idx[b] >= L) { free(owner); return ORC_BAD_INDEX; }
+    if (idx[b] == -1 || lens[b] == 0) continue;  /* no LoRA, or nothing to do */
+    if (start[b] < 0 || start[b] > T - lens[b]) { free(owner); return ORC_BAD_SEGMENT; }
+    for (int64_t m = 0; m < lens[b]; ++m) {
+      if (owner[start[b] + m] != -1) { free(owner); return ORC_BAD_SEGMENT; }
+      owner[start[b] + m] = b;
+    }
+  }
+  *owner_out = owner;
+  return ORC_OK;
+}
+
+/* Exact values of a whole (L, N, K) weight stack. */
+static double* decode_stack(const orc_slice* s, int64_t K, int64_t L) {
+  const int64_t n = L * s->N * K;
+  double* w = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  if (!w) return NULL;
+  for (int64_t i = 0; i < n; ++i) w[i] = orc_decode(s->w_dtype, load_bits(s->w_dtype, s->w, i));
+  return w;
+}
+
+/* Value of input element x[t][k] as it enters the product: float32 inputs
+ * are first rounded to the weight type (CAST_TYPE). */
+static double input_value(const orc_slice* s, int64_t t, int64_t k) {
+  const double v = orc_decode(s->x_dtype, load_bits(s->x_dtype, s->x, t * s->x_stride + k));
+  if (s->x_dtype == ORC_F32) return orc_decode(s->w_dtype, orc_encode(s->w_dtype, v));
+  return v;
+}
+
+/* Exact (fp64) slice value for row t, column n: the prior value when
+ * accumulating, plus the dot product over rank.  Products of 16-bit values
+ * are exact in fp64; the sum carries at most ~K ulp(fp64) of error. */
+static double slice_value(const orc_slice* s, const double* wval, const double* xrow,
+                          int64_t K, int64_t a, int64_t n, int add, double prior) {
+  double r = add ? prior : 0.0;
+  const double* wrow = wval + (a * s->N + n) * K;
+  for (int64_t k = 0; k < K; ++k) r += xrow[k] * wrow[k];
+  return r;
+}
+
+int orc_expand(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
+               void* out, int out_dtype, int64_t T, int64_t H, int64_t out_stride,
+               const int64_t* start, const int64_t* lens, const int64_t* idx,
+               int64_t batches, int add_inputs, double* ref, int threads) {
+  int rc = check_args(slices, num_slices, K, L, out_dtype, T, H, out_stride, batches);
+  if (rc != ORC_OK) return rc;
+  int64_t* owner = NULL;
+  rc = build_owner(T, L, start, lens, idx, batches, &owner);
+  if (rc != ORC_OK) return rc;
+  const int nt = orc_threads(threads);
+
+  int64_t ref_base = 0;
+  for (int si = 0; si < num_slices; ++si) {
+    const orc_slice* s = &slices[si];
+    double* wval = decode_stack(s, K, L);
+    if (!wval) { free(owner); return ORC_NO_MEMORY; }
+    int failed = 0;
+#pragma omp parallel num_threads(nt)
+    {
+      double* xrow = (double*)malloc(sizeof(double) * (size_t)K);
+      if (!xrow) {
+#pragma omp atomic write
+        failed = 1;
+      }
+#pragma omp for schedule(static)
+      for (int64_t t = 0; t < T; ++t) {
+        if (!xrow) continue;
+        const int64_t b = owner[t];
+        if (b < 0) continue;  /* not in an active segment: untouched */
+        const int64_t a = idx[b];
+        for (int64_t k = 0; k < K; ++k) xrow[k] = input_value(s, t, k);
+        for (int64_t n = 0; n < s->N; ++n) {
+          const int64_t o = t * out_stride + s->offset + n;
+          const double prior = add_inputs ? orc_decode(out_dtype, load_bits(out_dtype, out, o)) : 0.0;
+          const double r = slice_value(s, wval, xrow, K, a, n, add_inputs, prior);
+          if (ref) ref[ref_base + t * s->N + n] = r;
+          store_bits(out_dtype, out, o, orc_encode(out_dtype, r));
+        }
+      }
+      free(xrow);
+    }
+    free(wval);
+    if (failed) { free(owner); return ORC_NO_MEMORY; }
+    ref_base += T * s->N;
+  }
+  free(owner);
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Streaming comparator.                                                    */
+/* ---------------------------------------------------------------------- */
+static int is_nonfinite_bits(int dtype, uint32_t bits) {
+  int eb = 0, mb = 0;
+  if (!format_of(dtype, &eb, &mb)) return 1;
+  const uint32_t emask = (1u << eb) - 1u;
+  return ((bits >> mb) & emask) == emask;
+}
+
+static int is_nan_bits(int dtype, uint32_t bits) {
+  int eb = 0, mb = 0;
+  if (!format_of(dtype, &eb, &mb)) return 1;
+  return is_nonfinite_bits(dtype, bits) && (bits & ((1u << mb) - 1u)) != 0;
+}
+
+static void note_bad(orc_report* r, int64_t row, int64_t col) {
+  if (r->first_bad_row < 0 || row < r->first_bad_row ||
+      (row == r->first_bad_row && col < r->first_bad_col)) {
+    r->first_bad_row = row;
+    r->first_bad_col = col;
+  }
+}
+
+int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
+              const void* prior, const void* cand, int out_dtype,
+              int64_t T, int64_t H, int64_t out_stride,
+              const int64_t* start, const int64_t* lens, const int64_t* idx,
+              int64_t batches, int add_inputs, double atol, double rtol,
+              const int64_t* rows, int64_t num_rows, int threads,
+              orc_report* report) {
+  if (!report) return ORC_BAD_ARGUMENT;
+  int rc = check_args(slices, num_slices, K, L, out_dtype, T, H, out_stride, batches);
+  if (rc != ORC_OK) return rc;
+  if (rows) {
+    for (int64_t i = 0; i < num_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= T) return ORC_BAD_ARGUMENT;
+  }
+  int64_t* owner = NULL;
+  rc = build_owner(T, L, start, lens, idx, batches, &owner);
+  if (rc != ORC_OK) return rc;
+
+  double** wval = (double**)calloc((size_t)num_slices, sizeof(double*));
+  if (!wval) { free(owner); return ORC_NO_MEMORY; }
+  for (int si = 0; si < num_slices; ++si) {
+    wval[si] = decode_stack(&slices[si], K, L);
+    if (!wval[si]) rc = ORC_NO_MEMORY;
+  }
+  /* column -> slice map for one row (-1 = outside every slice) */
+  int* col_slice = (int*)malloc(sizeof(int) * (size_t)(H > 0 ? H : 1));
+  if (!col_slice) rc = ORC_NO_MEMORY;
+  if (rc != ORC_OK) {
+    for (int si = 0; si < num_slices; ++si) free(wval[si]);
+    free(wval); free(col_slice); free(owner);
+    return rc;
+  }
+  for (int64_t c = 0; c < H; ++c) col_slice[c] = -1;
+  for (int si = 0; si < num_slices; ++si)
+    for (int64_t n = 0; n < slices[si].N; ++n) col_slice[slices[si].offset + n] = si;
+
+  orc_report total;
+  memset(&total, 0, sizeof total);
+  total.first_bad_row = total.first_bad_col = -1;
+  const int64_t nrows = rows ? num_rows : T;
+  const int nt = orc_threads(threads);
+  int failed = 0;
+
+#pragma omp parallel num_threads(nt)
+  {
+    orc_report mine;
+    memset(&mine, 0, sizeof mine);
+    mine.first_bad_row = mine.first_bad_col = -1;
+    double* xrows = (double*)malloc(sizeof(double) * (size_t)(K * num_slices));
+    if (!xrows) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+      if (!xrows) continue;
+      const int64_t t = rows ? rows[i] : i;
+      const int64_t b = owner[t];
+      if (b >= 0)
+        for (int si = 0; si < num_slices; ++si)
+          for (int64_t k = 0; k < K; ++k) xrows[si * K + k] = input_value(&slices[si], t, k);
+      for (int64_t c = 0; c < H; ++c) {
+        const int64_t o = t * out_stride + c;
+        const uint32_t cb = load_bits(out_dtype, cand, o);
+        const uint32_t pb = load_bits(out_dtype, prior, o);
+        const int si = col_slice[c];
+        if (b < 0 || si < 0) {
+          /* untouched region: bit-identical to the prior output */
+          mine.checked_untouched++;
+          if (cb != pb) { mine.bad_untouched++; note_bad(&mine, t, c); }
+          continue;
+        }
+        const orc_slice* s = &slices[si];
+        const double r = slice_value(s, wval[si], xrows + si * K, K, idx[b],
+                                     c - s->offset, add_inputs, orc_decode(out_dtype, pb));
+        const uint32_t rb = orc_encode(out_dtype, r);
+        mine.checked_values++;
+        if (is_nonfinite_bits(out_dtype, rb)) {
+          const int ok = is_nan_bits(out_dtype, rb) ? is_nan_bits(out_dtype, cb) : (cb == rb);
+          if (!ok) { mine.bad_values++; note_bad(&mine, t, c); }
+          continue;
+        }
+        const double cv = orc_decode(out_dtype, cb);
+        if (!isfinite(cv)) { mine.bad_values++; note_bad(&mine, t, c); continue; }
+        const double err = fabs(cv - r);
+        const double allowed = atol + rtol * fabs(r);
+        if (err > mine.max_abs_err) mine.max_abs_err = err;
+        if (err / allowed > mine.max_tol_ratio) mine.max_tol_ratio = err / allowed;
+        if (!(err <= allowed)) { mine.bad_values++; note_bad(&mine, t, c); }
+      }
+    }
+    free(xrows);
+#pragma omp critical
+    {
+      total.checked_values += mine.checked_values;
+      total.checked_untouched += mine.checked_untouched;
+      total.bad_values += mine.bad_values;
+      total.bad_untouched += mine.bad_untouched;
+      if (mine.max_abs_err > total.max_abs_err) total.max_abs_err = mine.max_abs_err;
+      if (mine.max_tol_ratio > total.max_tol_ratio) total.max_tol_ratio = mine.max_tol_ratio;
+      if (mine.first_bad_row >= 0) note_bad(&total, mine.first_bad_row, mine.first_bad_col);
+    }
+  }
+
+  for (int si = 0; si < num_slices; ++si) free(wval[si]);
+  free(wval);
+  free(col_slice);
+  free(owner);
+  if (failed) return ORC_NO_MEMORY;
+  *report = total;
+  return ORC_OK;
+}

@@ -1,0 +1,268 @@
+"""Seeded synthetic inputs for SGMV expand-slice.
+
+This module only draws inputs: segment metadata, weights, inputs and the
+prior output.  It holds none of the operation's arithmetic and is shared by
+the oracle side (tests) and the GPU side (tests, benchmark) so that both see
+the same bits.
+
+Storage: 16-bit values are numpy ``uint16`` bit patterns, float32 values are
+``float32``.  Normals are drawn in float32 as ``rng.standard_normal * sigma``
+and rounded once to the storage type (numpy's float16 cast, torch's bfloat16
+cast; both round to nearest even).
+
+The five named workloads follow the shapes the SGMV expand-slice wiki page's
+usage describes (fused QKV and gate/up slices, packed variable-length
+prefill segments, index -1 for "no LoRA"); their sizes, distributions and
+draw order are fixed here:
+
+    seq_lens -> (placement) -> lora_indices -> lora_B per slice
+             -> inputs per slice -> prior output
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+
+DTYPE_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
+
+
+def _to_storage(values_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 draws to the storage dtype (round to nearest even)."""
+    values_f32 = np.asarray(values_f32, dtype=np.float32)
+    if dtype == "f32":
+        return np.ascontiguousarray(values_f32)
+    if dtype == "f16":
+        return np.ascontiguousarray(values_f32.astype(np.float16).view(np.uint16))
+    if dtype == "bf16":
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(values_f32)).to(torch.bfloat16)
+        return np.ascontiguousarray(t.view(torch.int16).numpy().view(np.uint16))
+    raise ValueError(dtype)
+
+
+def normal(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarray:
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        v = v * np.float32(sigma)
+    return _to_storage(v, dtype)
+
+
+def integers_as(rng: np.random.Generator, shape, lo: int, hi: int, dtype: str) -> np.ndarray:
+    """Small integers in [lo, hi] stored exactly in ``dtype``."""
+    v = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return _to_storage(v, dtype)
+
+
+@dataclass
+class SliceInput:
+    x: np.ndarray          # (T, K) or wider rows (row stride >= K)
+    x_dtype: str
+    w: np.ndarray          # (L, N, K) contiguous
+    w_dtype: str
+    offset: int
+
+    @property
+    def N(self) -> int:
+        return int(self.w.shape[1])
+
+
+@dataclass
+class Workload:
+    name: str
+    slices: List[SliceInput]
+    out0: np.ndarray       # (T, H) prior output
+    out_dtype: str
+    start: np.ndarray      # int64 [B]  (b_seq_start_loc)
+    lens: np.ndarray       # int64 [B]  (seq_len_tensor)
+    idx: np.ndarray        # int64 [B]  (lora_indices_tensor)
+    add: bool
+    K: int
+    L: int
+    seed: int = 0
+    notes: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return int(self.out0.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.out0.shape[1])
+
+    @property
+    def batches(self) -> int:
+        return int(len(self.lens))
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.lens.max()) if len(self.lens) else 0
+
+    def active_mask(self) -> np.ndarray:
+        return (self.idx != -1) & (self.lens > 0)
+
+
+def exclusive_cumsum(lens: Sequence[int]) -> np.ndarray:
+    """Start rows of packed segments: [4, 6] -> [0, 4]."""
+    lens = np.asarray(lens, dtype=np.int64)
+    out = np.zeros_like(lens)
+    if len(lens) > 1:
+        out[1:] = np.cumsum(lens)[:-1]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.
+# ---------------------------------------------------------------------------
+
+def tiny_ref(seed: int = 0) -> Workload:
+    """2 sequences of lengths [4, 6] (starts [0, 4]); rank 8; 2 adapters;
+    lora_B (2, 64, 8) fp16 N(0, 0.02); input (10, 8) fp16 N(0, 1); output
+    (10, 192) fp16 prefilled N(0, 1); slice [64, 128); indices [1, -1];
+    overwrite."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([4, 6], dtype=np.int64)
+    idx = np.array([1, -1], dtype=np.int64)
+    K, N, H, L, off = 8, 64, 192, 2, 64
+    T = int(lens.sum())
+    w = normal(rng, (L, N, K), 0.02, "f16")
+    x = normal(rng, (T, K), 1.0, "f16")
+    out0 = normal(rng, (T, H), 1.0, "f16")
+    return Workload("tiny_ref", [SliceInput(x, "f16", w, "f16", off)], out0, "f16",
+                    exclusive_cumsum(lens), lens, idx, False, K, L, seed)
+
+
+def llama7b_q_proj(seed: int = 0) -> Workload:
+    """Single slice, Llama-7B-like q_proj: 8 sequences with lengths uniform in
+    [64, 512]; rank 16; hidden 4096 = slice; 4 adapters, lora_B (4, 4096, 16)
+    bf16 N(0, 0.02); input bf16 N(0, 1); indices uniform in {-1, 0..3};
+    accumulate onto a bf16 N(0, 1) output."""
+    rng = np.random.default_rng(seed)
+    B, K, N, L = 8, 16, 4096, 4
+    lens = rng.integers(64, 513, size=B).astype(np.int64)
+    idx = rng.integers(-1, L, size=B).astype(np.int64)
+    T = int(lens.sum())
+    w = normal(rng, (L, N, K), 0.02, "bf16")
+    x = normal(rng, (T, K), 1.0, "bf16")
+    out0 = normal(rng, (T, N), 1.0, "bf16")
+    return Workload("llama7b_q_proj", [SliceInput(x, "bf16", w, "bf16", 0)], out0, "bf16",
+                    exclusive_cumsum(lens), lens, idx, True, K, L, seed)
+
+
+QKV_SLICES = ((0, 4096), (4096, 1024), (5120, 1024))
+
+
+def gqa_qkv(seed: int = 0, shared_input: bool = False) -> Workload:
+    """Fused GQA QKV: output width 6144 = Q [0, 4096) + K [4096, 5120) +
+    V [5120, 6144); rank 32; 16 adapters with per-slice lora_B bf16
+    N(0, 0.02); 32 sequences with lengths log-uniform in [1, 2048]; per-slice
+    inputs bf16 N(0, 1) (one shared input if ``shared_input``); accumulate
+    onto a bf16 N(0, 1) output; every sequence has an adapter."""
+    rng = np.random.default_rng(seed)
+    B, K, L, H = 32, 32, 16, 6144
+    u = rng.uniform(0.0, math.log(2048.0), size=B)
+    lens = np.clip(np.rint(np.exp(u)), 1, 2048).astype(np.int64)
+    idx = rng.integers(0, L, size=B).astype(np.int64)
+    T = int(lens.sum())
+    ws = [normal(rng, (L, n, K), 0.02, "bf16") for _, n in QKV_SLICES]
+    if shared_input:
+        x = normal(rng, (T, K), 1.0, "bf16")
+        xs = [x, x, x]
+    else:
+        xs = [normal(rng, (T, K), 1.0, "bf16") for _ in QKV_SLICES]
+    out0 = normal(rng, (T, H), 1.0, "bf16")
+    slices = [SliceInput(xs[i], "bf16", ws[i], "bf16", QKV_SLICES[i][0]) for i in range(3)]
+    return Workload("gqa_qkv", slices, out0, "bf16", exclusive_cumsum(lens), lens, idx, True,
+                    K, L, seed, {"shared_input": shared_input})
+
+
+def mlp_gate_up(seed: int = 0) -> Workload:
+    """MLP gate/up: output width 28672, slice [14336, 28672); rank 64; 64
+    adapters, lora_B (64, 14336, 64) bf16 N(0, 0.02); 64 sequences with
+    lengths uniform in [1, 512] (about 16384 tokens); input float32 N(0, 1)
+    cast to bf16 for the products; bf16 output (prefilled N(0, 1) so the
+    untouched half is checked); overwrite; every sequence has an adapter."""
+    rng = np.random.default_rng(seed)
+    B, K, N, H, L, off = 64, 64, 14336, 28672, 64, 14336
+    lens = rng.integers(1, 513, size=B).astype(np.int64)
+    idx = rng.integers(0, L, size=B).astype(np.int64)
+    T = int(lens.sum())
+    w = normal(rng, (L, N, K), 0.02, "bf16")
+    x = normal(rng, (T, K), 1.0, "f32")
+    out0 = normal(rng, (T, H), 1.0, "bf16")
+    return Workload("mlp_gate_up", [SliceInput(x, "f32", w, "bf16", off)], out0, "bf16",
+                    exclusive_cumsum(lens), lens, idx, False, K, L, seed)
+
+
+def skewed_mixed(seed: int = 0) -> Workload:
+    """Skewed mixed batch: 256 sequences, one of 8192 tokens and 255 of 1..16
+    tokens, in shuffled order; rank 128; slice = hidden = 8192; 128 adapters,
+    lora_B fp16 N(0, 0.02); input fp16 N(0, 1); indices uniform over adapters
+    with exactly 64 (25%) of the short sequences set to -1; accumulate onto
+    an fp16 N(0, 1) output."""
+    rng = np.random.default_rng(seed)
+    B, K, N, L = 256, 128, 8192, 128
+    short = rng.integers(1, 17, size=B - 1)
+    unordered = np.concatenate([[8192], short]).astype(np.int64)
+    perm = rng.permutation(B)
+    lens = unordered[perm]
+    idx = rng.integers(0, L, size=B).astype(np.int64)
+    short_positions = np.nonzero(perm != 0)[0]
+    off_positions = rng.choice(short_positions, size=64, replace=False)
+    idx[off_positions] = -1
+    T = int(lens.sum())
+    w = normal(rng, (L, N, K), 0.02, "f16")
+    x = normal(rng, (T, K), 1.0, "f16")
+    out0 = normal(rng, (T, N), 1.0, "f16")
+    return Workload("skewed_mixed", [SliceInput(x, "f16", w, "f16", 0)], out0, "f16",
+                    exclusive_cumsum(lens), lens, idx, True, K, L, seed)
+
+
+WORKLOADS: Dict[str, Callable[..., Workload]] = {
+    "tiny_ref": tiny_ref,
+    "llama7b_q_proj": llama7b_q_proj,
+    "gqa_qkv": gqa_qkv,
+    "mlp_gate_up": mlp_gate_up,
+    "skewed_mixed": skewed_mixed,
+}
+
+
+# ---------------------------------------------------------------------------
+# Free-form workloads for edge-case tests.
+# ---------------------------------------------------------------------------
+
+def custom(lens: Sequence[int], idx: Sequence[int], *, K: int, N: int, H: int, off: int,
+           L: int, x_dtype: str = "bf16", w_dtype: str = "bf16", out_dtype: str = "bf16",
+           add: bool = False, seed: int = 0, start: Optional[Sequence[int]] = None,
+           T: Optional[int] = None, values: str = "normal", x_pad: int = 0,
+           out_pad: int = 0, extra_slices: Sequence[tuple] = (), name: str = "custom") -> Workload:
+    """A workload with explicit segments.
+
+    ``values`` is "normal" (x, prior ~ N(0, 1), W ~ N(0, 0.02)) or "int"
+    (x, W in [-3, 3], prior in [-8, 8]: every product and partial sum is an
+    exactly representable small integer).  ``x_pad`` / ``out_pad`` widen the
+    rows (the extra columns are filled too, so strided views can be tested).
+    ``extra_slices`` adds (offset, N) slices after the first.
+    """
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    start = exclusive_cumsum(lens) if start is None else np.asarray(start, dtype=np.int64)
+    if T is None:
+        T = int((start + lens).max()) if len(lens) else 0
+
+    def draw(shape, sigma, lo, hi, dtype):
+        if values == "int":
+            return integers_as(rng, shape, lo, hi, dtype)
+        return normal(rng, shape, sigma, dtype)
+
+    slices = []
+    for (o, n) in [(off, N), *extra_slices]:
+        w = draw((L, n, K), 0.02, -3, 3, w_dtype)
+        xfull = draw((T, K + x_pad), 1.0, -3, 3, x_dtype)
+        slices.append(SliceInput(xfull[:, :K] if x_pad else xfull, x_dtype, w, w_dtype, o))
+    ofull = draw((T, H + out_pad), 1.0, -8, 8, out_dtype)
+    out0 = ofull[:, :H] if out_pad else ofull
+    return Workload(name, slices, out0, out_dtype, start, lens, idx, add, K, L, seed)
