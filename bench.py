@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of SGMV expand-slice on one MI355X.
+
+One step = one call of the hot path (sgmv_expand_slice, or one
+sgmv_expand_multi_slice call for the fused QKV workload) over one batch of
+seeded synthetic input already resident in HBM.  W untimed warm-up steps,
+then exactly K timed steps between HIP events on the launch stream, bracketed
+by device synchronisation.  Each step uses the next of S identical buffer
+sets (inputs, weights, output), S >= 2 and S * footprint >= 1 GiB, so no
+step finds its data in the 256 MB Infinity Cache or the L2s.
+
+Effective bandwidth uses the algorithmic byte count
+    T_act * rank * in_bytes + sum_distinct_adapters slice * rank * w_bytes
+    + T_act * slice * out_bytes * (1 + add_inputs)
+(T_act = rows of segments whose adapter index is not -1; summed over slices
+for the fused call).  tokens/s counts every row handed to the call once.
+
+Prints ONE JSON line.  Also reports the CPU oracle (bounded sample, host
+cores) as a baseline and the HBM traffic measured with rocprofv3 counters
+when a summary for the current kernel source is committed under profiles/.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak, GB/s
+DEFAULT_WORKLOAD = "llama7b_q_proj"
+KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemm_amd", "csrc", f)
+                  for f in ("sgmv_kernels.hip", "sgmv_launch.h", "sgmv_api.cpp")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def byte_model(wl):
+    """Algorithmic bytes of one call, active rows, distinct adapters."""
+    from sgmv_workloads import DTYPE_BYTES
+    act = wl.active_mask()
+    t_act = int(wl.lens[act].sum())
+    distinct = len(set(wl.idx[act].tolist()))
+    total = 0
+    ob = DTYPE_BYTES[wl.out_dtype]
+    for s in wl.slices:
+        total += t_act * wl.K * DTYPE_BYTES[s.x_dtype]
+        total += distinct * s.N * wl.K * DTYPE_BYTES[s.w_dtype]
+        total += t_act * s.N * ob * (2 if wl.add else 1)
+    return total, t_act, distinct
+
+
+def footprint_bytes(wl):
+    """Device bytes one buffer set occupies."""
+    n = wl.out0.nbytes
+    for s in wl.slices:
+        n += s.x.nbytes + s.w.nbytes
+    return n
+
+
+class BufferSet:
+    def __init__(self, wl, device):
+        import numpy as np
+        from sgmv_workloads import to_torch
+        self.x = [to_torch(s.x, s.x_dtype, device) for s in wl.slices]
+        self.w = [to_torch(np.ascontiguousarray(s.w), s.w_dtype, device) for s in wl.slices]
+        self.out = to_torch(wl.out0, wl.out_dtype, device)
+
+    def clone(self):
+        c = object.__new__(BufferSet)
+        c.x = [t.clone() for t in self.x]
+        c.w = [t.clone() for t in self.w]
+        c.out = self.out.clone()
+        return c
+
+
+def make_step(wl, meta, sets):
+    import segmented_gather_gemm_amd as sg
+    start, lens, idx = meta
+    B, M = wl.batches, wl.max_seq_len
+    if len(wl.slices) == 1:
+        s = wl.slices[0]
+
+        def step(i):
+            bs = sets[i % len(sets)]
+            sg.sgmv_expand_slice(bs.x[0], bs.w[0], bs.out, start, lens, idx, B, M, s.offset,
+                                 s.N, wl.add)
+    else:
+        offs = [s.offset for s in wl.slices]
+
+        def step(i):
+            bs = sets[i % len(sets)]
+            sg.sgmv_expand_multi_slice(list(zip(bs.x, bs.w, offs)), bs.out, start, lens, idx,
+                                       B, M, wl.add)
+    return step
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def copy_ceiling(nbytes, device, reps=20):
+    """GB/s of a plain device copy moving `nbytes` read + `nbytes` written
+    (context only)."""
+    import torch
+    n = max(1, nbytes // 2)
+    sets = max(2, math.ceil((1 << 30) / (2 * n)))
+    src = [torch.empty(n, dtype=torch.int16, device=device).fill_(1) for _ in range(sets)]
+    dst = [torch.empty_like(s) for s in src]
+    for i in range(5):
+        dst[i % sets].copy_(src[i % sets])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(reps):
+        dst[i % sets].copy_(src[i % sets])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    return 2 * n * 2 / (ms * 1e-3) / 1e9
+
+
+def traffic_from_profiles(workload, ksha):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
+    b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not b or m.group(1) != ksha:
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(wl, model_bytes, budget_s):
+    """Time the CPU oracle (as it stands) on the same workload, repeating the
+    whole call until about `budget_s` seconds of CPU time have been spent (a
+    bounded sample for big workloads: a prefix of the segments)."""
+    import numpy as np
+    import oracle
+    import sgmv_workloads as W
+    threads = len(os.sched_getaffinity(0))
+    slices = [oracle.Slice(s.x, s.x_dtype, s.w, s.w_dtype, s.offset) for s in wl.slices]
+    work_rows = int(wl.lens[wl.active_mask()].sum())
+    sample = wl
+    note = "full workload"
+    # estimate: ~1e8 fp64 multiply-adds per second per thread
+    macs = work_rows * sum(s.N for s in wl.slices) * wl.K
+    if macs / (1e8 * threads) > budget_s:
+        keep = max(1, int(len(wl.lens) * budget_s * 1e8 * threads / macs))
+        idx = wl.idx.copy()
+        idx[keep:] = -1
+        sample = W.Workload(wl.name, wl.slices, wl.out0, wl.out_dtype, wl.start, wl.lens, idx,
+                            wl.add, wl.K, wl.L)
+        note = f"first {keep} of {len(wl.lens)} segments"
+    sample_bytes, _, _ = byte_model(sample)
+    out = np.empty_like(sample.out0)
+    reps, spent = 0, 0.0
+    while spent < budget_s and reps < 1000:
+        out[...] = sample.out0
+        t0 = time.perf_counter()
+        oracle.expand(slices, out, sample.out_dtype, sample.start, sample.lens, sample.idx,
+                      sample.add, sample.K, sample.L, threads=threads)
+        spent += time.perf_counter() - t0
+        reps += 1
+    secs = spent / reps
+    return {"value": round(sample_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_call": round(secs, 4), "reps": reps,
+            "sample": f"{note} of {wl.name} seed {wl.seed}, fp64 C oracle, {reps} calls"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of CPU-oracle time for the baseline (0 = skip)")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sgmv_workloads as W
+    import segmented_gather_gemm_amd  # noqa: F401  (fails loudly if libsgmv.so is missing)
+
+    if args.workload not in W.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(W.WORKLOADS)}")
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    log(f"bench: generating {args.workload} seed {args.seed}")
+    wl = W.WORKLOADS[args.workload](args.seed)
+    model_bytes, t_act, distinct = byte_model(wl)
+    fp = footprint_bytes(wl)
+    nsets = max(2, math.ceil((1 << 30) / fp))
+    log(f"bench: {len(wl.slices)} slice(s), T={wl.T} (active {t_act}), rank {wl.K}, "
+        f"{distinct} distinct adapters, {model_bytes / 1e6:.2f} MB per call, "
+        f"{nsets} rotated buffer sets of {fp / 1e6:.1f} MB")
+    meta = tuple(torch.from_numpy(a).to(device) for a in (wl.start, wl.lens, wl.idx))
+    first = BufferSet(wl, device)
+    sets = [first] + [first.clone() for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+    step = make_step(wl, meta, sets)
+
+    log(f"bench: {args.warmup} warm-up + {args.steps} timed steps")
+    ms, wall = time_steps(step, args.steps, args.warmup)
+    sec = ms * 1e-3
+    gbs = model_bytes / sec / 1e9
+    tokens_s = wl.T / sec
+    ksha = kernel_source_hash()
+    traffic = traffic_from_profiles(args.workload, ksha)
+    log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
+        f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
+
+    ceiling = None if args.no_copy_ceiling else round(copy_ceiling(model_bytes // 2, device), 1)
+    del sets, first
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log("bench: timing the CPU oracle baseline")
+        cpu = cpu_baseline(wl, model_bytes, args.cpu_budget)
+
+    dtype = {"f16": "f16", "bf16": "bf16"}[wl.slices[0].w_dtype]
+    result = {
+        "metric": "effective HBM GB/s (% of MI355X peak) and tokens/s for sgmv_expand_slice",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(tokens_s, 1),
+        "config": {
+            "workload": args.workload,
+            "seed": args.seed,
+            "slices": [[s.offset, s.N] for s in wl.slices],
+            "rank": wl.K,
+            "batches": wl.batches,
+            "total_tokens": wl.T,
+            "active_tokens": t_act,
+            "distinct_adapters": distinct,
+            "add_inputs": wl.add,
+            "dtypes": {"inputs": wl.slices[0].x_dtype, "lora_b": wl.slices[0].w_dtype,
+                       "output": wl.out_dtype, "accumulate": "f32"},
+            "bytes_per_step": model_bytes,
+            "rotated_buffer_sets": nsets,
+            "call": "sgmv_expand_slice" if len(wl.slices) == 1 else "sgmv_expand_multi_slice",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "expand_kernel",
+            "kernel_source_sha256_16": ksha,
+        },
+        "copy_ceiling_gbs": ceiling,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+/*
+ * sgmv.h -- C ABI of libsgmv: SGMV expand-slice on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (wiki page "Implementation: Predibase Lorax SGMV Expand Slice
+ * Kernel", Description and I/O Contract): for each segment b of a packed
+ * batch and each token m of that segment, row t = b_seq_start_loc[b] + m of
+ * the output gets, in its column window [slice_offset, slice_offset +
+ * slice_size),
+ *
+ *     out[t][slice_offset + n] = (add_inputs ? out[t][slice_offset + n] : 0)
+ *                                + sum_k inputs[t][k] * lora_b[a][n][k],
+ *
+ * with a = lora_indices[b].  lora_b is stored (lora_num, slice_size, rank),
+ * so the product is inputs . lora_b[a]^T.  Index -1 means no LoRA: those rows
+ * are left untouched, as is every column outside the window.  Products are
+ * accumulated in fp32 and rounded once (nearest even) to the output dtype.
+ * float32 inputs are first rounded to the 16-bit weight dtype (the page's
+ * CAST_TYPE, "mixed-precision type casting").
+ *
+ * Every call enqueues GPU work on `stream` and returns; nothing here
+ * synchronises, copies device data to the host or allocates memory.  All
+ * argument checks happen before any HIP call; on a non-OK status nothing has
+ * been launched and sgmv_last_error() describes the problem.
+ */
+#ifndef SGMV_H
+#define SGMV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGMV_ABI_VERSION 1
+#define SGMV_MAX_SLICES 8      /* slices per multi-slice call                       */
+#define SGMV_MAX_RANK 256      /* largest rank (K) the kernels hold in registers    */
+#define SGMV_MAX_BATCHES 16000 /* segment table lives in on-chip memory (LDS, 64 KiB) */
+
+/* Element types (I/O Contract: weights float16/bfloat16; inputs
+ * float16/bfloat16/float32). */
+typedef enum { SGMV_F16 = 0, SGMV_BF16 = 1, SGMV_F32 = 2 } sgmv_dtype;
+
+typedef enum {
+  SGMV_OK = 0,
+  SGMV_ERR_INVALID_ARGUMENT = 1, /* shapes, strides, bounds, null pointers       */
+  SGMV_ERR_UNSUPPORTED = 2,      /* valid but not implemented (dtype mix, rank)  */
+  SGMV_ERR_HIP = 3               /* a HIP runtime call failed                    */
+} sgmv_status;
+
+/* A 2-D device matrix: `rows` x `cols` elements of `dtype`, rows
+ * `row_stride` elements apart, unit column stride.  Borrowed. */
+typedef struct {
+  void* data;
+  int32_t dtype;
+  int64_t rows, cols, row_stride;
+} sgmv_matrix;
+
+/* A contiguous device stack of `num` matrices, each `rows` x `cols`
+ * (lora_b: num = lora_num, rows = slice_size, cols = rank).  Borrowed. */
+typedef struct {
+  const void* data;
+  int32_t dtype;
+  int64_t num, rows, cols;
+} sgmv_stack;
+
+/* One slice of a fused output for sgmv_expand_multi_slice. */
+typedef struct {
+  sgmv_matrix inputs;     /* (total_tokens, rank)                         */
+  sgmv_stack lora_b;      /* (lora_num, slice_size, rank)                 */
+  int64_t slice_offset;   /* first output column of this slice            */
+  int64_t slice_size;     /* must equal lora_b.rows                       */
+} sgmv_slice;
+
+/*
+ * sgmv_expand_slice -- the page's sgmv_expand_slice (Signature; I/O Contract).
+ *
+ * inputs        device (total_tokens, rank) f16/bf16/f32; read only.
+ * lora_b        device (lora_num, slice_size, rank) f16/bf16, contiguous; read only.
+ *               inputs must be lora_b's dtype or f32.
+ * out           device (total_tokens, full_hidden_size) f16/bf16/f32, modified in
+ *               place only at rows of active segments x [slice_offset,
+ *               slice_offset + slice_size).  row_stride >= cols.
+ * b_seq_start_loc, seq_lens, lora_indices
+ *               device int64[batches]; read only, never copied to the host.
+ *               Segment b covers rows [b_seq_start_loc[b], +seq_lens[b]).
+ * batches       number of segments, 0..SGMV_MAX_BATCHES.
+ * max_seq_len   >= 0; a hint kept for signature parity (the device reads
+ *               seq_lens itself and does not need it).
+ * slice_offset, slice_size
+ *               column window; slice_size must equal lora_b.rows and
+ *               slice_offset + slice_size <= out.cols.
+ * add_inputs    nonzero: accumulate onto out; zero: overwrite.
+ * stream        HIP stream the work is enqueued on (0 = null stream).
+ *
+ * Device-side preconditions (not checkable without a sync): active segments
+ * lie in [0, total_tokens) and are pairwise disjoint, and -1 <= index <
+ * lora_num.  A segment that breaks the first or last of these is skipped
+ * with no out-of-bounds access; overlapping segments give unspecified
+ * values in the overlap.
+ *
+ * Returns SGMV_OK, or a status with nothing launched.  batches == 0,
+ * slice_size == 0 or total_tokens == 0 return SGMV_OK without a launch.
+ */
+sgmv_status sgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
+                              const int64_t* b_seq_start_loc, const int64_t* seq_lens,
+                              const int64_t* lora_indices, int64_t batches,
+                              int64_t max_seq_len, int64_t slice_offset, int64_t slice_size,
+                              int add_inputs, hipStream_t stream);
+
+/*
+ * sgmv_expand_multi_slice -- several slices of one fused output in a single
+ * launch (the page's Description: a future fused operator combining several
+ * slice operations in one launch, for fused QKV or gate/up layouts).
+ *
+ * Equal, element for element and bit for bit, to calling sgmv_expand_slice
+ * once per slice on the same `out`.  slices: host array of 1..SGMV_MAX_SLICES
+ * descriptors, read during the call only.  All slices share `out`, the
+ * segment metadata, the adapter indices, rank, dtypes, lora_num and
+ * add_inputs; their column windows must not overlap.
+ */
+sgmv_status sgmv_expand_multi_slice(const sgmv_slice* slices, int num_slices, sgmv_matrix out,
+                                    const int64_t* b_seq_start_loc, const int64_t* seq_lens,
+                                    const int64_t* lora_indices, int64_t batches,
+                                    int64_t max_seq_len, int add_inputs, hipStream_t stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the thread's next libsgmv call. */
+const char* sgmv_last_error(void);
+
+/* SGMV_ABI_VERSION of the loaded library. */
+int sgmv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SGMV_H */

@@ -1,0 +1,197 @@
+"""Python binding of libsgmv: SGMV expand-slice on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the operation runs in the HIP
+kernels of ``libsgmv.so`` (built in-tree by ``build.py``); PyTorch supplies
+device memory and the current stream.  There is no CPU or PyTorch fallback:
+if the library is missing, importing this package raises.
+
+Names and argument order follow the wiki page "Implementation: Predibase
+Lorax SGMV Expand Slice Kernel" (Signature; I/O Contract):
+
+    sgmv_expand_slice(inputs, lora_b_weights, output_tensor, b_seq_start_loc,
+                      seq_len_tensor, lora_indices_tensor, batches,
+                      max_seq_length, slice_offset, slice_size, add_inputs=False)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libsgmv.so")
+
+SGMV_OK, SGMV_ERR_INVALID_ARGUMENT, SGMV_ERR_UNSUPPORTED, SGMV_ERR_HIP = range(4)
+MAX_SLICES = 8
+
+# Every symbol include/sgmv.h declares.
+EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_last_error",
+                    "sgmv_abi_version")
+
+
+class Matrix(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("row_stride", ctypes.c_int64)]
+
+
+class Stack(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("num", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class SliceDesc(ctypes.Structure):
+    _fields_ = [("inputs", Matrix), ("lora_b", Stack), ("slice_offset", ctypes.c_int64),
+                ("slice_size", ctypes.c_int64)]
+
+
+def _load_library() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(
+            f"{LIBRARY_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            f"g.build()'` (or python segmented_gather_gemm_amd/build.py). There is no fallback.")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.sgmv_expand_slice.argtypes = [Matrix, Stack, Matrix, p, p, p, i64, i64, i64, i64,
+                                      ctypes.c_int, p]
+    lib.sgmv_expand_slice.restype = ctypes.c_int
+    lib.sgmv_expand_multi_slice.argtypes = [ctypes.POINTER(SliceDesc), ctypes.c_int, Matrix, p, p,
+                                            p, i64, i64, ctypes.c_int, p]
+    lib.sgmv_expand_multi_slice.restype = ctypes.c_int
+    lib.sgmv_last_error.argtypes = []
+    lib.sgmv_last_error.restype = ctypes.c_char_p
+    lib.sgmv_abi_version.argtypes = []
+    lib.sgmv_abi_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load_library()
+
+
+class SgmvError(RuntimeError):
+    """A HIP runtime failure reported by libsgmv."""
+
+
+def _raise(status: int):
+    msg = lib.sgmv_last_error().decode(errors="replace")
+    if status == SGMV_ERR_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    if status == SGMV_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise SgmvError(msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _matrix(t, what: str) -> Matrix:
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} must have unit column stride")
+    return Matrix(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1],
+                  t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0)))
+
+
+def _stack(w, what: str) -> Stack:
+    if w.dim() == 4:
+        if w.shape[1] != 1:
+            raise ValueError(f"{what}: a 4-D lora_b must be (lora_num, 1, slice_size, rank)")
+        w = w.squeeze(1)
+    if w.dim() != 3:
+        raise ValueError(f"{what} must be (lora_num, slice_size, rank), got {tuple(w.shape)}")
+    if not w.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return Stack(w.data_ptr(), _dtype_code(w), w.shape[0], w.shape[1], w.shape[2])
+
+
+def _meta(t, what: str, device):
+    import torch
+    if t.dim() != 1:
+        raise ValueError(f"{what} must be 1-D")
+    if t.device != device:
+        raise ValueError(f"{what} must be on {device}")
+    if t.dtype != torch.int64 or not t.is_contiguous():
+        t = t.to(torch.int64).contiguous()   # documented marshalling copy
+    return t
+
+
+def _common(output_tensor, metas):
+    device = output_tensor.device
+    if device.type != "cuda":
+        raise ValueError("output_tensor must be a GPU tensor")
+    kept = [_meta(m, n, device) for m, n in metas]
+    return device, kept
+
+
+def sgmv_expand_slice(inputs, lora_b_weights, output_tensor, b_seq_start_loc, seq_len_tensor,
+                      lora_indices_tensor, batches: int, max_seq_length: int, slice_offset: int,
+                      slice_size: int, add_inputs: bool = False):
+    """In place: output_tensor[start_b + m, slice_offset:slice_offset + slice_size]
+    (+)= inputs[start_b + m] @ lora_b_weights[lora_indices[b]].T for every
+    segment b with index != -1.  Enqueued on the current stream."""
+    import torch
+    device, (start, lens, idx) = _common(output_tensor, [
+        (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
+        (lora_indices_tensor, "lora_indices_tensor")])
+    for t, n in ((inputs, "inputs"), (lora_b_weights, "lora_b_weights")):
+        if t.device != device:
+            raise ValueError(f"{n} must be on {device}")
+    if len(start) < batches or len(lens) < batches or len(idx) < batches:
+        raise ValueError("segment metadata shorter than batches")
+    x = _matrix(inputs, "inputs")
+    w = _stack(lora_b_weights, "lora_b_weights")
+    out = _matrix(output_tensor, "output_tensor")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    with torch.cuda.device(device):
+        st = lib.sgmv_expand_slice(x, w, out, start.data_ptr(), lens.data_ptr(), idx.data_ptr(),
+                                   int(batches), int(max_seq_length), int(slice_offset),
+                                   int(slice_size), int(bool(add_inputs)), stream)
+    if st != SGMV_OK:
+        _raise(st)
+    return output_tensor
+
+
+def sgmv_expand_multi_slice(slices: Sequence[Tuple[object, object, int]], output_tensor,
+                            b_seq_start_loc, seq_len_tensor, lora_indices_tensor, batches: int,
+                            max_seq_length: int, add_inputs: bool = False):
+    """Several slices of one fused output (e.g. Q, K, V) in one launch.
+
+    ``slices``: sequence of (inputs, lora_b_weights, slice_offset); each
+    slice's size is its lora_b_weights.size(-2).  Bit-identical to one
+    sgmv_expand_slice call per slice."""
+    import torch
+    if not 1 <= len(slices) <= MAX_SLICES:
+        raise ValueError(f"1..{MAX_SLICES} slices, got {len(slices)}")
+    device, (start, lens, idx) = _common(output_tensor, [
+        (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
+        (lora_indices_tensor, "lora_indices_tensor")])
+    if len(start) < batches or len(lens) < batches or len(idx) < batches:
+        raise ValueError("segment metadata shorter than batches")
+    arr = (SliceDesc * len(slices))()
+    for i, (x, w, off) in enumerate(slices):
+        if x.device != device or w.device != device:
+            raise ValueError(f"slice {i} must be on {device}")
+        st = _stack(w, f"slice {i} lora_b")
+        arr[i] = SliceDesc(_matrix(x, f"slice {i} inputs"), st, int(off), st.rows)
+    out = _matrix(output_tensor, "output_tensor")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    with torch.cuda.device(device):
+        rc = lib.sgmv_expand_multi_slice(arr, len(slices), out, start.data_ptr(), lens.data_ptr(),
+                                         idx.data_ptr(), int(batches), int(max_seq_length),
+                                         int(bool(add_inputs)), stream)
+    if rc != SGMV_OK:
+        _raise(rc)
+    return output_tensor
+
+
+def abi_version() -> int:
+    return lib.sgmv_abi_version()
+
+
+__all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "abi_version", "SgmvError", "lib",
+           "Matrix", "Stack", "SliceDesc", "EXPORTED_SYMBOLS", "LIBRARY_PATH"]

@@ -1,0 +1,258 @@
+// sgmv_api.cpp -- libsgmv C entry points: argument checks, kernel variant
+// choice, grid sizing and launch.  No allocation, no synchronisation, no
+// device-to-host traffic: the segment metadata stays on the device and the
+// kernels schedule themselves from it.
+//
+// The checks follow the I/O Contract of the wiki page "Implementation:
+// Predibase Lorax SGMV Expand Slice Kernel": inputs (total_tokens, rank);
+// lora_b (lora_num, slice_size, rank) float16/bfloat16; output
+// (total_tokens, full_hidden_size); slice_size equal to lora_b's row count.
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "sgmv.h"
+#include "sgmv_launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+sgmv_status fail(sgmv_status status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return status;
+}
+
+bool known_dtype(int32_t d) { return d == SGMV_F16 || d == SGMV_BF16 || d == SGMV_F32; }
+int64_t elem_bytes(int32_t d) { return d == SGMV_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ksteps_for(int64_t rank) {
+  if (rank <= 32) return 1;
+  if (rank <= 64) return 2;
+  if (rank <= 128) return 4;
+  return 8;  // rank <= SGMV_MAX_RANK
+}
+
+// Per-device compute-unit counts and per-(device, kernel, LDS bucket)
+// occupancy, computed once.
+std::mutex g_mu;
+std::map<int, int> g_cus;
+std::map<std::tuple<int, const void*, size_t>, int> g_occupancy;
+
+hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const size_t bucket = (lds_bytes + 4095) / 4096 * 4096;
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto cu = g_cus.find(dev);
+  if (cu == g_cus.end()) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cu = g_cus.emplace(dev, n > 0 ? n : 1).first;
+  }
+  const auto key = std::make_tuple(dev, kernel, bucket);
+  auto occ = g_occupancy.find(key);
+  if (occ == g_occupancy.end()) {
+    int blocks = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, sgmv::kThreads, bucket);
+    if (e != hipSuccess) return e;
+    occ = g_occupancy.emplace(key, blocks > 0 ? blocks : 1).first;
+  }
+  *workgroups = cu->second * occ->second;
+  return hipSuccess;
+}
+
+// Checks shared by both entry points.  `slices` are host descriptors.
+sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matrix out,
+                             const int64_t* start, const int64_t* lens, const int64_t* idx,
+                             int64_t batches, int64_t max_seq_len, int add_inputs,
+                             hipStream_t stream) {
+  using namespace sgmv;
+  if (num_slices < 1 || num_slices > SGMV_MAX_SLICES)
+    return fail(SGMV_ERR_INVALID_ARGUMENT, "num_slices must be in 1..%d, got %d",
+                SGMV_MAX_SLICES, num_slices);
+  if (!known_dtype(out.dtype))
+    return fail(SGMV_ERR_INVALID_ARGUMENT, "unknown output dtype %d", out.dtype);
+  if (out.rows < 0 || out.cols < 0 || out.row_stride < out.cols)
+    return fail(SGMV_ERR_INVALID_ARGUMENT,
+                "output shape (%lld, %lld) with row stride %lld is invalid",
+                (long long)out.rows, (long long)out.cols, (long long)out.row_stride);
+  if (out.rows > INT32_MAX)
+    return fail(SGMV_ERR_UNSUPPORTED, "more than 2^31-1 tokens (%lld)", (long long)out.rows);
+  if (batches < 0) return fail(SGMV_ERR_INVALID_ARGUMENT, "batches must be >= 0");
+  if (batches > SGMV_MAX_BATCHES)
+    return fail(SGMV_ERR_UNSUPPORTED, "batches %lld exceeds %d", (long long)batches,
+                SGMV_MAX_BATCHES);
+  if (max_seq_len < 0) return fail(SGMV_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
+
+  const sgmv_slice& s0 = slices[0];
+  const int64_t K = s0.inputs.cols;
+  const int64_t L = s0.lora_b.num;
+  for (int i = 0; i < num_slices; ++i) {
+    const sgmv_slice& s = slices[i];
+    if (!known_dtype(s.inputs.dtype) || !known_dtype(s.lora_b.dtype))
+      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: unknown dtype", i);
+    if (s.lora_b.dtype == SGMV_F32)
+      return fail(SGMV_ERR_UNSUPPORTED, "slice %d: lora_b must be float16 or bfloat16", i);
+    if (s.inputs.dtype != s.lora_b.dtype && s.inputs.dtype != SGMV_F32)
+      return fail(SGMV_ERR_UNSUPPORTED,
+                  "slice %d: inputs must have lora_b's dtype or float32 (got %d with %d)", i,
+                  s.inputs.dtype, s.lora_b.dtype);
+    if (s.inputs.rows < 0 || s.inputs.cols < 1 || s.inputs.row_stride < s.inputs.cols)
+      return fail(SGMV_ERR_INVALID_ARGUMENT,
+                  "slice %d: inputs shape (%lld, %lld) with row stride %lld is invalid", i,
+                  (long long)s.inputs.rows, (long long)s.inputs.cols,
+                  (long long)s.inputs.row_stride);
+    if (s.lora_b.num < 0 || s.lora_b.rows < 0 || s.lora_b.cols < 1)
+      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: lora_b shape is invalid", i);
+    if (s.inputs.cols != s.lora_b.cols)
+      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: inputs rank %lld != lora_b rank %lld",
+                  i, (long long)s.inputs.cols, (long long)s.lora_b.cols);
+    if (s.lora_b.rows != s.slice_size)
+      return fail(SGMV_ERR_INVALID_ARGUMENT,
+                  "slice %d: slice_size %lld must equal lora_b.size(-2) = %lld", i,
+                  (long long)s.slice_size, (long long)s.lora_b.rows);
+    if (s.inputs.rows != out.rows)
+      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: inputs rows %lld != output rows %lld",
+                  i, (long long)s.inputs.rows, (long long)out.rows);
+    if (s.slice_offset < 0 || s.slice_size < 0 || s.slice_offset > out.cols - s.slice_size)
+      return fail(SGMV_ERR_INVALID_ARGUMENT,
+                  "slice %d: window [%lld, %lld) is outside the %lld output columns", i,
+                  (long long)s.slice_offset, (long long)(s.slice_offset + s.slice_size),
+                  (long long)out.cols);
+    if (i > 0) {
+      if (s.inputs.cols != K || s.lora_b.num != L || s.inputs.dtype != s0.inputs.dtype ||
+          s.lora_b.dtype != s0.lora_b.dtype)
+        return fail(SGMV_ERR_INVALID_ARGUMENT,
+                    "slice %d: rank, lora_num and dtypes must match slice 0", i);
+    }
+    for (int j = 0; j < i; ++j) {
+      const sgmv_slice& o = slices[j];
+      if (s.slice_size > 0 && o.slice_size > 0 &&
+          s.slice_offset < o.slice_offset + o.slice_size &&
+          o.slice_offset < s.slice_offset + s.slice_size)
+        return fail(SGMV_ERR_INVALID_ARGUMENT, "slices %d and %d overlap", j, i);
+    }
+  }
+  if (K > SGMV_MAX_RANK)
+    return fail(SGMV_ERR_UNSUPPORTED, "rank %lld exceeds %d", (long long)K, SGMV_MAX_RANK);
+  if (L > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "lora_num exceeds 2^31-1");
+
+  int64_t total_tiles = 0;
+  for (int i = 0; i < num_slices; ++i)
+    total_tiles += (slices[i].slice_size + kTileCols - 1) / kTileCols;
+  if (batches == 0 || out.rows == 0 || total_tiles == 0) {
+    g_error.clear();
+    return SGMV_OK;  // nothing to do
+  }
+  if (total_tiles > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "output window too wide");
+  if (!out.data) return fail(SGMV_ERR_INVALID_ARGUMENT, "output data pointer is null");
+  if (!start || !lens || !idx)
+    return fail(SGMV_ERR_INVALID_ARGUMENT, "segment metadata pointer is null");
+  for (int i = 0; i < num_slices; ++i) {
+    if (slices[i].slice_size == 0) continue;
+    if (!slices[i].inputs.data || (!slices[i].lora_b.data && L > 0))
+      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: null data pointer", i);
+  }
+
+  Params p{};
+  p.out = out.data;
+  p.start = start;
+  p.lens = lens;
+  p.idx = idx;
+  p.out_stride = out.row_stride;
+  p.T = out.rows;
+  p.batches = (int32_t)batches;
+  p.L = (int32_t)L;
+  p.K = (int32_t)K;
+  p.num_slices = num_slices;
+  p.total_tiles = (int32_t)total_tiles;
+  const int64_t ob = elem_bytes(out.dtype);
+  int32_t tile_begin = 0;
+  for (int i = 0; i < num_slices; ++i) {
+    const sgmv_slice& s = slices[i];
+    SliceDesc& d = p.s[i];
+    d.x = s.inputs.data;
+    d.w = s.lora_b.data;
+    d.x_stride = s.inputs.row_stride;
+    d.n = s.slice_size;
+    d.offset = s.slice_offset;
+    d.tile_begin = tile_begin;
+    tile_begin += (int32_t)((s.slice_size + kTileCols - 1) / kTileCols);
+    const int64_t xb = elem_bytes(s.inputs.dtype);
+    d.flags = 0;
+    if (aligned16(s.inputs.data) && (s.inputs.row_stride * xb) % 16 == 0 && K % 8 == 0)
+      d.flags |= kVecX;
+    if (aligned16(s.lora_b.data) && K % 8 == 0) d.flags |= kVecW;
+    if (aligned16(out.data) && (out.row_stride * ob) % 16 == 0 && (s.slice_offset * ob) % 16 == 0)
+      d.flags |= kVecOut;
+  }
+
+  Variant v{s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, ksteps_for(K)};
+  const void* kernel = kernel_for(v);
+  if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no kernel for this dtype combination");
+
+  // Upper bound on work units from host-known sizes only: active segments are
+  // disjoint inside [0, T), so row tiles <= ceil(T / 16) + min(batches, T).
+  const int64_t row_tiles = (out.rows + kTileRows - 1) / kTileRows +
+                            (batches < out.rows ? batches : out.rows);
+  const int64_t units = row_tiles * total_tiles;
+  const size_t lds = (size_t)(batches + 1) * sizeof(int32_t);
+  int capacity = 0;
+  hipError_t e = device_capacity(kernel, lds, &capacity);
+  if (e != hipSuccess)
+    return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  int64_t grid = units < capacity ? units : capacity;
+  if (grid > 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  p.grid = (int32_t)grid;
+
+  e = launch(kernel, p, (int)grid, lds, stream);
+  if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_error.clear();
+  return SGMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sgmv_status sgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
+                              const int64_t* b_seq_start_loc, const int64_t* seq_lens,
+                              const int64_t* lora_indices, int64_t batches,
+                              int64_t max_seq_len, int64_t slice_offset, int64_t slice_size,
+                              int add_inputs, hipStream_t stream) {
+  sgmv_slice s;
+  s.inputs = inputs;
+  s.lora_b = lora_b;
+  s.slice_offset = slice_offset;
+  s.slice_size = slice_size;
+  return check_and_launch(&s, 1, out, b_seq_start_loc, seq_lens, lora_indices, batches,
+                          max_seq_len, add_inputs, stream);
+}
+
+sgmv_status sgmv_expand_multi_slice(const sgmv_slice* slices, int num_slices, sgmv_matrix out,
+                                    const int64_t* b_seq_start_loc, const int64_t* seq_lens,
+                                    const int64_t* lora_indices, int64_t batches,
+                                    int64_t max_seq_len, int add_inputs, hipStream_t stream) {
+  if (!slices) return fail(SGMV_ERR_INVALID_ARGUMENT, "slices pointer is null");
+  return check_and_launch(slices, num_slices, out, b_seq_start_loc, seq_lens, lora_indices,
+                          batches, max_seq_len, add_inputs, stream);
+}
+
+const char* sgmv_last_error(void) { return g_error.c_str(); }
+
+int sgmv_abi_version(void) { return SGMV_ABI_VERSION; }
+
+}  // extern "C"

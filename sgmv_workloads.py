@@ -229,6 +229,23 @@ WORKLOADS: Dict[str, Callable[..., Workload]] = {
 }
 
 
+def to_torch(a: np.ndarray, dtype: str, device="cuda"):
+    """Storage array (uint16 bits or float32) -> torch tensor of ``dtype`` on
+    ``device`` holding the same bits.  A 2-D column-slice view of a wider
+    array becomes the same view of the whole array (row stride kept)."""
+    import torch
+    if a.ndim == 2 and not a.flags.c_contiguous and a.strides[1] == a.itemsize:
+        rs = a.strides[0] // a.itemsize
+        full = np.lib.stride_tricks.as_strided(a, shape=(a.shape[0], rs),
+                                               strides=(a.strides[0], a.itemsize))
+        return to_torch(np.ascontiguousarray(full), dtype, device)[:, :a.shape[1]]
+    a = np.ascontiguousarray(a)
+    if dtype == "f32":
+        return torch.from_numpy(a).to(device)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return torch.from_numpy(a.view(np.int16)).to(device).view(tdt)
+
+
 # ---------------------------------------------------------------------------
 # Free-form workloads for edge-case tests.
 # ---------------------------------------------------------------------------

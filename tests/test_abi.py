@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports exactly what
+include/sgmv.h declares, and rejects every host-checkable violation of the
+I/O Contract before any HIP call (wiki page "Implementation: Predibase Lorax
+SGMV Expand Slice Kernel", I/O Contract).  No compute call is made here."""
+import os
+import re
+
+import pytest
+
+import segmented_gather_gemm_amd as sg
+from segmented_gather_gemm_amd import Matrix, SliceDesc, Stack
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgmv.h")
+
+F16, BF16, F32 = 0, 1, 2
+OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
+FAKE = 0x10000  # never dereferenced: every case below fails (or no-ops) before a launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgmv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert names == sorted(sg.EXPORTED_SYMBOLS)
+    out = os.popen(f"nm -D --defined-only {sg.LIBRARY_PATH}").read()
+    exported = sorted(set(re.findall(r" T (sgmv_[a-z_]+)$", out, flags=re.M)))
+    assert exported == names
+    for n in names:
+        assert hasattr(sg.lib, n)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define SGMV_ABI_VERSION (\d+)", open(HEADER).read())
+    assert sg.abi_version() == int(m.group(1))
+
+
+def call(x=None, w=None, out=None, meta=(FAKE, FAKE, FAKE), batches=2, max_len=6, off=64,
+         size=64, add=0):
+    x = x or Matrix(FAKE, F16, 10, 8, 8)
+    w = w or Stack(FAKE, F16, 2, 64, 8)
+    out = out or Matrix(FAKE, F16, 10, 192, 192)
+    st = sg.lib.sgmv_expand_slice(x, w, out, *meta, batches, max_len, off, size, add, None)
+    return st, sg.lib.sgmv_last_error().decode()
+
+
+CASES = [
+    # (kwargs, status, message fragment)
+    (dict(x=Matrix(FAKE, F16, 10, 16, 16)), INVALID, "rank"),
+    (dict(size=32), INVALID, "slice_size"),
+    (dict(x=Matrix(FAKE, F16, 9, 8, 8)), INVALID, "rows"),
+    (dict(off=-1), INVALID, "window"),
+    (dict(off=129), INVALID, "window"),
+    (dict(out=Matrix(FAKE, F16, 10, 192, 191)), INVALID, "row stride"),
+    (dict(x=Matrix(FAKE, F16, 10, 8, 7)), INVALID, "row stride"),
+    (dict(x=Matrix(FAKE, F16, 10, 0, 0), w=Stack(FAKE, F16, 2, 64, 0)), INVALID, "inputs shape"),
+    (dict(batches=-1), INVALID, "batches"),
+    (dict(max_len=-1), INVALID, "max_seq_len"),
+    (dict(batches=1 << 20), UNSUPPORTED, "batches"),
+    (dict(out=Matrix(FAKE, 7, 10, 192, 192)), INVALID, "dtype"),
+    (dict(w=Stack(FAKE, F32, 2, 64, 8)), UNSUPPORTED, "float16 or bfloat16"),
+    (dict(x=Matrix(FAKE, BF16, 10, 8, 8)), UNSUPPORTED, "dtype"),
+    (dict(x=Matrix(FAKE, F16, 10, 300, 300), w=Stack(FAKE, F16, 2, 64, 300)), UNSUPPORTED, "rank"),
+    (dict(meta=(0, FAKE, FAKE)), INVALID, "metadata"),
+    (dict(out=Matrix(0, F16, 10, 192, 192)), INVALID, "output data"),
+    (dict(x=Matrix(0, F16, 10, 8, 8)), INVALID, "null data"),
+    (dict(out=Matrix(FAKE, F16, -1, 192, 192)), INVALID, "output shape"),
+]
+
+
+@pytest.mark.parametrize("kw,status,frag", CASES)
+def test_invalid_arguments_rejected_before_launch(kw, status, frag):
+    st, msg = call(**kw)
+    assert st == status, msg
+    assert frag in msg
+
+
+@pytest.mark.parametrize("kw", [dict(batches=0), dict(size=0, w=Stack(FAKE, F16, 2, 0, 8)),
+                                dict(x=Matrix(FAKE, F16, 0, 8, 8),
+                                     out=Matrix(FAKE, F16, 0, 192, 192)),
+                                dict(meta=(0, 0, 0), batches=0)])
+def test_no_op_calls_return_ok_without_launch(kw):
+    st, msg = call(**kw)
+    assert st == OK and msg == ""
+
+
+def test_error_message_cleared_after_ok():
+    assert call(off=-1)[0] == INVALID
+    assert call(batches=0) == (OK, "")
+
+
+def _slice(off, size, rank=8, dt=F16, num=2):
+    return SliceDesc(Matrix(FAKE, dt, 10, rank, rank), Stack(FAKE, dt, num, size, rank), off, size)
+
+
+def multi(slices, n=None, batches=2):
+    arr = (SliceDesc * max(len(slices), 1))(*slices)
+    st = sg.lib.sgmv_expand_multi_slice(arr, len(slices) if n is None else n,
+                                        Matrix(FAKE, F16, 10, 192, 192), FAKE, FAKE, FAKE,
+                                        batches, 6, 0, None)
+    return st, sg.lib.sgmv_last_error().decode()
+
+
+def test_multi_slice_checks():
+    assert multi([_slice(0, 64), _slice(32, 64)])[0] == INVALID            # overlap
+    assert "overlap" in multi([_slice(0, 64), _slice(32, 64)])[1]
+    assert multi([_slice(0, 64), _slice(64, 64, rank=16)])[0] == INVALID   # rank differs
+    assert multi([_slice(0, 64), _slice(64, 64, num=3)])[0] == INVALID     # lora_num differs
+    assert multi([_slice(0, 64), _slice(64, 64, dt=BF16)])[0] == INVALID   # dtype differs
+    assert multi([_slice(0, 64)] * 9)[0] == INVALID                         # > 8 slices
+    assert multi([_slice(0, 64)], n=0)[0] == INVALID
+    assert multi([_slice(0, 64), _slice(160, 64)])[0] == INVALID           # past the output
+    assert multi([_slice(0, 64), _slice(64, 64)], batches=0) == (OK, "")
+    st = sg.lib.sgmv_expand_multi_slice(None, 1, Matrix(FAKE, F16, 10, 192, 192), FAKE, FAKE,
+                                        FAKE, 2, 6, 0, None)
+    assert st == INVALID
+
+
+def test_python_wrapper_rejects_host_tensors():
+    import torch
+    x = torch.zeros(10, 8, dtype=torch.float16)
+    w = torch.zeros(2, 64, 8, dtype=torch.float16)
+    o = torch.zeros(10, 192, dtype=torch.float16)
+    m = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU"):
+        sg.sgmv_expand_slice(x, w, o, m, m, m, 2, 6, 64, 64)
