@@ -1,8 +1,9 @@
 """Build the CPU oracle's shared library (test infrastructure only).
 
-The oracle is plain C compiled by gcc: -O2, OpenMP over output rows, no
-fast-math and -ffp-contract=off, so every multiply and add in it is a
-separately rounded IEEE fp64 operation.
+The oracle is plain C compiled by gcc: -O2, POSIX threads over output rows,
+no fast-math and -ffp-contract=off, so every multiply and add in it is a
+separately rounded IEEE fp64 operation.  It links no OpenMP runtime (the
+process that loads it may already hold PyTorch's own).
 """
 import os
 import subprocess
@@ -12,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "sgmv_oracle.c")
 LIBRARY = os.path.join(HERE, "libsgmv_oracle.so")
 
-CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
           "-fno-fast-math", "-Wall", "-Wextra"]
 
 

@@ -2,9 +2,9 @@
  * sgmv_oracle.c -- plain fp64 CPU oracle for SGMV expand-slice.
  *
  * TEST INFRASTRUCTURE ONLY (see sgmv_oracle.h).  Nothing here is tuned:
- * the computation is the definition written out as loops, parallel over
- * output rows only (rows are independent).  Build without fast-math and
- * with -ffp-contract=off.
+ * the computation is the definition written out as loops, split over output
+ * rows only (rows are independent) with plain POSIX threads.  Build without
+ * fast-math and with -ffp-contract=off.
  *
  * Definition followed (wiki page "Implementation: Predibase Lorax SGMV
  * Expand Slice Kernel"):
@@ -20,14 +20,14 @@
  *     products.
  * Readings where the page is silent are listed beside the code below.
  */
+#define _GNU_SOURCE
 #include "sgmv_oracle.h"
 
 #include <math.h>
+#include <pthread.h>
+#include <sched.h>
 #include <stdlib.h>
 #include <string.h>
-#ifdef _OPENMP
-#include <omp.h>
-#endif
 
 /* ---------------------------------------------------------------------- */
 /* IEEE 754 binary formats: exponent field width and trailing significand  */
@@ -130,12 +130,59 @@ static void store_bits(int dtype, void* base, int64_t i, uint32_t bits) {
 }
 
 int orc_threads(int threads) {
-#ifdef _OPENMP
-  return threads > 0 ? threads : omp_get_max_threads();
-#else
-  (void)threads;
+  if (threads > 0) return threads;
+  cpu_set_t set;
+  if (sched_getaffinity(0, sizeof set, &set) == 0 && CPU_COUNT(&set) > 0) return CPU_COUNT(&set);
   return 1;
-#endif
+}
+
+/* Run fn(ctx, worker, begin, end) over `workers` contiguous chunks of
+ * [0, n); chunk 0 runs on the calling thread.  A chunk whose thread cannot
+ * be started runs on the calling thread after the others are joined. */
+typedef void (*chunk_fn)(void* ctx, int worker, int64_t begin, int64_t end);
+typedef struct {
+  chunk_fn fn;
+  void* ctx;
+  int worker;
+  int64_t begin, end;
+} chunk_job;
+
+static void* chunk_main(void* p) {
+  chunk_job* j = (chunk_job*)p;
+  j->fn(j->ctx, j->worker, j->begin, j->end);
+  return NULL;
+}
+
+static int run_chunks(int workers, int64_t n, chunk_fn fn, void* ctx) {
+  chunk_job* jobs = (chunk_job*)malloc(sizeof(chunk_job) * (size_t)workers);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)workers);
+  int* started = (int*)calloc((size_t)workers, sizeof(int));
+  if (!jobs || !th || !started) {
+    free(jobs); free(th); free(started);
+    return ORC_NO_MEMORY;
+  }
+  for (int i = 0; i < workers; ++i) {
+    jobs[i].fn = fn;
+    jobs[i].ctx = ctx;
+    jobs[i].worker = i;
+    jobs[i].begin = n * i / workers;
+    jobs[i].end = n * (i + 1) / workers;
+  }
+  for (int i = 1; i < workers; ++i)
+    started[i] = pthread_create(&th[i], NULL, chunk_main, &jobs[i]) == 0;
+  chunk_main(&jobs[0]);
+  for (int i = 1; i < workers; ++i) {
+    if (started[i]) pthread_join(th[i], NULL);
+    else chunk_main(&jobs[i]);
+  }
+  free(jobs); free(th); free(started);
+  return ORC_OK;
+}
+
+static int workers_for(int threads, int64_t n) {
+  int w = orc_threads(threads);
+  if (n < w) w = n > 0 ? (int)n : 1;
+  return w;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -214,6 +261,45 @@ static double slice_value(const orc_slice* s, const double* wval, const double* 
   return r;
 }
 
+typedef struct {
+  const orc_slice* s;
+  const double* wval;
+  int64_t K, out_stride, ref_base;
+  void* out;
+  int out_dtype, add;
+  const int64_t* owner;
+  const int64_t* idx;
+  double* ref;
+  int failed;
+} expand_ctx;
+
+/* Rows [begin, end) of one slice. */
+static void expand_rows(void* p, int worker, int64_t begin, int64_t end) {
+  (void)worker;
+  expand_ctx* c = (expand_ctx*)p;
+  const orc_slice* s = c->s;
+  double* xrow = (double*)malloc(sizeof(double) * (size_t)c->K);
+  if (!xrow) {
+    __atomic_store_n(&c->failed, 1, __ATOMIC_RELAXED);
+    return;
+  }
+  for (int64_t t = begin; t < end; ++t) {
+    const int64_t b = c->owner[t];
+    if (b < 0) continue;  /* not in an active segment: untouched */
+    const int64_t a = c->idx[b];
+    for (int64_t k = 0; k < c->K; ++k) xrow[k] = input_value(s, t, k);
+    for (int64_t n = 0; n < s->N; ++n) {
+      const int64_t o = t * c->out_stride + s->offset + n;
+      const double prior =
+          c->add ? orc_decode(c->out_dtype, load_bits(c->out_dtype, c->out, o)) : 0.0;
+      const double r = slice_value(s, c->wval, xrow, c->K, a, n, c->add, prior);
+      if (c->ref) c->ref[c->ref_base + t * s->N + n] = r;
+      store_bits(c->out_dtype, c->out, o, orc_encode(c->out_dtype, r));
+    }
+  }
+  free(xrow);
+}
+
 int orc_expand(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
                void* out, int out_dtype, int64_t T, int64_t H, int64_t out_stride,
                const int64_t* start, const int64_t* lens, const int64_t* idx,
@@ -223,40 +309,17 @@ int orc_expand(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
   int64_t* owner = NULL;
   rc = build_owner(T, L, start, lens, idx, batches, &owner);
   if (rc != ORC_OK) return rc;
-  const int nt = orc_threads(threads);
 
   int64_t ref_base = 0;
   for (int si = 0; si < num_slices; ++si) {
     const orc_slice* s = &slices[si];
     double* wval = decode_stack(s, K, L);
     if (!wval) { free(owner); return ORC_NO_MEMORY; }
-    int failed = 0;
-#pragma omp parallel num_threads(nt)
-    {
-      double* xrow = (double*)malloc(sizeof(double) * (size_t)K);
-      if (!xrow) {
-#pragma omp atomic write
-        failed = 1;
-      }
-#pragma omp for schedule(static)
-      for (int64_t t = 0; t < T; ++t) {
-        if (!xrow) continue;
-        const int64_t b = owner[t];
-        if (b < 0) continue;  /* not in an active segment: untouched */
-        const int64_t a = idx[b];
-        for (int64_t k = 0; k < K; ++k) xrow[k] = input_value(s, t, k);
-        for (int64_t n = 0; n < s->N; ++n) {
-          const int64_t o = t * out_stride + s->offset + n;
-          const double prior = add_inputs ? orc_decode(out_dtype, load_bits(out_dtype, out, o)) : 0.0;
-          const double r = slice_value(s, wval, xrow, K, a, n, add_inputs, prior);
-          if (ref) ref[ref_base + t * s->N + n] = r;
-          store_bits(out_dtype, out, o, orc_encode(out_dtype, r));
-        }
-      }
-      free(xrow);
-    }
+    expand_ctx c = {s, wval, K, out_stride, ref_base, out, out_dtype, add_inputs,
+                    owner, idx, ref, 0};
+    rc = run_chunks(workers_for(threads, T), T, expand_rows, &c);
     free(wval);
-    if (failed) { free(owner); return ORC_NO_MEMORY; }
+    if (rc != ORC_OK || c.failed) { free(owner); return ORC_NO_MEMORY; }
     ref_base += T * s->N;
   }
   free(owner);
@@ -287,6 +350,73 @@ static void note_bad(orc_report* r, int64_t row, int64_t col) {
   }
 }
 
+typedef struct {
+  const orc_slice* slices;
+  int num_slices;
+  double** wval;
+  int64_t K, H, out_stride;
+  const void* prior;
+  const void* cand;
+  int out_dtype, add;
+  double atol, rtol;
+  const int64_t* owner;
+  const int64_t* idx;
+  const int64_t* rows;
+  const int* col_slice;
+  orc_report* part;  /* one per worker */
+  int failed;
+} check_ctx;
+
+/* Compare rows [begin, end) of the row list (or of the output). */
+static void check_rows(void* p, int worker, int64_t begin, int64_t end) {
+  check_ctx* c = (check_ctx*)p;
+  orc_report* mine = &c->part[worker];
+  const int64_t K = c->K;
+  const int od = c->out_dtype;
+  double* xrows = (double*)malloc(sizeof(double) * (size_t)(K * c->num_slices));
+  if (!xrows) {
+    __atomic_store_n(&c->failed, 1, __ATOMIC_RELAXED);
+    return;
+  }
+  for (int64_t i = begin; i < end; ++i) {
+    const int64_t t = c->rows ? c->rows[i] : i;
+    const int64_t b = c->owner[t];
+    if (b >= 0)
+      for (int si = 0; si < c->num_slices; ++si)
+        for (int64_t k = 0; k < K; ++k) xrows[si * K + k] = input_value(&c->slices[si], t, k);
+    for (int64_t col = 0; col < c->H; ++col) {
+      const int64_t o = t * c->out_stride + col;
+      const uint32_t cb = load_bits(od, c->cand, o);
+      const uint32_t pb = load_bits(od, c->prior, o);
+      const int si = c->col_slice[col];
+      if (b < 0 || si < 0) {
+        /* untouched region: bit-identical to the prior output */
+        mine->checked_untouched++;
+        if (cb != pb) { mine->bad_untouched++; note_bad(mine, t, col); }
+        continue;
+      }
+      const orc_slice* s = &c->slices[si];
+      const double r = slice_value(s, c->wval[si], xrows + si * K, K, c->idx[b],
+                                   col - s->offset, c->add, orc_decode(od, pb));
+      const uint32_t rb = orc_encode(od, r);
+      mine->checked_values++;
+      if (is_nonfinite_bits(od, rb)) {
+        const int ok = is_nan_bits(od, rb) ? is_nan_bits(od, cb) : (cb == rb);
+        if (!ok) { mine->bad_values++; note_bad(mine, t, col); }
+        continue;
+      }
+      const double cv = orc_decode(od, cb);
+      if (!isfinite(cv)) { mine->bad_values++; note_bad(mine, t, col); continue; }
+      const double err = fabs(cv - r);
+      const double allowed = c->atol + c->rtol * fabs(r);
+      if (err > mine->max_abs_err) mine->max_abs_err = err;
+      if (err / allowed > mine->max_tol_ratio) mine->max_tol_ratio = err / allowed;
+      if (!(err <= allowed)) { mine->bad_values++; note_bad(mine, t, col); }
+    }
+  }
+  free(xrows);
+}
+
 int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
               const void* prior, const void* cand, int out_dtype,
               int64_t T, int64_t H, int64_t out_stride,
@@ -305,97 +435,48 @@ int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
   rc = build_owner(T, L, start, lens, idx, batches, &owner);
   if (rc != ORC_OK) return rc;
 
+  const int64_t nrows = rows ? num_rows : T;
+  const int workers = workers_for(threads, nrows);
   double** wval = (double**)calloc((size_t)num_slices, sizeof(double*));
-  if (!wval) { free(owner); return ORC_NO_MEMORY; }
-  for (int si = 0; si < num_slices; ++si) {
+  int* col_slice = (int*)malloc(sizeof(int) * (size_t)(H > 0 ? H : 1));
+  orc_report* part = (orc_report*)calloc((size_t)workers, sizeof(orc_report));
+  if (!wval || !col_slice || !part) rc = ORC_NO_MEMORY;
+  for (int si = 0; rc == ORC_OK && si < num_slices; ++si) {
     wval[si] = decode_stack(&slices[si], K, L);
     if (!wval[si]) rc = ORC_NO_MEMORY;
   }
-  /* column -> slice map for one row (-1 = outside every slice) */
-  int* col_slice = (int*)malloc(sizeof(int) * (size_t)(H > 0 ? H : 1));
-  if (!col_slice) rc = ORC_NO_MEMORY;
-  if (rc != ORC_OK) {
+  if (rc == ORC_OK) {
+    /* column -> slice map for one row (-1 = outside every slice) */
+    for (int64_t col = 0; col < H; ++col) col_slice[col] = -1;
+    for (int si = 0; si < num_slices; ++si)
+      for (int64_t n = 0; n < slices[si].N; ++n) col_slice[slices[si].offset + n] = si;
+    for (int w = 0; w < workers; ++w) part[w].first_bad_row = part[w].first_bad_col = -1;
+    check_ctx c = {slices, num_slices, wval, K, H, out_stride, prior, cand, out_dtype,
+                   add_inputs, atol, rtol, owner, idx, rows, col_slice, part, 0};
+    rc = run_chunks(workers, nrows, check_rows, &c);
+    if (rc == ORC_OK && c.failed) rc = ORC_NO_MEMORY;
+  }
+  if (rc == ORC_OK) {
+    orc_report total;
+    memset(&total, 0, sizeof total);
+    total.first_bad_row = total.first_bad_col = -1;
+    for (int w = 0; w < workers; ++w) {
+      const orc_report* m = &part[w];
+      total.checked_values += m->checked_values;
+      total.checked_untouched += m->checked_untouched;
+      total.bad_values += m->bad_values;
+      total.bad_untouched += m->bad_untouched;
+      if (m->max_abs_err > total.max_abs_err) total.max_abs_err = m->max_abs_err;
+      if (m->max_tol_ratio > total.max_tol_ratio) total.max_tol_ratio = m->max_tol_ratio;
+      if (m->first_bad_row >= 0) note_bad(&total, m->first_bad_row, m->first_bad_col);
+    }
+    *report = total;
+  }
+  if (wval)
     for (int si = 0; si < num_slices; ++si) free(wval[si]);
-    free(wval); free(col_slice); free(owner);
-    return rc;
-  }
-  for (int64_t c = 0; c < H; ++c) col_slice[c] = -1;
-  for (int si = 0; si < num_slices; ++si)
-    for (int64_t n = 0; n < slices[si].N; ++n) col_slice[slices[si].offset + n] = si;
-
-  orc_report total;
-  memset(&total, 0, sizeof total);
-  total.first_bad_row = total.first_bad_col = -1;
-  const int64_t nrows = rows ? num_rows : T;
-  const int nt = orc_threads(threads);
-  int failed = 0;
-
-#pragma omp parallel num_threads(nt)
-  {
-    orc_report mine;
-    memset(&mine, 0, sizeof mine);
-    mine.first_bad_row = mine.first_bad_col = -1;
-    double* xrows = (double*)malloc(sizeof(double) * (size_t)(K * num_slices));
-    if (!xrows) {
-#pragma omp atomic write
-      failed = 1;
-    }
-#pragma omp for schedule(static)
-    for (int64_t i = 0; i < nrows; ++i) {
-      if (!xrows) continue;
-      const int64_t t = rows ? rows[i] : i;
-      const int64_t b = owner[t];
-      if (b >= 0)
-        for (int si = 0; si < num_slices; ++si)
-          for (int64_t k = 0; k < K; ++k) xrows[si * K + k] = input_value(&slices[si], t, k);
-      for (int64_t c = 0; c < H; ++c) {
-        const int64_t o = t * out_stride + c;
-        const uint32_t cb = load_bits(out_dtype, cand, o);
-        const uint32_t pb = load_bits(out_dtype, prior, o);
-        const int si = col_slice[c];
-        if (b < 0 || si < 0) {
-          /* untouched region: bit-identical to the prior output */
-          mine.checked_untouched++;
-          if (cb != pb) { mine.bad_untouched++; note_bad(&mine, t, c); }
-          continue;
-        }
-        const orc_slice* s = &slices[si];
-        const double r = slice_value(s, wval[si], xrows + si * K, K, idx[b],
-                                     c - s->offset, add_inputs, orc_decode(out_dtype, pb));
-        const uint32_t rb = orc_encode(out_dtype, r);
-        mine.checked_values++;
-        if (is_nonfinite_bits(out_dtype, rb)) {
-          const int ok = is_nan_bits(out_dtype, rb) ? is_nan_bits(out_dtype, cb) : (cb == rb);
-          if (!ok) { mine.bad_values++; note_bad(&mine, t, c); }
-          continue;
-        }
-        const double cv = orc_decode(out_dtype, cb);
-        if (!isfinite(cv)) { mine.bad_values++; note_bad(&mine, t, c); continue; }
-        const double err = fabs(cv - r);
-        const double allowed = atol + rtol * fabs(r);
-        if (err > mine.max_abs_err) mine.max_abs_err = err;
-        if (err / allowed > mine.max_tol_ratio) mine.max_tol_ratio = err / allowed;
-        if (!(err <= allowed)) { mine.bad_values++; note_bad(&mine, t, c); }
-      }
-    }
-    free(xrows);
-#pragma omp critical
-    {
-      total.checked_values += mine.checked_values;
-      total.checked_untouched += mine.checked_untouched;
-      total.bad_values += mine.bad_values;
-      total.bad_untouched += mine.bad_untouched;
-      if (mine.max_abs_err > total.max_abs_err) total.max_abs_err = mine.max_abs_err;
-      if (mine.max_tol_ratio > total.max_tol_ratio) total.max_tol_ratio = mine.max_tol_ratio;
-      if (mine.first_bad_row >= 0) note_bad(&total, mine.first_bad_row, mine.first_bad_col);
-    }
-  }
-
-  for (int si = 0; si < num_slices; ++si) free(wval[si]);
   free(wval);
   free(col_slice);
+  free(part);
   free(owner);
-  if (failed) return ORC_NO_MEMORY;
-  *report = total;
-  return ORC_OK;
+  return rc;
 }

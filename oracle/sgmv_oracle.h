@@ -71,7 +71,7 @@ typedef struct {
  * in place.  `out` must hold the prior output O0 on entry.  If `ref` is not
  * NULL it receives, per slice in order, a (T, N_s) fp64 array of the exact
  * (pre-rounding) values for rows of active segments (other rows untouched).
- * `threads` <= 0 lets OpenMP choose.  Returns an ORC_* code; on error `out`
+ * `threads` <= 0 uses every CPU the process may run on.  Returns an ORC_* code; on error `out`
  * is unchanged.
  */
 int orc_expand(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
@@ -107,7 +107,8 @@ int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
               const int64_t* rows, int64_t num_rows, int threads,
               orc_report* report);
 
-/* Number of OpenMP threads a parallel region with `threads` would use. */
+/* Worker threads a call with `threads` uses at most (<= 0: the CPUs in the
+ * process's affinity mask). */
 int orc_threads(int threads);
 
 #ifdef __cplusplus
