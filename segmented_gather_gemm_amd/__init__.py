@@ -44,12 +44,34 @@ class SliceDesc(ctypes.Structure):
                 ("slice_size", ctypes.c_int64)]
 
 
+def _hip_runtimes_mapped():
+    """Distinct HIP runtime files mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1] if line.strip() else ""
+                if "libamdhip64.so" in os.path.basename(path):
+                    found.add(os.path.realpath(path))
+    except OSError:
+        pass
+    return found
+
+
 def _load_library() -> ctypes.CDLL:
+    # PyTorch ships its own HIP runtime.  Load it first so that libsgmv's
+    # dependency on libamdhip64.so.7 resolves to that same, already mapped
+    # runtime: two HIP runtimes in one process do not share devices, streams
+    # or allocations.
+    import torch  # noqa: F401
     if not os.path.exists(LIBRARY_PATH):
         raise ImportError(
             f"{LIBRARY_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
             f"g.build()'` (or python segmented_gather_gemm_amd/build.py). There is no fallback.")
     lib = ctypes.CDLL(LIBRARY_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
     i64, p = ctypes.c_int64, ctypes.c_void_p
     lib.sgmv_expand_slice.argtypes = [Matrix, Stack, Matrix, p, p, p, i64, i64, i64, i64,
                                       ctypes.c_int, p]

@@ -3,6 +3,10 @@ import sys
 
 import pytest
 
+# PyTorch carries its own HIP runtime; import it before anything can load
+# libsgmv.so so that the whole process uses that one runtime.
+import torch  # noqa: F401,E402
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

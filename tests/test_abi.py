@@ -128,3 +128,8 @@ def test_python_wrapper_rejects_host_tensors():
     m = torch.zeros(2, dtype=torch.int64)
     with pytest.raises(ValueError, match="GPU"):
         sg.sgmv_expand_slice(x, w, o, m, m, m, 2, 6, 64, 64)
+
+
+def test_one_hip_runtime_in_process():
+    """libsgmv resolves to the HIP runtime PyTorch already mapped."""
+    assert len(sg._hip_runtimes_mapped()) == 1
