@@ -128,6 +128,40 @@ def time_steps(step, steps, warmup):
     return t0.elapsed_time(t1) / steps, wall
 
 
+def time_steps_graph(step, steps, warmup):
+    """Capture `warmup` and `steps` consecutive steps into two HIP graphs and
+    time one replay of the second: the same launches with the host's launch
+    overhead taken out of the loop."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):            # first calls fill the library's device caches
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        for i in range(warmup):
+            step(i)
+    with torch.cuda.graph(g_timed):
+        for i in range(steps):
+            step(warmup + i)
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    g_timed.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, wall
+
+
 def copy_ceiling(nbytes, device, reps=20):
     """GB/s of a plain device copy moving `nbytes` read + `nbytes` written
     (context only)."""
@@ -211,6 +245,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU-oracle time for the baseline (0 = skip)")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: HIP-graph replay, eager also reported)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -241,8 +277,15 @@ def main():
     torch.cuda.synchronize()
     step = make_step(wl, meta, sets)
 
-    log(f"bench: {args.warmup} warm-up + {args.steps} timed steps")
-    ms, wall = time_steps(step, args.steps, args.warmup)
+    log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
+    ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
+    log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
+    if args.eager:
+        ms, wall, mode = ms_eager, wall_eager, "eager"
+    else:
+        log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
+        ms, wall = time_steps_graph(step, args.steps, args.warmup)
+        mode = "hip-graph replay"
     sec = ms * 1e-3
     gbs = model_bytes / sec / 1e9
     tokens_s = wl.T / sec
@@ -291,6 +334,8 @@ def main():
             "bytes_per_step": model_bytes,
             "rotated_buffer_sets": nsets,
             "call": "sgmv_expand_slice" if len(wl.slices) == 1 else "sgmv_expand_multi_slice",
+            "launch": mode,
+            "eager_us_per_step": round(ms_eager * 1e3, 3),
         },
         "roofline": {
             "bound": "hbm",

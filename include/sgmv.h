@@ -34,8 +34,9 @@ extern "C" {
 
 #define SGMV_ABI_VERSION 1
 #define SGMV_MAX_SLICES 8      /* slices per multi-slice call                       */
-#define SGMV_MAX_RANK 256      /* largest rank (K) the kernels hold in registers    */
-#define SGMV_MAX_BATCHES 16000 /* segment table lives in on-chip memory (LDS, 64 KiB) */
+#define SGMV_MAX_RANK 256      /* largest rank the register-tiled kernels take; larger
+                                  ranks (any size) run on the generic kernel */
+#define SGMV_MAX_BATCHES 4000  /* segment table lives in on-chip memory (LDS, 64 KiB) */
 
 /* Element types (I/O Contract: weights float16/bfloat16; inputs
  * float16/bfloat16/float32). */

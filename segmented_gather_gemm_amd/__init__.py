@@ -142,6 +142,16 @@ def _meta(t, what: str, device):
     return t
 
 
+def _on_device(device):
+    """Context that makes `device` current for the launch (a no-op when it
+    already is)."""
+    import contextlib
+    import torch
+    if torch.cuda.current_device() == device.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _common(output_tensor, metas):
     device = output_tensor.device
     if device.type != "cuda":
@@ -169,7 +179,7 @@ def sgmv_expand_slice(inputs, lora_b_weights, output_tensor, b_seq_start_loc, se
     w = _stack(lora_b_weights, "lora_b_weights")
     out = _matrix(output_tensor, "output_tensor")
     stream = torch.cuda.current_stream(device).cuda_stream
-    with torch.cuda.device(device):
+    with _on_device(device):
         st = lib.sgmv_expand_slice(x, w, out, start.data_ptr(), lens.data_ptr(), idx.data_ptr(),
                                    int(batches), int(max_seq_length), int(slice_offset),
                                    int(slice_size), int(bool(add_inputs)), stream)
@@ -202,7 +212,7 @@ def sgmv_expand_multi_slice(slices: Sequence[Tuple[object, object, int]], output
         arr[i] = SliceDesc(_matrix(x, f"slice {i} inputs"), st, int(off), st.rows)
     out = _matrix(output_tensor, "output_tensor")
     stream = torch.cuda.current_stream(device).cuda_stream
-    with torch.cuda.device(device):
+    with _on_device(device):
         rc = lib.sgmv_expand_multi_slice(arr, len(slices), out, start.data_ptr(), lens.data_ptr(),
                                          idx.data_ptr(), int(batches), int(max_seq_length),
                                          int(bool(add_inputs)), stream)

@@ -15,35 +15,64 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libsgmv.so")
-SOURCES = [os.path.join(CSRC, "sgmv_api.cpp"), os.path.join(CSRC, "sgmv_kernels.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("sgmv_api.cpp", "sgmv_generic.hip", "sgmv_fast_ks1.hip", "sgmv_fast_ks2.hip",
+            "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile libsgmv.so next to this file (always rebuilds); return its path."""
-    tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra_flags, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    t0 = time.time()
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _compile(src: str, obj: str, flags) -> subprocess.CompletedProcess:
+    cmd = [HIPCC, *FLAGS, *flags, "-c", src, "-o", obj]
+    return cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _diagnostics(text: str) -> str:
     # hipcc's host pass does not know the packed-fp32 feature and says so; keep
     # the rest of the diagnostics.
     noise = "is not a recognized feature for this target"
-    diag = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{diag}")
-    if diag.strip() and verbose:
-        print(diag)
-    os.replace(tmp, LIBRARY)
+    return "\n".join(l for l in text.splitlines() if noise not in l)
+
+
+def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY) -> str:
+    """Compile every translation unit in parallel and link libsgmv.so (always
+    rebuilds); return its path."""
+    t0 = time.time()
+    tmpdir = output + ".objs%d" % os.getpid()
+    os.makedirs(tmpdir, exist_ok=True)
+    try:
+        jobs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd, proc = _compile(src, obj, [f for f in extra_flags if f != "-shared"])
+            jobs.append((src, obj, cmd, proc))
+        for src, obj, cmd, proc in jobs:
+            out, _ = proc.communicate()
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if proc.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src} ({proc.returncode}):\n{_diagnostics(out)}")
+            diag = _diagnostics(out)
+            if diag.strip() and verbose:
+                print(diag)
+        tmp = output + ".tmp%d" % os.getpid()
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o, _, _ in jobs],
+                "-o", tmp]
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{_diagnostics(res.stdout + res.stderr)}")
+        os.replace(tmp, output)
+    finally:
+        for f in os.listdir(tmpdir):
+            os.remove(os.path.join(tmpdir, f))
+        os.rmdir(tmpdir)
     if verbose:
-        print(f"built {LIBRARY} in {time.time() - t0:.1f}s", flush=True)
-    return LIBRARY
+        print(f"built {output} in {time.time() - t0:.1f}s", flush=True)
+    return output
 
 
 if __name__ == "__main__":

@@ -42,6 +42,21 @@ int ksteps_for(int64_t rank) {
   return 8;  // rank <= SGMV_MAX_RANK
 }
 
+// The kernel for a call: a fast (pipelined) kernel when rank, slice widths
+// and alignment allow it, else the generic one.
+const void* pick_kernel(int xd, int wd, int od, bool add, int64_t K, bool fast_shapes) {
+  using namespace sgmv;
+  if (fast_shapes && K % 8 == 0 && K <= SGMV_MAX_RANK) {
+    switch (ksteps_for(K)) {
+      case 1: return fast_kernel_ks1(xd, wd, od, add);
+      case 2: return fast_kernel_ks2(xd, wd, od, add);
+      case 4: return fast_kernel_ks4(xd, wd, od, add);
+      default: return fast_kernel_ks8(xd, wd, od, add);
+    }
+  }
+  return generic_kernel(xd, wd, od, add);
+}
+
 // Per-device compute-unit counts and per-(device, kernel, LDS bucket)
 // occupancy, computed once.
 std::mutex g_mu;
@@ -145,8 +160,7 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
         return fail(SGMV_ERR_INVALID_ARGUMENT, "slices %d and %d overlap", j, i);
     }
   }
-  if (K > SGMV_MAX_RANK)
-    return fail(SGMV_ERR_UNSUPPORTED, "rank %lld exceeds %d", (long long)K, SGMV_MAX_RANK);
+  if (K > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "rank exceeds 2^31-1");
   if (L > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "lora_num exceeds 2^31-1");
 
   int64_t total_tiles = 0;
@@ -199,8 +213,14 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
       d.flags |= kVecOut;
   }
 
-  Variant v{s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, ksteps_for(K)};
-  const void* kernel = kernel_for(v);
+  bool fast_shapes = true;
+  for (int i = 0; i < num_slices; ++i) {
+    if (slices[i].slice_size == 0) continue;
+    const int32_t need = kVecX | kVecW | kVecOut;
+    if (slices[i].slice_size % 8 != 0 || (p.s[i].flags & need) != need) fast_shapes = false;
+  }
+  const void* kernel =
+      pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast_shapes);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no kernel for this dtype combination");
 
   // Upper bound on work units from host-known sizes only: active segments are
@@ -208,7 +228,7 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   const int64_t row_tiles = (out.rows + kTileRows - 1) / kTileRows +
                             (batches < out.rows ? batches : out.rows);
   const int64_t units = row_tiles * total_tiles;
-  const size_t lds = (size_t)(batches + 1) * sizeof(int32_t);
+  const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);  // segment table
   int capacity = 0;
   hipError_t e = device_capacity(kernel, lds, &capacity);
   if (e != hipSuccess)
@@ -218,7 +238,8 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
 
-  e = launch(kernel, p, (int)grid, lds, stream);
+  void* args[] = {&p};
+  e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
   if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_error.clear();
   return SGMV_OK;

@@ -1,0 +1,698 @@
+// sgmv_device.h -- gfx950 device code for SGMV expand-slice (included by the
+// kernel translation units; internal to libsgmv).
+//
+// Operation (wiki page "Implementation: Predibase Lorax SGMV Expand Slice
+// Kernel", Description and I/O Contract): for segment b with adapter
+// a = idx[b] != -1 and each row t of the segment,
+//     out[t][off + n] (+)= sum_k x[t][k] * W[a][n][k],   n in [0, N).
+//
+// Design (MI355X-first; the page's Triton GroupGEMM tiling is prior art only):
+//
+//  * One persistent launch.  Every workgroup first scans the segment
+//    metadata (device int64 arrays, never read back by the host) into an LDS
+//    table of row-tile prefix sums, row ranges and adapters -- the
+//    device-side scheduler.  Index -1 segments and segments outside [0, T)
+//    get no tiles.
+//  * Work unit = (column tile of 256 output columns, 16-row tile of one
+//    segment).  Units are ordered column-tile-major, so consecutive units of
+//    a workgroup walk down the rows of a segment under one column tile and
+//    the adapter's weight tile stays in registers across all of them.
+//    Workgroups take equal contiguous unit ranges; workgroup ids are
+//    remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
+//    owns one contiguous eighth of the range, i.e. its own column tiles and
+//    hence its own slice of every adapter's weights in its L2.
+//  * Each of the 4 wavefronts owns 64 of the 256 columns.  The contraction
+//    runs on the matrix cores as C^T = W . X^T with v_mfma_f32_16x16x32_
+//    {bf16,f16}: the weight rows are the MFMA rows (A operand, stationary in
+//    VGPRs), the 16 tokens of the tile are the MFMA columns (B operand).
+//    Weight rows are assigned to MFMA rows so that every lane ends up holding
+//    8 consecutive output columns of one token: the epilogue then reads the
+//    prior output and writes the result with 16-byte accesses, 64 contiguous
+//    bytes per token per instruction.
+//  * Rank step ks of the MFMA covers rank [32 ks, 32 ks + 32); lane group g
+//    loads the 16-byte block 32 ks + 8 g of its token's input row and of its
+//    weight row, so one load instruction reads 64 contiguous bytes of each
+//    of 16 rows.
+//  * fp32 accumulation; with add_inputs the prior output seeds the
+//    accumulator, so the result is rounded once (v_cvt_pk_{bf16,f16}_f32,
+//    nearest even).  float32 inputs are rounded to the weight dtype first.
+//
+// Two kernels share this structure:
+//  * expand_fast: software-pipelined.  The next unit's loads are issued
+//    before the current unit's contraction and stores.  Every unit issues
+//    the same vector-memory instructions (addresses of lanes that have no
+//    data are clamped to valid locations, their values are masked in
+//    registers and their stores are predicated), so the compiler can wait
+//    for one unit's data with a nonzero vmcnt instead of draining the queue
+//    -- on gfx9 the counter covers loads and stores alike and retires in
+//    issue order.  Needs rank % 8 == 0, slice widths % 8 == 0 and 16-byte
+//    alignment of rows and column groups.
+//  * expand_generic: any shape, stride and alignment (element-wise edges),
+//    any rank (rank processed in 32-wide chunks, weights reloaded per unit).
+#pragma once
+
+#include "sgmv_launch.h"
+
+// Largest rank-step count (rank <= 32 * steps) whose fast kernels keep a
+// second weight tile in registers to prefetch across adapter / column-tile
+// changes.
+#ifndef SGMV_DOUBLE_W_MAX_KSTEPS
+#define SGMV_DOUBLE_W_MAX_KSTEPS 2
+#endif
+
+namespace sgmv {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { F16 = 0, BF16 = 1, F32 = 2 };
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// D = A . B + C on 16x16 fp32, A 16x32 and B 32x16 of the weight dtype.
+template <int WD>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (WD == BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> one packed pair of 16-bit values, round to nearest even.
+template <int D>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  if constexpr (D == BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// One 16-bit value (low half of h) -> float, exact.
+template <int D>
+__device__ __forceinline__ float widen(uint32_t h) {
+  if constexpr (D == BF16)
+    return __uint_as_float(h << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ int clamp8(int64_t v) {
+  return v <= 0 ? 0 : (v >= 8 ? 8 : (int)v);
+}
+
+template <int D>
+constexpr int raw_vecs() { return D == F32 ? 2 : 1; }
+
+// Eight consecutive elements of dtype D at element `e` with 16-byte loads
+// (one for 16-bit types, two for float32); the block must be aligned.
+template <int D>
+__device__ __forceinline__ void load_vec8(const void* base, int64_t e, u32x4* dst) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const char*>(base) +
+                                                        e * (D == F32 ? 4 : 2));
+  dst[0] = *reinterpret_cast<const u32x4*>(p);
+  if constexpr (D == F32) dst[1] = *reinterpret_cast<const u32x4*>(p + 4);
+}
+
+// Eight consecutive elements of dtype D at element `e`, the first `cnt`
+// (0..8) real and the rest zero; vector loads when `vec` (aligned) and the
+// block is whole, element loads otherwise.
+template <int D>
+__device__ __forceinline__ void load_any8(const void* base, int64_t e, int cnt, bool vec,
+                                          u32x4* dst) {
+  if (vec && cnt == 8) {
+    load_vec8<D>(base, e, dst);
+    return;
+  }
+  if constexpr (D == F32) {
+    const uint32_t* p = static_cast<const uint32_t*>(base) + e;
+    uint32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = i < cnt ? p[i] : 0u;
+    dst[0] = u32x4{v[0], v[1], v[2], v[3]};
+    dst[1] = u32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + e;
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = i < cnt ? (uint32_t)p[i] : 0u;
+    dst[0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16)};
+  }
+}
+
+// Raw input block -> packed 16-bit MFMA operand of the weight dtype (float32
+// inputs are rounded to nearest even here).
+template <int XD, int WD>
+__device__ __forceinline__ u32x4 x_operand(const u32x4* raw) {
+  if constexpr (XD == F32) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      r[2 * i] = pack2<WD>(__uint_as_float(raw[i][0]), __uint_as_float(raw[i][1]));
+      r[2 * i + 1] = pack2<WD>(__uint_as_float(raw[i][2]), __uint_as_float(raw[i][3]));
+    }
+    return r;
+  } else {
+    return raw[0];
+  }
+}
+
+// Raw output block -> eight floats (exact).
+template <int OD>
+__device__ __forceinline__ void out_values(const u32x4* raw, float* v) {
+  if constexpr (OD == F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(raw[0][i]);
+      v[4 + i] = __uint_as_float(raw[1][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = widen<OD>(raw[0][i] & 0xFFFFu);
+      v[2 * i + 1] = widen<OD>(raw[0][i] >> 16);
+    }
+  }
+}
+
+// Eight floats -> raw output block (rounded to the output dtype).
+template <int OD>
+__device__ __forceinline__ void out_pack(const float* v, u32x4* raw) {
+  if constexpr (OD == F32) {
+    raw[0] = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                   __float_as_uint(v[3])};
+    raw[1] = u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                   __float_as_uint(v[7])};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[0][i] = pack2<OD>(v[2 * i], v[2 * i + 1]);
+  }
+}
+
+template <int OD>
+__device__ __forceinline__ void store_vec8(void* base, int64_t e, const u32x4* raw) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + e * (OD == F32 ? 4 : 2));
+  *reinterpret_cast<u32x4*>(p) = raw[0];
+  if constexpr (OD == F32) *reinterpret_cast<u32x4*>(p + 4) = raw[1];
+}
+
+// Store the first `cnt` of eight rounded output values (element-wise unless
+// the block is whole and aligned).
+template <int OD>
+__device__ __forceinline__ void store_any8(void* base, int64_t e, int cnt, bool vec,
+                                           const float* v) {
+  u32x4 raw[raw_vecs<OD>()];
+  out_pack<OD>(v, raw);
+  if (vec && cnt == 8) {
+    store_vec8<OD>(base, e, raw);
+    return;
+  }
+  if constexpr (OD == F32) {
+    float* p = static_cast<float*>(base) + e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < cnt) p[i] = v[i];
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(base) + e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < cnt) p[i] = (uint16_t)(i & 1 ? raw[0][i / 2] >> 16 : raw[0][i / 2] & 0xFFFFu);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scheduler.
+// ---------------------------------------------------------------------------
+
+// Segment table in LDS, filled by build_tile_table:
+//   tile_start[0..batches]  exclusive prefix sum of row tiles per segment
+//   seg_row[b], seg_end[b]  first row and one-past-last row of segment b
+//   seg_lora[b]             its adapter index
+// A segment is active (gets tiles) when its index lies in [0, lora_num), its
+// length is positive and it lies inside [0, T).
+struct SegTable {
+  int32_t* tile_start;
+  int32_t* seg_row;
+  int32_t* seg_end;
+  int32_t* seg_lora;
+};
+
+__device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
+  SegTable t;
+  t.tile_start = lds;
+  t.seg_row = lds + (batches + 1);
+  t.seg_end = t.seg_row + batches;
+  t.seg_lora = t.seg_end + batches;
+  return t;
+}
+
+// Fill the table (every thread of the workgroup takes part); returns the
+// total number of row tiles (wave-uniform).
+__device__ __forceinline__ int64_t build_tile_table(const Params& p, const SegTable& tab,
+                                                    int32_t* wave_total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int32_t carry = 0;
+  for (int base = 0; base < p.batches; base += kThreads) {
+    const int b = base + tid;
+    int32_t tiles = 0;
+    if (b < p.batches) {
+      const int64_t st = p.start[b], ln = p.lens[b], a = p.idx[b];
+      const bool active = a >= 0 && a < p.L && ln > 0 && st >= 0 && st <= p.T - ln;
+      if (active) tiles = (int32_t)((ln + kTileRows - 1) / kTileRows);
+      tab.seg_row[b] = active ? (int32_t)st : 0;
+      tab.seg_end[b] = active ? (int32_t)(st + ln) : 0;
+      tab.seg_lora[b] = active ? (int32_t)a : 0;
+    }
+    int32_t incl = tiles;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) wave_total[wave] = incl;
+    __syncthreads();
+    int32_t before = carry, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int32_t s = wave_total[w];
+      before += w < wave ? s : 0;
+      all += s;
+    }
+    if (b < p.batches) tab.tile_start[b] = before + incl - tiles;
+    carry += all;
+    __syncthreads();
+  }
+  if (tid == 0) tab.tile_start[p.batches] = carry;
+  __syncthreads();
+  return uniform(carry);
+}
+
+// This workgroup's contiguous range [begin, end) of the U units; workgroup
+// ids are remapped so each XCD gets one contiguous eighth of the range.
+__device__ __forceinline__ void unit_range(const Params& p, int64_t U, int64_t* begin,
+                                           int64_t* end) {
+  const int bid = blockIdx.x;
+  const int lw = (p.grid >= 16 && (p.grid & 7) == 0) ? (bid & 7) * (p.grid >> 3) + (bid >> 3)
+                                                      : bid;
+  *begin = U * lw / p.grid;
+  *end = U * (lw + 1) / p.grid;
+}
+
+// Largest b in [0, n) with table[b] <= key (table non-decreasing, table[0] = 0).
+__device__ __forceinline__ int last_at_most(const int32_t* table, int n, int64_t key) {
+  int lo = 0, hi = n;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uniform(table[mid]) <= key) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int slice_of(const Params& p, int tile) {
+  int si = 0;
+  while (si + 1 < p.num_slices && p.s[si + 1].tile_begin <= tile) ++si;
+  return si;
+}
+
+// One work unit as one wavefront sees it.
+struct Unit {
+  int64_t col0;    // first of the wave's 64 columns, within the slice
+  int64_t a;       // adapter
+  int64_t t;       // this lane's output row (token j of the tile)
+  int64_t seg_t0;  // first row of the segment (a valid row for clamping)
+  int tile;        // global column tile
+  int si;          // slice
+  bool row_ok;     // token j lies inside the segment
+};
+
+// Wave-uniform walk over the units of a range, column-tile-major; the
+// segment's row range and adapter come from the LDS table.
+struct Cursor {
+  const Params& p;
+  const SegTable& tab;
+  int64_t RT, rt;
+  int tile, b, si;
+
+  __device__ __forceinline__ Cursor(const Params& p_, const SegTable& t, int64_t rt_total,
+                                    int64_t u)
+      : p(p_), tab(t), RT(rt_total) {
+    tile = (int)(u / RT);
+    rt = u - (int64_t)tile * RT;
+    b = last_at_most(tab.tile_start, p.batches + 1, rt);
+    while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+    si = slice_of(p, tile);
+  }
+
+  __device__ __forceinline__ void advance() {
+    if (++rt == RT) {
+      rt = 0;
+      ++tile;
+      b = 0;
+      si = slice_of(p, tile);
+    }
+    while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+  }
+
+  __device__ __forceinline__ Unit decode(int wave, int j) const {
+    const int64_t seg_row = uniform(tab.seg_row[b]);
+    const int64_t seg_end = uniform(tab.seg_end[b]);
+    const SliceDesc& S = p.s[si];
+    Unit u;
+    u.tile = tile;
+    u.si = si;
+    u.col0 = (int64_t)(tile - S.tile_begin) * kTileCols + wave * kWaveCols;
+    u.a = uniform(tab.seg_lora[b]);
+    u.t = seg_row + (rt - uniform(tab.tile_start[b])) * kTileRows + j;
+    u.row_ok = u.t < seg_end;
+    u.seg_t0 = seg_row;
+    return u;
+  }
+};
+
+// Weight row held by MFMA row i = j of subtile s = 2q + h: the accumulator
+// rows of lane group g are then the 8 consecutive output columns
+// col0 + 32q + 8g + 0..7.
+__device__ __forceinline__ int64_t weight_row(int64_t col0, int s, int j) {
+  return col0 + 32 * (s >> 1) + 8 * (j >> 2) + 4 * (s & 1) + (j & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Fast kernel.
+// ---------------------------------------------------------------------------
+
+// Loads of one unit that are in flight while the previous unit computes.
+template <int XD, int OD, int KS>
+struct Stage {
+  u32x4 x[KS * raw_vecs<XD>()];   // this lane's rank blocks of its token
+  u32x4 o[2 * raw_vecs<OD>()];    // prior output: two 8-column groups
+};
+
+template <int XD, int WD, int OD, bool ADD, int KS>
+__global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
+  extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
+  __shared__ int32_t wave_total[kWaves];
+  const SegTable tab = seg_table(lds, p.batches);
+  const int64_t RT = build_tile_table(p, tab, wave_total);
+  const int64_t U = RT * p.total_tiles;
+  if (U == 0) return;
+  int64_t u_begin, u_end;
+  unit_range(p, U, &u_begin, &u_end);
+  if (u_begin >= u_end) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;   // lane group: rank sub-block / column group
+  const int j = lane & 15;   // token of the tile / MFMA row of the A operand
+  const int K = p.K;
+  // Rank step ks covers rank [32 ks, 32 ks + 32); lane group g holds the
+  // 8-element block 32 ks + 8 g (the same grouping as the generic kernel, so
+  // both give bit-identical results).  Blocks past K (when K is not a
+  // multiple of 32 * KS) are zero in both operands.
+  const bool k_tail = K < 32 * KS;
+  bool kvalid[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kvalid[ks] = 32 * ks + 8 * g < K;
+
+  Cursor cur_pos(p, tab, RT, u_begin);
+
+  // Weight tile of a unit.  Every lane loads: rows past the slice width read
+  // the slice's last row and rank blocks past K read block 0 (masked to zero
+  // when the tile is installed).
+  auto load_w = [&](u32x4 (&w)[4][KS], const Unit& u) __attribute__((always_inline)) {
+    const SliceDesc& S = p.s[u.si];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int64_t n = weight_row(u.col0, s, j);
+      n = n < S.n ? n : S.n - 1;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int kb = kvalid[ks] ? 32 * ks + 8 * g : 0;
+        load_vec8<WD>(S.w, (u.a * S.n + n) * K + kb, &w[s][ks]);
+      }
+    }
+  };
+  auto mask_w = [&](u32x4 (&dst)[4][KS], const u32x4 (&src)[4][KS])
+                    __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        dst[s][ks] = (!k_tail || kvalid[ks]) ? src[s][ks] : u32x4{0u, 0u, 0u, 0u};
+  };
+  // Inputs and prior output of a unit.  Rows outside the segment read the
+  // segment's first row, column groups past the slice read group 0; their
+  // values are never stored.
+  auto load_stage = [&](Stage<XD, OD, KS>& st, const Unit& u) __attribute__((always_inline)) {
+    const SliceDesc& S = p.s[u.si];
+    const int64_t t = u.row_ok ? u.t : u.seg_t0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kb = kvalid[ks] ? 32 * ks + 8 * g : 0;
+      load_vec8<XD>(S.x, t * S.x_stride + kb, &st.x[ks * raw_vecs<XD>()]);
+    }
+    if constexpr (ADD) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int64_t c = u.col0 + 32 * q + 8 * g;
+        c = c < S.n ? c : 0;
+        load_vec8<OD>(p.out, t * p.out_stride + S.offset + c, &st.o[q * raw_vecs<OD>()]);
+      }
+    }
+  };
+  auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][KS],
+                           const Unit& u) __attribute__((always_inline)) {
+    const SliceDesc& S = p.s[u.si];
+    f32x4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (ADD) out_values<OD>(&st.o[q * raw_vecs<OD>()], v);
+      acc[2 * q] = f32x4{v[0], v[1], v[2], v[3]};
+      acc[2 * q + 1] = f32x4{v[4], v[5], v[6], v[7]};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 xo = x_operand<XD, WD>(&st.x[ks * raw_vecs<XD>()]);
+      if (k_tail && !kvalid[ks]) xo = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[s] = mfma<WD>(w[s][ks], xo, acc[s]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float v[8] = {acc[2 * q][0], acc[2 * q][1], acc[2 * q][2], acc[2 * q][3],
+                          acc[2 * q + 1][0], acc[2 * q + 1][1], acc[2 * q + 1][2],
+                          acc[2 * q + 1][3]};
+      u32x4 raw[raw_vecs<OD>()];
+      out_pack<OD>(v, raw);
+      const int64_t c = u.col0 + 32 * q + 8 * g;
+      if (u.row_ok && c < S.n) store_vec8<OD>(p.out, u.t * p.out_stride + S.offset + c, raw);
+    }
+  };
+
+  // Software pipeline (see the file comment).  wA holds the weight tile of
+  // the unit being computed; with double buffering a changed tile for the
+  // next unit is loaded into wB one unit ahead and installed (masked) into
+  // wA before that unit computes.
+  constexpr bool kDoubleW = KS <= SGMV_DOUBLE_W_MAX_KSTEPS;
+  u32x4 wA[4][KS], wB[4][kDoubleW ? KS : 1];
+  Stage<XD, OD, KS> sA, sB;
+
+  Unit cur = cur_pos.decode(wave, j);
+  {
+    u32x4 wl[4][KS];
+    load_w(wl, cur);
+    mask_w(wA, wl);
+  }
+  int w_tile = cur.tile;
+  int64_t w_a = cur.a;
+  bool w_pending = false;
+  load_stage(sA, cur);
+
+  int64_t u = u_begin;
+  auto step = [&](Stage<XD, OD, KS>& s_cur, Stage<XD, OD, KS>& s_nxt)
+                  __attribute__((always_inline)) -> bool {
+    if constexpr (kDoubleW) {
+      if (w_pending) {
+        mask_w(wA, wB);
+        w_pending = false;
+      }
+    }
+    const bool more = u + 1 < u_end;
+    Unit nxt = cur;
+    if (more) {
+      cur_pos.advance();
+      nxt = cur_pos.decode(wave, j);
+    }
+    const bool wswitch = nxt.tile != w_tile || nxt.a != w_a;
+    if constexpr (kDoubleW) {
+      if (wswitch) {
+        load_w(wB, nxt);
+        w_pending = true;
+        w_tile = nxt.tile;
+        w_a = nxt.a;
+      }
+    }
+    load_stage(s_nxt, nxt);
+    // Keep the next unit's loads ahead of this unit's waits and arithmetic.
+    __builtin_amdgcn_sched_barrier(0);
+    compute_store(s_cur, wA, cur);
+    if constexpr (!kDoubleW) {
+      if (wswitch) {
+        u32x4 wl[4][KS];
+        load_w(wl, nxt);
+        mask_w(wA, wl);
+        w_tile = nxt.tile;
+        w_a = nxt.a;
+      }
+    }
+    if (!more) return false;
+    ++u;
+    cur = nxt;
+    return true;
+  };
+  while (step(sA, sB) && step(sB, sA)) {
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: any shape, stride, alignment and rank.
+// ---------------------------------------------------------------------------
+
+template <int XD, int WD, int OD, bool ADD>
+__global__ __launch_bounds__(kThreads) void expand_generic(const Params p) {
+  extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
+  __shared__ int32_t wave_total[kWaves];
+  const SegTable tab = seg_table(lds, p.batches);
+  const int64_t RT = build_tile_table(p, tab, wave_total);
+  const int64_t U = RT * p.total_tiles;
+  if (U == 0) return;
+  int64_t u_begin, u_end;
+  unit_range(p, U, &u_begin, &u_end);
+  if (u_begin >= u_end) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int K = p.K;
+
+  Cursor pos(p, tab, RT, u_begin);
+  for (int64_t u = u_begin;;) {
+    const Unit un = pos.decode(wave, j);
+    const SliceDesc& S = p.s[un.si];
+    if (un.col0 < S.n) {
+      const bool vec_x = S.flags & kVecX;
+      const bool vec_w = S.flags & kVecW;
+      const bool vec_o = S.flags & kVecOut;
+      f32x4 acc[4];
+      int64_t ocol[2];
+      int ocnt[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t c = un.col0 + 32 * q + 8 * g;
+        ocol[q] = un.t * p.out_stride + S.offset + c;
+        ocnt[q] = un.row_ok ? clamp8(S.n - c) : 0;
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (ADD) {
+          u32x4 raw[raw_vecs<OD>()];
+          load_any8<OD>(p.out, ocol[q], ocnt[q], vec_o, raw);
+          out_values<OD>(raw, v);
+        }
+        acc[2 * q] = f32x4{v[0], v[1], v[2], v[3]};
+        acc[2 * q + 1] = f32x4{v[4], v[5], v[6], v[7]};
+      }
+      // Rank in chunks of 32: lane group g holds rank block k0 + 8g.
+      for (int k0 = 0; k0 < K; k0 += 32) {
+        const int kb = k0 + 8 * g;
+        u32x4 xraw[raw_vecs<XD>()];
+        load_any8<XD>(S.x, un.t * S.x_stride + kb, un.row_ok ? clamp8(K - kb) : 0, vec_x,
+                      xraw);
+        const u32x4 xo = x_operand<XD, WD>(xraw);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int64_t n = weight_row(un.col0, s, j);
+          u32x4 w;
+          load_any8<WD>(S.w, (un.a * S.n + n) * K + kb, n < S.n ? clamp8(K - kb) : 0, vec_w,
+                        &w);
+          acc[s] = mfma<WD>(w, xo, acc[s]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float v[8] = {acc[2 * q][0], acc[2 * q][1], acc[2 * q][2], acc[2 * q][3],
+                            acc[2 * q + 1][0], acc[2 * q + 1][1], acc[2 * q + 1][2],
+                            acc[2 * q + 1][3]};
+        store_any8<OD>(p.out, ocol[q], ocnt[q], vec_o, v);
+      }
+    }
+    if (++u == u_end) break;
+    pos.advance();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel tables.
+// ---------------------------------------------------------------------------
+
+template <int XD, int WD, int OD, int KS>
+const void* fast_entry(bool add) {
+  return add ? reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, true, KS>)
+             : reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, false, KS>);
+}
+
+template <int XD, int WD, int KS>
+const void* fast_by_out(int od, bool add) {
+  switch (od) {
+    case F16: return fast_entry<XD, WD, F16, KS>(add);
+    case BF16: return fast_entry<XD, WD, BF16, KS>(add);
+    case F32: return fast_entry<XD, WD, F32, KS>(add);
+    default: return nullptr;
+  }
+}
+
+template <int KS>
+const void* fast_table(int xd, int wd, int od, bool add) {
+  if (wd == BF16 && xd == BF16) return fast_by_out<BF16, BF16, KS>(od, add);
+  if (wd == BF16 && xd == F32) return fast_by_out<F32, BF16, KS>(od, add);
+  if (wd == F16 && xd == F16) return fast_by_out<F16, F16, KS>(od, add);
+  if (wd == F16 && xd == F32) return fast_by_out<F32, F16, KS>(od, add);
+  return nullptr;
+}
+
+template <int XD, int WD, int OD>
+const void* generic_entry(bool add) {
+  return add ? reinterpret_cast<const void*>(&expand_generic<XD, WD, OD, true>)
+             : reinterpret_cast<const void*>(&expand_generic<XD, WD, OD, false>);
+}
+
+template <int XD, int WD>
+const void* generic_by_out(int od, bool add) {
+  switch (od) {
+    case F16: return generic_entry<XD, WD, F16>(add);
+    case BF16: return generic_entry<XD, WD, BF16>(add);
+    case F32: return generic_entry<XD, WD, F32>(add);
+    default: return nullptr;
+  }
+}
+
+inline const void* generic_table(int xd, int wd, int od, bool add) {
+  if (wd == BF16 && xd == BF16) return generic_by_out<BF16, BF16>(od, add);
+  if (wd == BF16 && xd == F32) return generic_by_out<F32, BF16>(od, add);
+  if (wd == F16 && xd == F16) return generic_by_out<F16, F16>(od, add);
+  if (wd == F16 && xd == F32) return generic_by_out<F32, F16>(od, add);
+  return nullptr;
+}
+
+}  // namespace dev
+}  // namespace sgmv

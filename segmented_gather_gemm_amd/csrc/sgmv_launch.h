@@ -47,20 +47,17 @@ struct Params {
   SliceDesc s[kMaxSlices];
 };
 
-// Kernel variant: dtypes, accumulate flag and the number of 32-wide rank
-// steps held in registers (K <= 32 * ksteps).
-struct Variant {
-  int xd, wd, od;
-  bool add;
-  int ksteps;
-};
-
-// Returns the kernel entry for a variant, or nullptr if none is built.
-const void* kernel_for(const Variant& v);
-
-// Launch `kernel` with `grid` workgroups of kThreads and `lds_bytes` of
-// dynamic LDS.  Returns the HIP status of the launch.
-hipError_t launch(const void* kernel, const Params& p, int grid, size_t lds_bytes,
-                  hipStream_t stream);
+// Kernel entries, by dtype codes (F16 = 0, BF16 = 1, F32 = 2), accumulate
+// flag and, for the fast kernels, the number of 32-wide rank steps they hold
+// in registers (rank <= 32 * steps).  nullptr: no such kernel.
+//
+// Fast kernels need rank % 8 == 0, every slice width % 8 == 0 and 16-byte
+// aligned input rows, weight rows and output column groups; the generic
+// kernel takes any shape, stride and alignment.
+const void* fast_kernel_ks1(int xd, int wd, int od, bool add);
+const void* fast_kernel_ks2(int xd, int wd, int od, bool add);
+const void* fast_kernel_ks4(int xd, int wd, int od, bool add);
+const void* fast_kernel_ks8(int xd, int wd, int od, bool add);
+const void* generic_kernel(int xd, int wd, int od, bool add);
 
 }  // namespace sgmv

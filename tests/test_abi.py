@@ -64,7 +64,8 @@ CASES = [
     (dict(out=Matrix(FAKE, 7, 10, 192, 192)), INVALID, "dtype"),
     (dict(w=Stack(FAKE, F32, 2, 64, 8)), UNSUPPORTED, "float16 or bfloat16"),
     (dict(x=Matrix(FAKE, BF16, 10, 8, 8)), UNSUPPORTED, "dtype"),
-    (dict(x=Matrix(FAKE, F16, 10, 300, 300), w=Stack(FAKE, F16, 2, 64, 300)), UNSUPPORTED, "rank"),
+    (dict(x=Matrix(FAKE, F16, 1 << 31, 8, 8), out=Matrix(FAKE, F16, 1 << 31, 192, 192)),
+     UNSUPPORTED, "tokens"),
     (dict(meta=(0, FAKE, FAKE)), INVALID, "metadata"),
     (dict(out=Matrix(0, F16, 10, 192, 192)), INVALID, "output data"),
     (dict(x=Matrix(0, F16, 10, 8, 8)), INVALID, "null data"),

@@ -1,0 +1,36 @@
+"""HIP-graph capture of the C-ABI calls: a captured sgmv_expand_slice /
+sgmv_expand_multi_slice replayed several times, with eager work and
+synchronisation between replays, gives the eager result on every replay
+(the library records no memset or allocation, only kernel launches)."""
+import numpy as np
+import pytest
+
+import sgmv_workloads as W
+from gpu_util import DeviceWorkload, assert_parity, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("multi", [False, True])
+def test_graph_replays_match_eager(multi):
+    import torch
+    extra = [(300, 70)] if multi else []
+    wl = W.custom([40, 3, 0, 19, 70], [1, 0, 1, -1, 0], K=32, N=256, H=400, off=16, L=2,
+                  add=True, seed=31, extra_slices=extra)
+    dw = DeviceWorkload(wl)
+    run = dw.run_multi if multi else dw.run_all_single
+    eager = to_host_bits(run(dw.fresh_out()))
+    assert_parity(wl, eager)
+    out = dw.fresh_out()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run(out)
+    for replay in range(4):
+        out.copy_(dw.out0)                       # eager reset between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), eager), f"replay {replay}"
+        other = to_host_bits(run(dw.fresh_out()))  # eager work in between
+        torch.cuda.synchronize()
+        assert np.array_equal(other, eager)
