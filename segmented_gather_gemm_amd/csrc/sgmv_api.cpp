@@ -19,6 +19,14 @@
 
 namespace {
 
+// Row tiles (16 rows each) per band of the fast kernels' walk: each XCD
+// covers its column group band by band, so a band's input rows and weight
+// tiles are re-read from its L2 rather than from memory.
+#ifndef SGMV_BAND_TILES
+#define SGMV_BAND_TILES 64
+#endif
+constexpr int32_t kBandTiles = SGMV_BAND_TILES;
+
 thread_local std::string g_error;
 
 sgmv_status fail(sgmv_status status, const char* fmt, ...) {
@@ -186,6 +194,8 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   p.lens = lens;
   p.idx = idx;
   p.out_stride = out.row_stride;
+  p.out_row_bytes = out.row_stride * elem_bytes(out.dtype);
+  p.band_tiles = kBandTiles;
   p.T = out.rows;
   p.batches = (int32_t)batches;
   p.L = (int32_t)L;
@@ -200,6 +210,7 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
     d.x = s.inputs.data;
     d.w = s.lora_b.data;
     d.x_stride = s.inputs.row_stride;
+    d.x_row_bytes = s.inputs.row_stride * elem_bytes(s.inputs.dtype);
     d.n = s.slice_size;
     d.offset = s.slice_offset;
     d.tile_begin = tile_begin;
@@ -213,11 +224,15 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
       d.flags |= kVecOut;
   }
 
-  bool fast_shapes = true;
+  // Fast kernels: whole 16-byte blocks everywhere, and 16 rows of inputs or
+  // output spanning less than 2 GiB (their buffer offsets are 32-bit).
+  bool fast_shapes = 16 * p.out_row_bytes < (int64_t(1) << 31);
   for (int i = 0; i < num_slices; ++i) {
     if (slices[i].slice_size == 0) continue;
     const int32_t need = kVecX | kVecW | kVecOut;
-    if (slices[i].slice_size % 8 != 0 || (p.s[i].flags & need) != need) fast_shapes = false;
+    if (slices[i].slice_size % 8 != 0 || (p.s[i].flags & need) != need ||
+        16 * p.s[i].x_row_bytes >= (int64_t(1) << 31))
+      fast_shapes = false;
   }
   const void* kernel =
       pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast_shapes);

@@ -391,6 +391,159 @@ __device__ __forceinline__ int64_t weight_row(int64_t col0, int s, int j) {
 // Fast kernel.
 // ---------------------------------------------------------------------------
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): a 16-byte access at an
+// offset past `bytes` reads zero and writes nothing.  The fourth word selects
+// 32-bit data format, as untyped buffer accesses require on gfx9.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Lane offset that lies past every resource this kernel builds (the host
+// only picks the fast kernel when 16 rows of inputs or output span < 2 GiB).
+constexpr uint32_t kOut = 0x80000000u;
+
+template <int D>
+__device__ __forceinline__ void buf_load8(rsrc_t r, uint32_t off, u32x4* dst) {
+  dst[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  if constexpr (D == F32)
+    dst[1] = __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0));
+}
+
+template <int D>
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const u32x4* src) {
+  __builtin_amdgcn_raw_buffer_store_b128(src[0], r, (int)off, 0, 0);
+  if constexpr (D == F32) __builtin_amdgcn_raw_buffer_store_b128(src[1], r, (int)(off + 16), 0, 0);
+}
+
+// One unit of the fast kernel: scalar (wave-uniform) resources over the
+// unit's valid input rows and the wave's output block, and the weight tile
+// it needs.
+struct FastUnit {
+  rsrc_t x;       // inputs: the tile's valid rows (rows past the segment read zero)
+  rsrc_t o;       // output: from (row0, off + col0) to the end of the last valid row's block
+  int64_t a;      // adapter
+  int64_t col0;   // first of the wave's 64 columns, within the slice
+  int32_t n_rem;  // slice columns left from col0 (<= 0: the wave has none)
+  int tile;       // global column tile
+  int si;         // slice
+};
+
+// Walk of the fast kernels over their unit range.  Order: column group
+// (kColumnGroups contiguous ranges of column tiles, one per XCD), then band
+// of band_tiles row tiles, then column tile, then row tile.  Within a run of
+// row tiles of one segment under one column tile, a step only advances row
+// offsets; segment, tile and band changes re-read the LDS table.
+struct Walk {
+  const Params& p;
+  const SegTable& tab;
+  int64_t RT;       // row tiles
+  int wave;
+  int ob;           // bytes per output element
+  // position
+  int gi, tile_lo, tile_hi;   // column group and its tiles [lo, hi)
+  int64_t band_lo, band_hi;   // band's row tiles [lo, hi)
+  int band_b;                 // segment holding band_lo
+  int tile, si, b;
+  int64_t rt;
+  int64_t seg_tile_end;       // first row tile after segment b
+  // run state for (tile, b) at row tile rt
+  const char* x_row;          // inputs: first row of the row tile
+  const char* o_row;          // output: first row, first column of the wave's block
+  int64_t rows_left;          // segment rows from the tile's first row on
+  int64_t x_step, o_step;     // bytes per row tile
+  int64_t a, col0;
+  int32_t n_rem;
+
+  __device__ __forceinline__ int group_tile(int g) const {
+    return (int)((int64_t)p.total_tiles * g / kColumnGroups);
+  }
+
+  __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, int64_t rt_total,
+                                  int wave_, int ob_, int64_t u)
+      : p(p_), tab(t), RT(rt_total), wave(wave_), ob(ob_) {
+    // group: units of group g start at group_tile(g) * RT
+    gi = 0;
+    while (gi + 1 < kColumnGroups && (int64_t)group_tile(gi + 1) * RT <= u) ++gi;
+    tile_lo = group_tile(gi);
+    tile_hi = group_tile(gi + 1);
+    const int64_t nt = tile_hi - tile_lo;
+    const int64_t v = u - (int64_t)tile_lo * RT;
+    const int64_t RB = p.band_tiles;
+    const int64_t nb = (RT + RB - 1) / RB;
+    int64_t bi = v / (RB * nt);
+    if (bi > nb - 1) bi = nb - 1;
+    band_lo = bi * RB;
+    band_hi = band_lo + RB < RT ? band_lo + RB : RT;
+    const int64_t w = v - band_lo * nt;
+    const int64_t rb = band_hi - band_lo;
+    tile = tile_lo + (int)(w / rb);
+    rt = band_lo + w % rb;
+    band_b = last_at_most(tab.tile_start, p.batches + 1, band_lo);
+    while (uniform(tab.tile_start[band_b + 1]) <= band_lo) ++band_b;
+    b = band_b;
+    while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+    si = slice_of(p, tile);
+    new_run();
+  }
+
+  __device__ __forceinline__ void new_run() {
+    const SliceDesc& S = p.s[si];
+    col0 = (int64_t)(tile - S.tile_begin) * kTileCols + wave * kWaveCols;
+    const int64_t n_left = S.n - col0;
+    n_rem = n_left <= 0 ? 0 : (n_left > kWaveCols ? kWaveCols : (int32_t)n_left);
+    const int64_t seg_row = uniform(tab.seg_row[b]);
+    const int64_t seg_end = uniform(tab.seg_end[b]);
+    a = uniform(tab.seg_lora[b]);
+    seg_tile_end = uniform(tab.tile_start[b + 1]);
+    const int64_t row0 = seg_row + (rt - uniform(tab.tile_start[b])) * kTileRows;
+    rows_left = seg_end - row0;
+    x_step = kTileRows * S.x_row_bytes;
+    o_step = kTileRows * p.out_row_bytes;
+    x_row = static_cast<const char*>(S.x) + row0 * S.x_row_bytes;
+    o_row = static_cast<const char*>(p.out) + row0 * p.out_row_bytes + (S.offset + col0) * ob;
+  }
+
+  __device__ __forceinline__ void advance() {
+    ++rt;
+    if (rt == band_hi) {
+      ++tile;
+      if (tile == tile_hi) {  // next band of the group (or next group)
+        band_lo = band_hi;
+        if (band_lo == RT) {
+          do {
+            ++gi;
+            tile_lo = group_tile(gi);
+            tile_hi = group_tile(gi + 1);
+          } while (tile_lo == tile_hi && gi + 1 < kColumnGroups);
+          band_lo = 0;
+          b = 0;
+        }
+        band_hi = band_lo + p.band_tiles < RT ? band_lo + p.band_tiles : RT;
+        tile = tile_lo;
+        while (uniform(tab.tile_start[b + 1]) <= band_lo) ++b;
+        band_b = b;
+      }
+      rt = band_lo;
+      b = band_b;
+      si = slice_of(p, tile);
+      while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+      new_run();
+    } else if (rt == seg_tile_end) {
+      ++b;
+      while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+      new_run();
+    } else {
+      x_row += x_step;
+      o_row += o_step;
+      rows_left -= kTileRows;
+    }
+  }
+};
+
 // Loads of one unit that are in flight while the previous unit computes.
 template <int XD, int OD, int KS>
 struct Stage {
@@ -410,69 +563,74 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   unit_range(p, U, &u_begin, &u_end);
   if (u_begin >= u_end) return;
 
+  constexpr int xb = XD == F32 ? 4 : 2;
+  constexpr int ob = OD == F32 ? 4 : 2;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);  // resources built from it stay scalar
   const int g = lane >> 4;   // lane group: rank sub-block / column group
   const int j = lane & 15;   // token of the tile / MFMA row of the A operand
   const int K = p.K;
+  const int64_t os_bytes = p.out_row_bytes;
+
   // Rank step ks covers rank [32 ks, 32 ks + 32); lane group g holds the
   // 8-element block 32 ks + 8 g (the same grouping as the generic kernel, so
-  // both give bit-identical results).  Blocks past K (when K is not a
-  // multiple of 32 * KS) are zero in both operands.
-  const bool k_tail = K < 32 * KS;
-  bool kvalid[KS];
+  // both give bit-identical results).  Blocks past K read zero.
+  // Loop-invariant lane offsets: output (row j, column group 32 q + 8 g of
+  // the wave's block) and weights (row weight_row(0, s, j) of the tile).
+  uint32_t o_off[2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kvalid[ks] = 32 * ks + 8 * g < K;
-
-  Cursor cur_pos(p, tab, RT, u_begin);
-
-  // Weight tile of a unit.  Every lane loads: rows past the slice width read
-  // the slice's last row and rank blocks past K read block 0 (masked to zero
-  // when the tile is installed).
-  auto load_w = [&](u32x4 (&w)[4][KS], const Unit& u) __attribute__((always_inline)) {
-    const SliceDesc& S = p.s[u.si];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      int64_t n = weight_row(u.col0, s, j);
-      n = n < S.n ? n : S.n - 1;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kb = kvalid[ks] ? 32 * ks + 8 * g : 0;
-        load_vec8<WD>(S.w, (u.a * S.n + n) * K + kb, &w[s][ks]);
-      }
-    }
+  for (int q = 0; q < 2; ++q) o_off[q] = (uint32_t)(j * os_bytes) + (32 * q + 8 * g) * ob;
+  auto w_off = [&](int s, int ks) __attribute__((always_inline)) -> uint32_t {
+    const int kb = 32 * ks + 8 * g;
+    return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
   };
-  auto mask_w = [&](u32x4 (&dst)[4][KS], const u32x4 (&src)[4][KS])
-                    __attribute__((always_inline)) {
+  // Input offsets depend on the slice's row stride.
+  uint32_t x_off[KS];
+  int x_si = -1;
+  auto set_x_off = [&](int si) __attribute__((always_inline)) {
+    const int64_t xs_bytes = p.s[si].x_row_bytes;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kb = 32 * ks + 8 * g;
+      x_off[ks] = kb < K ? (uint32_t)(j * xs_bytes + kb * xb) : kOut;
+    }
+    x_si = si;
+  };
+
+  Walk pos(p, tab, RT, wave, ob, u_begin);
+  auto next_unit = [&]() __attribute__((always_inline)) -> FastUnit {
+    const int64_t rows = pos.rows_left < kTileRows ? pos.rows_left : kTileRows;
+    FastUnit u;
+    u.tile = pos.tile;
+    u.si = pos.si;
+    u.a = pos.a;
+    u.col0 = pos.col0;
+    u.n_rem = pos.n_rem;
+    u.x = make_rsrc(pos.x_row, rows * p.s[pos.si].x_row_bytes);
+    u.o = make_rsrc(pos.o_row, u.n_rem > 0 ? (rows - 1) * p.out_row_bytes + (int64_t)u.n_rem * ob : 0);
+    return u;
+  };
+
+  auto load_w = [&](u32x4 (&w)[4][KS], const FastUnit& u) __attribute__((always_inline)) {
+    const SliceDesc& S = p.s[u.si];
+    const rsrc_t r = make_rsrc(static_cast<const char*>(S.w) + (u.a * S.n + u.col0) * K * 2,
+                               (int64_t)u.n_rem * K * 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        dst[s][ks] = (!k_tail || kvalid[ks]) ? src[s][ks] : u32x4{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < KS; ++ks) buf_load8<WD>(r, w_off(s, ks), &w[s][ks]);
   };
-  // Inputs and prior output of a unit.  Rows outside the segment read the
-  // segment's first row, column groups past the slice read group 0; their
-  // values are never stored.
-  auto load_stage = [&](Stage<XD, OD, KS>& st, const Unit& u) __attribute__((always_inline)) {
-    const SliceDesc& S = p.s[u.si];
-    const int64_t t = u.row_ok ? u.t : u.seg_t0;
+  auto load_stage = [&](Stage<XD, OD, KS>& st, const FastUnit& u) __attribute__((always_inline)) {
+    if (u.si != x_si) set_x_off(u.si);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int kb = kvalid[ks] ? 32 * ks + 8 * g : 0;
-      load_vec8<XD>(S.x, t * S.x_stride + kb, &st.x[ks * raw_vecs<XD>()]);
-    }
+    for (int ks = 0; ks < KS; ++ks) buf_load8<XD>(u.x, x_off[ks], &st.x[ks * raw_vecs<XD>()]);
     if constexpr (ADD) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int64_t c = u.col0 + 32 * q + 8 * g;
-        c = c < S.n ? c : 0;
-        load_vec8<OD>(p.out, t * p.out_stride + S.offset + c, &st.o[q * raw_vecs<OD>()]);
-      }
+      for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, o_off[q], &st.o[q * raw_vecs<OD>()]);
     }
   };
   auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][KS],
-                           const Unit& u) __attribute__((always_inline)) {
-    const SliceDesc& S = p.s[u.si];
+                           const FastUnit& u) __attribute__((always_inline)) {
     f32x4 acc[4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -483,8 +641,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 xo = x_operand<XD, WD>(&st.x[ks * raw_vecs<XD>()]);
-      if (k_tail && !kvalid[ks]) xo = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 xo = x_operand<XD, WD>(&st.x[ks * raw_vecs<XD>()]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[s] = mfma<WD>(w[s][ks], xo, acc[s]);
     }
@@ -495,25 +652,24 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
                           acc[2 * q + 1][3]};
       u32x4 raw[raw_vecs<OD>()];
       out_pack<OD>(v, raw);
-      const int64_t c = u.col0 + 32 * q + 8 * g;
-      if (u.row_ok && c < S.n) store_vec8<OD>(p.out, u.t * p.out_stride + S.offset + c, raw);
+      // Column groups past the slice (only in a slice's last column tile)
+      // take an out-of-range offset; rows past the segment already lie
+      // outside the resource.
+      const uint32_t off = 32 * q + 8 * g < u.n_rem ? o_off[q] : kOut;
+      buf_store8<OD>(u.o, off, raw);
     }
   };
 
   // Software pipeline (see the file comment).  wA holds the weight tile of
   // the unit being computed; with double buffering a changed tile for the
-  // next unit is loaded into wB one unit ahead and installed (masked) into
-  // wA before that unit computes.
+  // next unit is loaded into wB one unit ahead and copied into wA before
+  // that unit computes.
   constexpr bool kDoubleW = KS <= SGMV_DOUBLE_W_MAX_KSTEPS;
   u32x4 wA[4][KS], wB[4][kDoubleW ? KS : 1];
   Stage<XD, OD, KS> sA, sB;
 
-  Unit cur = cur_pos.decode(wave, j);
-  {
-    u32x4 wl[4][KS];
-    load_w(wl, cur);
-    mask_w(wA, wl);
-  }
+  FastUnit cur = next_unit();
+  load_w(wA, cur);
   int w_tile = cur.tile;
   int64_t w_a = cur.a;
   bool w_pending = false;
@@ -524,15 +680,18 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
                   __attribute__((always_inline)) -> bool {
     if constexpr (kDoubleW) {
       if (w_pending) {
-        mask_w(wA, wB);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) wA[s][ks] = wB[s][ks];
         w_pending = false;
       }
     }
     const bool more = u + 1 < u_end;
-    Unit nxt = cur;
+    FastUnit nxt = cur;
     if (more) {
-      cur_pos.advance();
-      nxt = cur_pos.decode(wave, j);
+      pos.advance();
+      nxt = next_unit();
     }
     const bool wswitch = nxt.tile != w_tile || nxt.a != w_a;
     if constexpr (kDoubleW) {
@@ -549,9 +708,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     compute_store(s_cur, wA, cur);
     if constexpr (!kDoubleW) {
       if (wswitch) {
-        u32x4 wl[4][KS];
-        load_w(wl, nxt);
-        mask_w(wA, wl);
+        load_w(wA, nxt);
         w_tile = nxt.tile;
         w_a = nxt.a;
       }

@@ -13,6 +13,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kWaveCols = 64;          // output columns one wavefront owns per unit
 constexpr int kTileCols = kWaves * kWaveCols;  // columns per work unit (256)
 constexpr int kTileRows = 16;          // rows per work unit (one MFMA column block)
+constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk order
 
 // Bits of SliceDesc::flags: 16-byte vector access is legal for ...
 enum : int32_t {
@@ -25,6 +26,7 @@ struct SliceDesc {
   const void* x;        // inputs (T, K), row stride x_stride elements
   const void* w;        // lora_b (L, N, K) contiguous
   int64_t x_stride;
+  int64_t x_row_bytes;  // x_stride * sizeof(input element)
   int64_t n;            // slice_size
   int64_t offset;       // slice_offset
   int32_t tile_begin;   // first global column-tile index of this slice
@@ -37,6 +39,7 @@ struct Params {
   const int64_t* lens;
   const int64_t* idx;
   int64_t out_stride;   // elements
+  int64_t out_row_bytes;  // out_stride * sizeof(output element)
   int64_t T;            // rows of out (and of every inputs matrix)
   int32_t batches;
   int32_t L;            // lora_num
@@ -44,6 +47,7 @@ struct Params {
   int32_t num_slices;
   int32_t total_tiles;  // column tiles over all slices
   int32_t grid;         // workgroups launched
+  int32_t band_tiles;   // row tiles per band of the fast kernels' walk
   SliceDesc s[kMaxSlices];
 };
 
