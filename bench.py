@@ -33,8 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak, GB/s
 DEFAULT_WORKLOAD = "llama7b_q_proj"
-KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemm_amd", "csrc", f)
-                  for f in ("sgmv_kernels.hip", "sgmv_launch.h", "sgmv_api.cpp")]
+CSRC = os.path.join(ROOT, "segmented_gather_gemm_amd", "csrc")
 
 
 def log(msg):
@@ -42,10 +41,13 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of every library source file (kernels, launch and entry points)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -185,8 +187,9 @@ def copy_ceiling(nbytes, device, reps=20):
 
 
 def traffic_from_profiles(workload, ksha):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    """Measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a
+    plain copy) from a committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -290,7 +293,8 @@ def main():
     gbs = model_bytes / sec / 1e9
     tokens_s = wl.T / sec
     ksha = kernel_source_hash()
-    traffic = traffic_from_profiles(args.workload, ksha)
+    traffic_bytes = traffic_from_profiles(args.workload, ksha)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / sec / 1e9, 2)
     log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
         f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
 
@@ -344,7 +348,8 @@ def main():
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "expand_kernel",
+            "traffic_bytes_per_launch": traffic_bytes,
+            "kernel": "expand_fast",
             "kernel_source_sha256_16": ksha,
         },
         "copy_ceiling_gbs": ceiling,

@@ -1,0 +1,46 @@
+"""Host-side parts of the benchmark: the byte model against a hand count,
+the source hash, and the refusal of a multi-GPU run (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import sgmv_workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_byte_model_hand_count():
+    # 3 segments: 5 rows adapter 1, 7 rows index -1, 2 rows adapter 1; rank 16,
+    # slice 64 of bf16, accumulate: active rows 7, one distinct adapter.
+    wl = W.custom([5, 7, 2], [1, -1, 1], K=16, N=64, H=80, off=8, L=2, add=True)
+    total, t_act, distinct = bench.byte_model(wl)
+    assert (t_act, distinct) == (7, 1)
+    assert total == 7 * 16 * 2 + 1 * 64 * 16 * 2 + 7 * 64 * 2 * 2
+
+
+def test_byte_model_multi_slice_and_fp32_input():
+    wl = W.custom([4, 4], [0, 1], K=8, N=16, H=64, off=0, L=2, x_dtype="f32", add=False,
+                  extra_slices=[(32, 8)])
+    total, t_act, distinct = bench.byte_model(wl)
+    per_slice = lambda n: 8 * 8 * 4 + 2 * n * 8 * 2 + 8 * n * 2
+    assert total == per_slice(16) + per_slice(8)
+
+
+def test_named_workload_byte_counts():
+    total, t_act, distinct = bench.byte_model(W.llama7b_q_proj(0))
+    assert (t_act, distinct) == (1279, 3)
+    assert total == 1279 * 16 * 2 + 3 * 4096 * 16 * 2 + 1279 * 4096 * 2 * 2
+
+
+def test_kernel_source_hash_is_stable():
+    assert bench.kernel_source_hash() == bench.kernel_source_hash()
+    assert len(bench.kernel_source_hash()) == 16
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
