@@ -544,10 +544,14 @@ struct Walk {
   }
 };
 
-// Loads of one unit that are in flight while the previous unit computes.
+// Loads of one unit that are in flight while the previous unit computes:
+// the rank chunks of the input tile this wave loads for the workgroup
+// (chunk ks = wave + 4 i, 16 rows x 32 rank in MFMA operand order) and the
+// prior output of the wave's own block.
 template <int XD, int OD, int KS>
 struct Stage {
-  u32x4 x[KS * raw_vecs<XD>()];   // this lane's rank blocks of its token
+  static constexpr int kChunks = (KS + kWaves - 1) / kWaves;
+  u32x4 x[kChunks * raw_vecs<XD>()];
   u32x4 o[2 * raw_vecs<OD>()];    // prior output: two 8-column groups
 };
 
@@ -584,15 +588,20 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     const int kb = 32 * ks + 8 * g;
     return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
   };
-  // Input offsets depend on the slice's row stride.
-  uint32_t x_off[KS];
+  // Input tile: the workgroup shares it through LDS.  Rank chunk ks (16 rows
+  // x 32 rank, one 16-byte block per lane in MFMA operand order) is loaded
+  // by wave ks % 4 and read by all four; offsets depend on the slice's row
+  // stride.
+  constexpr int kChunks = Stage<XD, OD, KS>::kChunks;
+  __shared__ u32x4 x_lds[2][KS][64];
+  uint32_t x_off[kChunks];
   int x_si = -1;
   auto set_x_off = [&](int si) __attribute__((always_inline)) {
     const int64_t xs_bytes = p.s[si].x_row_bytes;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int kb = 32 * ks + 8 * g;
-      x_off[ks] = kb < K ? (uint32_t)(j * xs_bytes + kb * xb) : kOut;
+    for (int i = 0; i < kChunks; ++i) {
+      const int kb = 32 * (wave + kWaves * i) + 8 * g;
+      x_off[i] = kb < K ? (uint32_t)(j * xs_bytes + kb * xb) : kOut;
     }
     x_si = si;
   };
@@ -623,14 +632,25 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   auto load_stage = [&](Stage<XD, OD, KS>& st, const FastUnit& u) __attribute__((always_inline)) {
     if (u.si != x_si) set_x_off(u.si);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) buf_load8<XD>(u.x, x_off[ks], &st.x[ks * raw_vecs<XD>()]);
+    for (int i = 0; i < kChunks; ++i)
+      if (wave + kWaves * i < KS) buf_load8<XD>(u.x, x_off[i], &st.x[i * raw_vecs<XD>()]);
     if constexpr (ADD) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, o_off[q], &st.o[q * raw_vecs<OD>()]);
     }
   };
+  // Publish this wave's chunks of a unit's input tile to LDS buffer `buf`
+  // (float32 inputs are rounded to the weight dtype here) and wait for the
+  // other waves' chunks.
+  auto publish_x = [&](const Stage<XD, OD, KS>& st, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      if (wave + kWaves * i < KS)
+        x_lds[buf][wave + kWaves * i][lane] = x_operand<XD, WD>(&st.x[i * raw_vecs<XD>()]);
+    __syncthreads();
+  };
   auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][KS],
-                           const FastUnit& u) __attribute__((always_inline)) {
+                           const FastUnit& u, int buf) __attribute__((always_inline)) {
     f32x4 acc[4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -641,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 xo = x_operand<XD, WD>(&st.x[ks * raw_vecs<XD>()]);
+      const u32x4 xo = x_lds[buf][ks][lane];
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[s] = mfma<WD>(w[s][ks], xo, acc[s]);
     }
@@ -676,8 +696,13 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   load_stage(sA, cur);
 
   int64_t u = u_begin;
-  auto step = [&](Stage<XD, OD, KS>& s_cur, Stage<XD, OD, KS>& s_nxt)
+  // One step: publish the current unit's input tile to LDS buffer `buf`,
+  // issue the next unit's loads, then compute and store the current unit.
+  // The LDS buffers alternate; the barrier in publish_x also orders every
+  // wave's reads of a buffer before the next write to it.
+  auto step = [&](Stage<XD, OD, KS>& s_cur, Stage<XD, OD, KS>& s_nxt, int buf)
                   __attribute__((always_inline)) -> bool {
+    publish_x(s_cur, buf);
     if constexpr (kDoubleW) {
       if (w_pending) {
 #pragma unroll
@@ -705,7 +730,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     load_stage(s_nxt, nxt);
     // Keep the next unit's loads ahead of this unit's waits and arithmetic.
     __builtin_amdgcn_sched_barrier(0);
-    compute_store(s_cur, wA, cur);
+    compute_store(s_cur, wA, cur, buf);
     if constexpr (!kDoubleW) {
       if (wswitch) {
         load_w(wA, nxt);
@@ -718,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     cur = nxt;
     return true;
   };
-  while (step(sA, sB) && step(sB, sA)) {
+  while (step(sA, sB, 0) && step(sB, sA, 1)) {
   }
 }
 
