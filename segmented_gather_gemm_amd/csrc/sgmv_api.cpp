@@ -179,6 +179,14 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
     return SGMV_OK;  // nothing to do
   }
   if (total_tiles > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "output window too wide");
+  // Upper bound on work units from host-known sizes only: active segments are
+  // disjoint inside [0, T), so row tiles <= ceil(T / 16) + min(batches, T).
+  // The kernels' scheduler counts units in 32 bits.
+  const int64_t row_tiles = (out.rows + kTileRows - 1) / kTileRows +
+                            (batches < out.rows ? batches : out.rows);
+  const int64_t units = row_tiles * total_tiles;
+  if (units > INT32_MAX)
+    return fail(SGMV_ERR_UNSUPPORTED, "more than 2^31-1 work units (16-row x 256-column tiles)");
   if (!out.data) return fail(SGMV_ERR_INVALID_ARGUMENT, "output data pointer is null");
   if (!start || !lens || !idx)
     return fail(SGMV_ERR_INVALID_ARGUMENT, "segment metadata pointer is null");
@@ -238,11 +246,6 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
       pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast_shapes);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no kernel for this dtype combination");
 
-  // Upper bound on work units from host-known sizes only: active segments are
-  // disjoint inside [0, T), so row tiles <= ceil(T / 16) + min(batches, T).
-  const int64_t row_tiles = (out.rows + kTileRows - 1) / kTileRows +
-                            (batches < out.rows ? batches : out.rows);
-  const int64_t units = row_tiles * total_tiles;
   const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);  // segment table
   int capacity = 0;
   hipError_t e = device_capacity(kernel, lds, &capacity);

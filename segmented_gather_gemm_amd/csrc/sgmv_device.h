@@ -246,6 +246,22 @@ struct SegTable {
   int32_t* seg_lora;
 };
 
+// Kernel arguments live in memory and the compiler fetches each scalar on
+// first use, so the scheduler's chain of uses would pay one dependent round
+// trip per field.  Touch every 64-byte line of the argument block at kernel
+// entry so all of them are fetched together; later reads hit the scalar
+// cache.
+__device__ __forceinline__ void prefetch_params(const Params& p) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&p);
+  constexpr int kLast = (int)(sizeof(Params) / 4) - 1;
+  static_assert(sizeof(Params) <= 576, "touch list below covers 9 lines");
+  asm volatile("" ::"s"(w[0]), "s"(w[16 < kLast ? 16 : kLast]), "s"(w[32 < kLast ? 32 : kLast]),
+               "s"(w[48 < kLast ? 48 : kLast]), "s"(w[64 < kLast ? 64 : kLast]),
+               "s"(w[80 < kLast ? 80 : kLast]), "s"(w[96 < kLast ? 96 : kLast]),
+               "s"(w[112 < kLast ? 112 : kLast]), "s"(w[128 < kLast ? 128 : kLast]),
+               "s"(w[kLast]));
+}
+
 __device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
   SegTable t;
   t.tile_start = lds;
@@ -257,7 +273,7 @@ __device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
 
 // Fill the table (every thread of the workgroup takes part); returns the
 // total number of row tiles (wave-uniform).
-__device__ __forceinline__ int64_t build_tile_table(const Params& p, const SegTable& tab,
+__device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTable& tab,
                                                     int32_t* wave_total) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -298,19 +314,26 @@ __device__ __forceinline__ int64_t build_tile_table(const Params& p, const SegTa
   return uniform(carry);
 }
 
-// This workgroup's contiguous range [begin, end) of the U units; workgroup
-// ids are remapped so each XCD gets one contiguous eighth of the range.
-__device__ __forceinline__ void unit_range(const Params& p, int64_t U, int64_t* begin,
-                                           int64_t* end) {
-  const int bid = blockIdx.x;
-  const int lw = (p.grid >= 16 && (p.grid & 7) == 0) ? (bid & 7) * (p.grid >> 3) + (bid >> 3)
-                                                      : bid;
-  *begin = U * lw / p.grid;
-  *end = U * (lw + 1) / p.grid;
+// Unit counts, unit indices and row-tile counts are below 2^31 (the host
+// refuses larger problems), so the scheduler's arithmetic is 32-bit: 64-bit
+// division is a long scalar sequence that every wave of a compute unit would
+// queue for on the shared scalar ALU.
+//
+// This workgroup's contiguous range [begin, end) of the U units (sizes differ
+// by at most one); workgroup ids are remapped so each XCD gets one contiguous
+// eighth of the range.
+__device__ __forceinline__ void unit_range(const Params& p, uint32_t U, uint32_t* begin,
+                                           uint32_t* end) {
+  const uint32_t bid = blockIdx.x;
+  const uint32_t G = (uint32_t)p.grid;
+  const uint32_t lw = (G >= 16 && (G & 7) == 0) ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+  const uint32_t q = U / G, r = U - q * G;
+  *begin = lw * q + (lw < r ? lw : r);
+  *end = *begin + q + (lw < r ? 1 : 0);
 }
 
 // Largest b in [0, n) with table[b] <= key (table non-decreasing, table[0] = 0).
-__device__ __forceinline__ int last_at_most(const int32_t* table, int n, int64_t key) {
+__device__ __forceinline__ int last_at_most(const int32_t* table, int n, int32_t key) {
   int lo = 0, hi = n;  // answer in [lo, hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -341,14 +364,14 @@ struct Unit {
 struct Cursor {
   const Params& p;
   const SegTable& tab;
-  int64_t RT, rt;
+  int32_t RT, rt;
   int tile, b, si;
 
-  __device__ __forceinline__ Cursor(const Params& p_, const SegTable& t, int64_t rt_total,
-                                    int64_t u)
+  __device__ __forceinline__ Cursor(const Params& p_, const SegTable& t, int32_t rt_total,
+                                    uint32_t u)
       : p(p_), tab(t), RT(rt_total) {
-    tile = (int)(u / RT);
-    rt = u - (int64_t)tile * RT;
+    tile = (int)(u / (uint32_t)RT);
+    rt = (int32_t)(u - (uint32_t)tile * (uint32_t)RT);
     b = last_at_most(tab.tile_start, p.batches + 1, rt);
     while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
     si = slice_of(p, tile);
@@ -373,7 +396,7 @@ struct Cursor {
     u.si = si;
     u.col0 = (int64_t)(tile - S.tile_begin) * kTileCols + wave * kWaveCols;
     u.a = uniform(tab.seg_lora[b]);
-    u.t = seg_row + (rt - uniform(tab.tile_start[b])) * kTileRows + j;
+    u.t = seg_row + (int64_t)(rt - uniform(tab.tile_start[b])) * kTileRows + j;
     u.row_ok = u.t < seg_end;
     u.seg_t0 = seg_row;
     return u;
@@ -440,16 +463,16 @@ struct FastUnit {
 struct Walk {
   const Params& p;
   const SegTable& tab;
-  int64_t RT;       // row tiles
+  int32_t RT;       // row tiles
   int wave;
   int ob;           // bytes per output element
   // position
   int gi, tile_lo, tile_hi;   // column group and its tiles [lo, hi)
-  int64_t band_lo, band_hi;   // band's row tiles [lo, hi)
+  int32_t band_lo, band_hi;   // band's row tiles [lo, hi)
   int band_b;                 // segment holding band_lo
   int tile, si, b;
-  int64_t rt;
-  int64_t seg_tile_end;       // first row tile after segment b
+  int32_t rt;
+  int32_t seg_tile_end;       // first row tile after segment b
   // run state for (tile, b) at row tile rt
   const char* x_row;          // inputs: first row of the row tile
   const char* o_row;          // output: first row, first column of the wave's block
@@ -459,29 +482,31 @@ struct Walk {
   int32_t n_rem;
 
   __device__ __forceinline__ int group_tile(int g) const {
-    return (int)((int64_t)p.total_tiles * g / kColumnGroups);
+    return (int)((uint32_t)p.total_tiles * (uint32_t)g / kColumnGroups);
   }
 
-  __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, int64_t rt_total,
-                                  int wave_, int ob_, int64_t u)
+  __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, int32_t rt_total,
+                                  int wave_, int ob_, uint32_t u)
       : p(p_), tab(t), RT(rt_total), wave(wave_), ob(ob_) {
     // group: units of group g start at group_tile(g) * RT
+    const uint32_t rt_n = (uint32_t)RT;
     gi = 0;
-    while (gi + 1 < kColumnGroups && (int64_t)group_tile(gi + 1) * RT <= u) ++gi;
+    while (gi + 1 < kColumnGroups && (uint32_t)group_tile(gi + 1) * rt_n <= u) ++gi;
     tile_lo = group_tile(gi);
     tile_hi = group_tile(gi + 1);
-    const int64_t nt = tile_hi - tile_lo;
-    const int64_t v = u - (int64_t)tile_lo * RT;
-    const int64_t RB = p.band_tiles;
-    const int64_t nb = (RT + RB - 1) / RB;
-    int64_t bi = v / (RB * nt);
+    const uint32_t nt = (uint32_t)(tile_hi - tile_lo);
+    const uint32_t v = u - (uint32_t)tile_lo * rt_n;
+    const uint32_t RB = (uint32_t)p.band_tiles;
+    const uint32_t nb = (rt_n + RB - 1) / RB;
+    uint32_t bi = v / (RB * nt);
     if (bi > nb - 1) bi = nb - 1;
-    band_lo = bi * RB;
-    band_hi = band_lo + RB < RT ? band_lo + RB : RT;
-    const int64_t w = v - band_lo * nt;
-    const int64_t rb = band_hi - band_lo;
-    tile = tile_lo + (int)(w / rb);
-    rt = band_lo + w % rb;
+    band_lo = (int32_t)(bi * RB);
+    band_hi = band_lo + p.band_tiles < RT ? band_lo + p.band_tiles : RT;
+    const uint32_t w = v - (uint32_t)band_lo * nt;
+    const uint32_t rb = (uint32_t)(band_hi - band_lo);
+    const uint32_t wq = w / rb;
+    tile = tile_lo + (int)wq;
+    rt = band_lo + (int32_t)(w - wq * rb);
     band_b = last_at_most(tab.tile_start, p.batches + 1, band_lo);
     while (uniform(tab.tile_start[band_b + 1]) <= band_lo) ++band_b;
     b = band_b;
@@ -499,7 +524,7 @@ struct Walk {
     const int64_t seg_end = uniform(tab.seg_end[b]);
     a = uniform(tab.seg_lora[b]);
     seg_tile_end = uniform(tab.tile_start[b + 1]);
-    const int64_t row0 = seg_row + (rt - uniform(tab.tile_start[b])) * kTileRows;
+    const int64_t row0 = seg_row + (int64_t)(rt - uniform(tab.tile_start[b])) * kTileRows;
     rows_left = seg_end - row0;
     x_step = kTileRows * S.x_row_bytes;
     o_step = kTileRows * p.out_row_bytes;
@@ -557,13 +582,14 @@ struct Stage {
 
 template <int XD, int WD, int OD, bool ADD, int KS>
 __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
+  prefetch_params(p);
   extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kWaves];
   const SegTable tab = seg_table(lds, p.batches);
-  const int64_t RT = build_tile_table(p, tab, wave_total);
-  const int64_t U = RT * p.total_tiles;
+  const int32_t RT = build_tile_table(p, tab, wave_total);
+  const uint32_t U = (uint32_t)RT * (uint32_t)p.total_tiles;
   if (U == 0) return;
-  int64_t u_begin, u_end;
+  uint32_t u_begin, u_end;
   unit_range(p, U, &u_begin, &u_end);
   if (u_begin >= u_end) return;
 
@@ -695,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   bool w_pending = false;
   load_stage(sA, cur);
 
-  int64_t u = u_begin;
+  uint32_t u = u_begin;
   // One step: publish the current unit's input tile to LDS buffer `buf`,
   // issue the next unit's loads, then compute and store the current unit.
   // The LDS buffers alternate; the barrier in publish_x also orders every
@@ -753,13 +779,14 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 
 template <int XD, int WD, int OD, bool ADD>
 __global__ __launch_bounds__(kThreads) void expand_generic(const Params p) {
+  prefetch_params(p);
   extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kWaves];
   const SegTable tab = seg_table(lds, p.batches);
-  const int64_t RT = build_tile_table(p, tab, wave_total);
-  const int64_t U = RT * p.total_tiles;
+  const int32_t RT = build_tile_table(p, tab, wave_total);
+  const uint32_t U = (uint32_t)RT * (uint32_t)p.total_tiles;
   if (U == 0) return;
-  int64_t u_begin, u_end;
+  uint32_t u_begin, u_end;
   unit_range(p, U, &u_begin, &u_end);
   if (u_begin >= u_end) return;
 
@@ -770,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void expand_generic(const Params p) {
   const int K = p.K;
 
   Cursor pos(p, tab, RT, u_begin);
-  for (int64_t u = u_begin;;) {
+  for (uint32_t u = u_begin;;) {
     const Unit un = pos.decode(wave, j);
     const SliceDesc& S = p.s[un.si];
     if (un.col0 < S.n) {

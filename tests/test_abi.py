@@ -66,6 +66,9 @@ CASES = [
     (dict(x=Matrix(FAKE, BF16, 10, 8, 8)), UNSUPPORTED, "dtype"),
     (dict(x=Matrix(FAKE, F16, 1 << 31, 8, 8), out=Matrix(FAKE, F16, 1 << 31, 192, 192)),
      UNSUPPORTED, "tokens"),
+    (dict(x=Matrix(FAKE, F16, 1 << 30, 8, 8), w=Stack(FAKE, F16, 2, 1 << 15, 8),
+          out=Matrix(FAKE, F16, 1 << 30, 1 << 15, 1 << 15), off=0, size=1 << 15),
+     UNSUPPORTED, "work units"),
     (dict(meta=(0, FAKE, FAKE)), INVALID, "metadata"),
     (dict(out=Matrix(0, F16, 10, 192, 192)), INVALID, "output data"),
     (dict(x=Matrix(0, F16, 10, 8, 8)), INVALID, "null data"),
