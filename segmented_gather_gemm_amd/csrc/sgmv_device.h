@@ -436,10 +436,16 @@ __device__ __forceinline__ void buf_load8(rsrc_t r, uint32_t off, u32x4* dst) {
                                 __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0));
 }
 
-template <int D>
+// Cache policy of a store: 0 is the default; kStream (non-temporal at device
+// scope) marks lines that are written once and not read again, so they do not
+// displace reused weight and input lines from L2.
+constexpr int kStream = 0x12;  // nt | sc1
+
+template <int D, int POLICY = 0>
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const u32x4* src) {
-  __builtin_amdgcn_raw_buffer_store_b128(src[0], r, (int)off, 0, 0);
-  if constexpr (D == F32) __builtin_amdgcn_raw_buffer_store_b128(src[1], r, (int)(off + 16), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(src[0], r, (int)off, 0, POLICY);
+  if constexpr (D == F32)
+    __builtin_amdgcn_raw_buffer_store_b128(src[1], r, (int)(off + 16), 0, POLICY);
 }
 
 // One unit of the fast kernel: scalar (wave-uniform) resources over the
@@ -702,7 +708,9 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       // take an out-of-range offset; rows past the segment already lie
       // outside the resource.
       const uint32_t off = 32 * q + 8 * g < u.n_rem ? o_off[q] : kOut;
-      buf_store8<OD>(u.o, off, raw);
+      // An overwrite writes each output line once and never reads it: stream
+      // it.  An accumulation has just read the line into L2; keep the default.
+      buf_store8<OD, ADD ? 0 : kStream>(u.o, off, raw);
     }
   };
 
