@@ -44,6 +44,7 @@ int64_t elem_bytes(int32_t d) { return d == SGMV_F32 ? 4 : 2; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int ksteps_for(int64_t rank) {
+  if (rank <= 16) return 0;
   if (rank <= 32) return 1;
   if (rank <= 64) return 2;
   if (rank <= 128) return 4;
@@ -56,6 +57,7 @@ const void* pick_kernel(int xd, int wd, int od, bool add, int64_t K, bool fast_s
   using namespace sgmv;
   if (fast_shapes && K % 8 == 0 && K <= SGMV_MAX_RANK) {
     switch (ksteps_for(K)) {
+      case 0: return fast_kernel_ks0(xd, wd, od, add);
       case 1: return fast_kernel_ks1(xd, wd, od, add);
       case 2: return fast_kernel_ks2(xd, wd, od, add);
       case 4: return fast_kernel_ks4(xd, wd, od, add);

@@ -448,6 +448,14 @@ __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const u32x4* 
     __builtin_amdgcn_raw_buffer_store_b128(src[1], r, (int)(off + 16), 0, POLICY);
 }
 
+// Wave issue priority 0..3 (levels above 3 clamp to 3).
+__device__ __forceinline__ void set_priority(uint32_t level) {
+  if (level >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (level == 2) __builtin_amdgcn_s_setprio(2);
+  else if (level == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // One unit of the fast kernel: scalar (wave-uniform) resources over the
 // unit's valid input rows and the wave's output block, and the weight tile
 // it needs.
@@ -575,19 +583,31 @@ struct Walk {
   }
 };
 
+// Fast-kernel variants by KS: rank <= 32 KS for KS >= 1, with the input tile
+// shared by the workgroup's waves through LDS; KS = 0 is rank <= 16 with one
+// rank step and no sharing -- each wave loads its own (small) input tile,
+// which beats a barrier per unit when workgroups have only a unit or two.
+template <int KS>
+struct FastShape {
+  static constexpr int kSteps = KS == 0 ? 1 : KS;  // 32-wide rank steps
+  static constexpr bool kShareX = KS != 0;
+  static constexpr int kChunks = kShareX ? (kSteps + kWaves - 1) / kWaves : 1;
+};
+
 // Loads of one unit that are in flight while the previous unit computes:
-// the rank chunks of the input tile this wave loads for the workgroup
-// (chunk ks = wave + 4 i, 16 rows x 32 rank in MFMA operand order) and the
+// the rank chunks of the input tile this wave loads (shared: chunk ks = wave
+// + 4 i, 16 rows x 32 rank in MFMA operand order, for the workgroup) and the
 // prior output of the wave's own block.
 template <int XD, int OD, int KS>
 struct Stage {
-  static constexpr int kChunks = (KS + kWaves - 1) / kWaves;
-  u32x4 x[kChunks * raw_vecs<XD>()];
+  u32x4 x[FastShape<KS>::kChunks * raw_vecs<XD>()];
   u32x4 o[2 * raw_vecs<OD>()];    // prior output: two 8-column groups
 };
 
 template <int XD, int WD, int OD, bool ADD, int KS>
 __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
+  constexpr int kSteps = FastShape<KS>::kSteps;
+  constexpr bool kShareX = FastShape<KS>::kShareX;
   prefetch_params(p);
   extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kWaves];
@@ -620,19 +640,22 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     const int kb = 32 * ks + 8 * g;
     return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
   };
-  // Input tile: the workgroup shares it through LDS.  Rank chunk ks (16 rows
-  // x 32 rank, one 16-byte block per lane in MFMA operand order) is loaded
-  // by wave ks % 4 and read by all four; offsets depend on the slice's row
-  // stride.
-  constexpr int kChunks = Stage<XD, OD, KS>::kChunks;
-  __shared__ u32x4 x_lds[2][KS][64];
+  // Input tile: shared through LDS (KS >= 1): rank chunk ks (16 rows x 32
+  // rank, one 16-byte block per lane in MFMA operand order) is loaded by wave
+  // ks % 4 and read by all four.  Unshared (KS = 0): every wave loads chunk 0
+  // itself.  Offsets depend on the slice's row stride.
+  constexpr int kChunks = FastShape<KS>::kChunks;
+  __shared__ u32x4 x_lds[2][kShareX ? kSteps : 1][64];
   uint32_t x_off[kChunks];
   int x_si = -1;
+  auto x_chunk = [&](int i) __attribute__((always_inline)) -> int {
+    return kShareX ? wave + kWaves * i : 0;
+  };
   auto set_x_off = [&](int si) __attribute__((always_inline)) {
     const int64_t xs_bytes = p.s[si].x_row_bytes;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const int kb = 32 * (wave + kWaves * i) + 8 * g;
+      const int kb = 32 * x_chunk(i) + 8 * g;
       x_off[i] = kb < K ? (uint32_t)(j * xs_bytes + kb * xb) : kOut;
     }
     x_si = si;
@@ -652,20 +675,20 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     return u;
   };
 
-  auto load_w = [&](u32x4 (&w)[4][KS], const FastUnit& u) __attribute__((always_inline)) {
+  auto load_w = [&](u32x4 (&w)[4][kSteps], const FastUnit& u) __attribute__((always_inline)) {
     const SliceDesc& S = p.s[u.si];
     const rsrc_t r = make_rsrc(static_cast<const char*>(S.w) + (u.a * S.n + u.col0) * K * 2,
                                (int64_t)u.n_rem * K * 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) buf_load8<WD>(r, w_off(s, ks), &w[s][ks]);
+      for (int ks = 0; ks < kSteps; ++ks) buf_load8<WD>(r, w_off(s, ks), &w[s][ks]);
   };
   auto load_stage = [&](Stage<XD, OD, KS>& st, const FastUnit& u) __attribute__((always_inline)) {
     if (u.si != x_si) set_x_off(u.si);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
-      if (wave + kWaves * i < KS) buf_load8<XD>(u.x, x_off[i], &st.x[i * raw_vecs<XD>()]);
+      if (x_chunk(i) < kSteps) buf_load8<XD>(u.x, x_off[i], &st.x[i * raw_vecs<XD>()]);
     if constexpr (ADD) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, o_off[q], &st.o[q * raw_vecs<OD>()]);
@@ -675,13 +698,15 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // (float32 inputs are rounded to the weight dtype here) and wait for the
   // other waves' chunks.
   auto publish_x = [&](const Stage<XD, OD, KS>& st, int buf) __attribute__((always_inline)) {
+    if constexpr (kShareX) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      if (wave + kWaves * i < KS)
-        x_lds[buf][wave + kWaves * i][lane] = x_operand<XD, WD>(&st.x[i * raw_vecs<XD>()]);
-    __syncthreads();
+      for (int i = 0; i < kChunks; ++i)
+        if (x_chunk(i) < kSteps)
+          x_lds[buf][x_chunk(i)][lane] = x_operand<XD, WD>(&st.x[i * raw_vecs<XD>()]);
+      __syncthreads();
+    }
   };
-  auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][KS],
+  auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][kSteps],
                            const FastUnit& u, int buf) __attribute__((always_inline)) {
     f32x4 acc[4];
 #pragma unroll
@@ -692,8 +717,10 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       acc[2 * q + 1] = f32x4{v[4], v[5], v[6], v[7]};
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 xo = x_lds[buf][ks][lane];
+    for (int ks = 0; ks < kSteps; ++ks) {
+      u32x4 xo;
+      if constexpr (kShareX) xo = x_lds[buf][ks][lane];
+      else xo = x_operand<XD, WD>(&st.x[0]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[s] = mfma<WD>(w[s][ks], xo, acc[s]);
     }
@@ -718,8 +745,8 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // the unit being computed; with double buffering a changed tile for the
   // next unit is loaded into wB one unit ahead and copied into wA before
   // that unit computes.
-  constexpr bool kDoubleW = KS <= SGMV_DOUBLE_W_MAX_KSTEPS;
-  u32x4 wA[4][KS], wB[4][kDoubleW ? KS : 1];
+  constexpr bool kDoubleW = kSteps <= SGMV_DOUBLE_W_MAX_KSTEPS;
+  u32x4 wA[4][kSteps], wB[4][kDoubleW ? kSteps : 1];
   Stage<XD, OD, KS> sA, sB;
 
   FastUnit cur = next_unit();
@@ -742,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) wA[s][ks] = wB[s][ks];
+          for (int ks = 0; ks < kSteps; ++ks) wA[s][ks] = wB[s][ks];
         w_pending = false;
       }
     }
@@ -752,6 +779,12 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       pos.advance();
       nxt = next_unit();
     }
+    // Issue priority from the share of this workgroup's range still to do:
+    // the workgroups placed first on a compute unit win issue slots and run
+    // ahead, so those that fall behind are raised until they catch up.  Only
+    // for ranges long enough to fall behind in.
+    if (u_end - u_begin >= 8)
+      set_priority((uint32_t)(u_end - u) * 4u / (uint32_t)(u_end - u_begin + 1));
     const bool wswitch = nxt.tile != w_tile || nxt.a != w_a;
     if constexpr (kDoubleW) {
       if (wswitch) {

@@ -53,11 +53,13 @@ struct Params {
 
 // Kernel entries, by dtype codes (F16 = 0, BF16 = 1, F32 = 2), accumulate
 // flag and, for the fast kernels, the number of 32-wide rank steps they hold
-// in registers (rank <= 32 * steps).  nullptr: no such kernel.
+// in registers (rank <= 32 * steps; ks0: rank <= 16, one step, input tile not
+// shared between waves).  nullptr: no such kernel.
 //
 // Fast kernels need rank % 8 == 0, every slice width % 8 == 0 and 16-byte
 // aligned input rows, weight rows and output column groups; the generic
 // kernel takes any shape, stride and alignment.
+const void* fast_kernel_ks0(int xd, int wd, int od, bool add);
 const void* fast_kernel_ks1(int xd, int wd, int od, bool add);
 const void* fast_kernel_ks2(int xd, int wd, int od, bool add);
 const void* fast_kernel_ks4(int xd, int wd, int od, bool add);
