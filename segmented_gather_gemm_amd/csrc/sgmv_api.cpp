@@ -27,6 +27,15 @@ namespace {
 #endif
 constexpr int32_t kBandTiles = SGMV_BAND_TILES;
 
+// Units per chunk of the fast kernels' strided assignment: a workgroup keeps
+// its weight tile in registers over a chunk, and the workgroups of an XCD
+// stay within about (workgroups per XCD) chunks of each other in the walk.
+#ifndef SGMV_CHUNK_UNITS
+#define SGMV_CHUNK_UNITS 32
+#endif
+constexpr int32_t kChunkUnits = SGMV_CHUNK_UNITS;
+static_assert(kChunkUnits >= 1, "chunk size");
+
 thread_local std::string g_error;
 
 sgmv_status fail(sgmv_status status, const char* fmt, ...) {
@@ -206,6 +215,8 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   p.out_stride = out.row_stride;
   p.out_row_bytes = out.row_stride * elem_bytes(out.dtype);
   p.band_tiles = kBandTiles;
+  p.chunk_units = kChunkUnits;
+  p.sort_slots = batches >= kSortMinBatches && batches <= kSortMaxBatches;
   p.T = out.rows;
   p.batches = (int32_t)batches;
   p.L = (int32_t)L;

@@ -233,9 +233,10 @@ __device__ __forceinline__ void store_any8(void* base, int64_t e, int cnt, bool 
 // Scheduler.
 // ---------------------------------------------------------------------------
 
-// Segment table in LDS, filled by build_tile_table:
-//   tile_start[0..batches]  exclusive prefix sum of row tiles per segment
-//   seg_row[b], seg_end[b]  first row and one-past-last row of segment b
+// Segment table in LDS, filled by build_tile_table, one slot per segment
+// (slot order: see build_tile_table):
+//   tile_start[0..batches]  exclusive prefix sum of row tiles per slot
+//   seg_row[b], seg_end[b]  first row and one-past-last row of slot b's segment
 //   seg_lora[b]             its adapter index
 // A segment is active (gets tiles) when its index lies in [0, lora_num), its
 // length is positive and it lies inside [0, T).
@@ -271,6 +272,7 @@ __device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
   return t;
 }
 
+
 // Fill the table (every thread of the workgroup takes part); returns the
 // total number of row tiles (wave-uniform).
 __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTable& tab,
@@ -278,18 +280,76 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int32_t carry = 0;
-  for (int base = 0; base < p.batches; base += kThreads) {
-    const int b = base + tid;
-    int32_t tiles = 0;
-    if (b < p.batches) {
-      const int64_t st = p.start[b], ln = p.lens[b], a = p.idx[b];
-      const bool active = a >= 0 && a < p.L && ln > 0 && st >= 0 && st <= p.T - ln;
-      if (active) tiles = (int32_t)((ln + kTileRows - 1) / kTileRows);
-      tab.seg_row[b] = active ? (int32_t)st : 0;
-      tab.seg_end[b] = active ? (int32_t)(st + ln) : 0;
-      tab.seg_lora[b] = active ? (int32_t)a : 0;
+  const int B = p.batches;
+  // Segment b: its row range, adapter and row-tile count (0 when inactive).
+  auto read_segment = [&](int b, int32_t* row, int32_t* end, int32_t* a32,
+                          int32_t* tiles) __attribute__((always_inline)) {
+    const int64_t st = p.start[b], ln = p.lens[b], a = p.idx[b];
+    const bool active = a >= 0 && a < p.L && ln > 0 && st >= 0 && st <= p.T - ln;
+    *row = active ? (int32_t)st : 0;
+    *end = active ? (int32_t)(st + ln) : 0;
+    *a32 = active ? (int32_t)a : -1;
+    *tiles = active ? (int32_t)((ln + kTileRows - 1) / kTileRows) : 0;
+  };
+  // First pass: table slot of every segment; tile_start[slot] temporarily
+  // holds the segment's tile count.
+  // With p.sort_slots the table lists segments in order of (adapter, index),
+  // inactive ones last, so that segments sharing an adapter are adjacent in
+  // the walk and its weight tiles are reused instead of re-read; otherwise
+  // in index order.  Every workgroup computes the same order.
+  if (p.sort_slots && B <= kSortMaxBatches) {
+    constexpr int kPer = kSortMaxBatches / kThreads;
+    int32_t row[kPer], end[kPer], a32[kPer], tiles[kPer], key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = tid + i * kThreads;
+      if (b < B) {
+        read_segment(b, &row[i], &end[i], &a32[i], &tiles[i]);
+        key[i] = a32[i] < 0 ? INT32_MAX : a32[i];
+        tab.tile_start[b] = key[i];
+      }
     }
+    __syncthreads();
+    int32_t slot[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = tid + i * kThreads;
+      int32_t n = 0;
+      if (b < B) {
+        for (int c = 0; c < B; ++c) {
+          const int32_t kc = tab.tile_start[c];
+          n += (kc < key[i] || (kc == key[i] && c < b)) ? 1 : 0;
+        }
+      }
+      slot[i] = n;
+    }
+    __syncthreads();  // every key read before the slots are written
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = tid + i * kThreads;
+      if (b < B) {
+        tab.tile_start[slot[i]] = tiles[i];
+        tab.seg_row[slot[i]] = row[i];
+        tab.seg_end[slot[i]] = end[i];
+        tab.seg_lora[slot[i]] = a32[i] < 0 ? 0 : a32[i];
+      }
+    }
+  } else {
+    for (int b = tid; b < B; b += kThreads) {
+      int32_t row, end, a32, tiles;
+      read_segment(b, &row, &end, &a32, &tiles);
+      tab.tile_start[b] = tiles;
+      tab.seg_row[b] = row;
+      tab.seg_end[b] = end;
+      tab.seg_lora[b] = a32 < 0 ? 0 : a32;
+    }
+  }
+  __syncthreads();
+  // Second pass: exclusive prefix sum of the tile counts over table slots.
+  int32_t carry = 0;
+  for (int base = 0; base < B; base += kThreads) {
+    const int i = base + tid;
+    const int32_t tiles = i < B ? tab.tile_start[i] : 0;
     int32_t incl = tiles;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -305,11 +365,11 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
       before += w < wave ? s : 0;
       all += s;
     }
-    if (b < p.batches) tab.tile_start[b] = before + incl - tiles;
+    if (i < B) tab.tile_start[i] = before + incl - tiles;
     carry += all;
     __syncthreads();
   }
-  if (tid == 0) tab.tile_start[p.batches] = carry;
+  if (tid == 0) tab.tile_start[B] = carry;
   __syncthreads();
   return uniform(carry);
 }
@@ -319,6 +379,11 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
 // division is a long scalar sequence that every wave of a compute unit would
 // queue for on the shared scalar ALU.
 //
+// First column tile of column group g (g = kColumnGroups: one past the last).
+__device__ __forceinline__ int column_group_tile(const Params& p, int g) {
+  return (int)((uint32_t)p.total_tiles * (uint32_t)g / kColumnGroups);
+}
+
 // This workgroup's contiguous range [begin, end) of the U units (sizes differ
 // by at most one); workgroup ids are remapped so each XCD gets one contiguous
 // eighth of the range.
@@ -459,11 +524,14 @@ __device__ __forceinline__ void set_priority(uint32_t level) {
 // One unit of the fast kernel: scalar (wave-uniform) resources over the
 // unit's valid input rows and the wave's output block, and the weight tile
 // it needs.
+// Adapter indices, columns within a slice and segment row counts fit in 32
+// bits on the fast path (its output rows span less than 2 GiB per 16 rows),
+// which keeps the scalar state of the pipelined loop small.
 struct FastUnit {
   rsrc_t x;       // inputs: the tile's valid rows (rows past the segment read zero)
   rsrc_t o;       // output: from (row0, off + col0) to the end of the last valid row's block
-  int64_t a;      // adapter
-  int64_t col0;   // first of the wave's 64 columns, within the slice
+  int32_t a;      // adapter
+  int32_t col0;   // first of the wave's 64 columns, within the slice
   int32_t n_rem;  // slice columns left from col0 (<= 0: the wave has none)
   int tile;       // global column tile
   int si;         // slice
@@ -490,18 +558,40 @@ struct Walk {
   // run state for (tile, b) at row tile rt
   const char* x_row;          // inputs: first row of the row tile
   const char* o_row;          // output: first row, first column of the wave's block
-  int64_t rows_left;          // segment rows from the tile's first row on
-  int64_t x_step, o_step;     // bytes per row tile
-  int64_t a, col0;
+  int32_t rows_left;          // segment rows from the tile's first row on
+  int32_t a, col0;
+  // this workgroup's chunks (see the fast kernel): units left in the current
+  // chunk after the current unit, and the next chunk's offset in the group
+  uint32_t c_left, next_off, g_base, g_size, chunk, stride;
   int32_t n_rem;
 
-  __device__ __forceinline__ int group_tile(int g) const {
-    return (int)((uint32_t)p.total_tiles * (uint32_t)g / kColumnGroups);
-  }
+  __device__ __forceinline__ int group_tile(int g) const { return column_group_tile(p, g); }
 
   __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, int32_t rt_total,
                                   int wave_, int ob_, uint32_t u)
       : p(p_), tab(t), RT(rt_total), wave(wave_), ob(ob_) {
+    seek(u);
+  }
+
+  // Move to the next unit of the workgroup: the rest of the current chunk,
+  // else the start of the next chunk.  False when there is none.
+  __device__ __forceinline__ bool next() {
+    if (c_left > 0) {
+      advance();
+      --c_left;
+      return true;
+    }
+    if (next_off < g_size) {
+      seek(g_base + next_off);
+      c_left = (g_size - next_off < chunk ? g_size - next_off : chunk) - 1;
+      next_off += stride;
+      return true;
+    }
+    return false;
+  }
+
+  // Position on unit u (any unit of the launch).
+  __device__ __forceinline__ void seek(uint32_t u) {
     // group: units of group g start at group_tile(g) * RT
     const uint32_t rt_n = (uint32_t)RT;
     gi = 0;
@@ -539,9 +629,7 @@ struct Walk {
     a = uniform(tab.seg_lora[b]);
     seg_tile_end = uniform(tab.tile_start[b + 1]);
     const int64_t row0 = seg_row + (int64_t)(rt - uniform(tab.tile_start[b])) * kTileRows;
-    rows_left = seg_end - row0;
-    x_step = kTileRows * S.x_row_bytes;
-    o_step = kTileRows * p.out_row_bytes;
+    rows_left = (int32_t)(seg_end - row0);
     x_row = static_cast<const char*>(S.x) + row0 * S.x_row_bytes;
     o_row = static_cast<const char*>(p.out) + row0 * p.out_row_bytes + (S.offset + col0) * ob;
   }
@@ -576,8 +664,8 @@ struct Walk {
       while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
       new_run();
     } else {
-      x_row += x_step;
-      o_row += o_step;
+      x_row += kTileRows * p.s[si].x_row_bytes;
+      o_row += kTileRows * p.out_row_bytes;
       rows_left -= kTileRows;
     }
   }
@@ -615,9 +703,43 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   const int32_t RT = build_tile_table(p, tab, wave_total);
   const uint32_t U = (uint32_t)RT * (uint32_t)p.total_tiles;
   if (U == 0) return;
-  uint32_t u_begin, u_end;
-  unit_range(p, U, &u_begin, &u_end);
-  if (u_begin >= u_end) return;
+
+  // Work assignment.  With a grid of 8 k workgroups (k >= 2), workgroup i
+  // serves column group i % 8 (its XCD, under the round-robin dispatch of
+  // workgroups to XCDs) and takes the chunks i / 8, i / 8 + k, i / 8 + 2 k,
+  // ... of `chunk` consecutive units of that group's walk.  The k workgroups
+  // of an XCD thus sweep the walk side by side, within a window of about
+  // k chunks, so its L2 holds the input rows and weight tiles they share;
+  // inside a chunk the weight tile stays in registers.  Otherwise one
+  // contiguous range per workgroup.
+  const uint32_t G = (uint32_t)p.grid;
+  uint32_t c_start, c_len;     // current chunk: [c_start, c_start + c_len)
+  uint32_t g_base = 0, g_size = 0, chunk = 0, stride = 0, next_off = 0;
+  uint32_t n_total;            // units of this workgroup
+  if (G >= 16 && (G & 7) == 0) {
+    const int grp = blockIdx.x & 7;
+    const int t_lo = column_group_tile(p, grp), t_hi = column_group_tile(p, grp + 1);
+    g_base = (uint32_t)t_lo * (uint32_t)RT;
+    g_size = (uint32_t)(t_hi - t_lo) * (uint32_t)RT;
+    const uint32_t k = G >> 3;
+    const uint32_t per_wg = (g_size + k - 1) / k;
+    chunk = per_wg < (uint32_t)p.chunk_units ? (per_wg > 0 ? per_wg : 1) : (uint32_t)p.chunk_units;
+    stride = k * chunk;
+    const uint32_t s0 = (blockIdx.x >> 3) * chunk;
+    if (s0 >= g_size) return;
+    c_start = g_base + s0;
+    c_len = g_size - s0 < chunk ? g_size - s0 : chunk;
+    next_off = s0 + stride;
+    const uint32_t n_chunks = (g_size - s0 - 1) / stride + 1;
+    const uint32_t last = s0 + (n_chunks - 1) * stride;
+    n_total = (n_chunks - 1) * chunk + (g_size - last < chunk ? g_size - last : chunk);
+  } else {
+    uint32_t u_end;
+    unit_range(p, U, &c_start, &u_end);
+    if (c_start >= u_end) return;
+    c_len = u_end - c_start;
+    n_total = c_len;
+  }
 
   constexpr int xb = XD == F32 ? 4 : 2;
   constexpr int ob = OD == F32 ? 4 : 2;
@@ -661,7 +783,13 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     x_si = si;
   };
 
-  Walk pos(p, tab, RT, wave, ob, u_begin);
+  Walk pos(p, tab, RT, wave, ob, c_start);
+  pos.c_left = c_len - 1;
+  pos.next_off = next_off;
+  pos.g_base = g_base;
+  pos.g_size = g_size;
+  pos.chunk = chunk;
+  pos.stride = stride;
   auto next_unit = [&]() __attribute__((always_inline)) -> FastUnit {
     const int64_t rows = pos.rows_left < kTileRows ? pos.rows_left : kTileRows;
     FastUnit u;
@@ -752,11 +880,11 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   FastUnit cur = next_unit();
   load_w(wA, cur);
   int w_tile = cur.tile;
-  int64_t w_a = cur.a;
+  int32_t w_a = cur.a;
   bool w_pending = false;
   load_stage(sA, cur);
 
-  uint32_t u = u_begin;
+  uint32_t n_left = n_total;    // units of this workgroup from cur on
   // One step: publish the current unit's input tile to LDS buffer `buf`,
   // issue the next unit's loads, then compute and store the current unit.
   // The LDS buffers alternate; the barrier in publish_x also orders every
@@ -773,18 +901,16 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
         w_pending = false;
       }
     }
-    const bool more = u + 1 < u_end;
+    // Next unit, if any (without one the loads below repeat cur's, so every
+    // step issues the same memory instructions).
+    const bool more = pos.next();
     FastUnit nxt = cur;
-    if (more) {
-      pos.advance();
-      nxt = next_unit();
-    }
+    if (more) nxt = next_unit();
     // Issue priority from the share of this workgroup's range still to do:
     // the workgroups placed first on a compute unit win issue slots and run
     // ahead, so those that fall behind are raised until they catch up.  Only
     // for ranges long enough to fall behind in.
-    if (u_end - u_begin >= 8)
-      set_priority((uint32_t)(u_end - u) * 4u / (uint32_t)(u_end - u_begin + 1));
+    if (n_total >= 8) set_priority(n_left * 4u / (n_total + 1));
     const bool wswitch = nxt.tile != w_tile || nxt.a != w_a;
     if constexpr (kDoubleW) {
       if (wswitch) {
@@ -806,7 +932,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       }
     }
     if (!more) return false;
-    ++u;
+    --n_left;
     cur = nxt;
     return true;
   };

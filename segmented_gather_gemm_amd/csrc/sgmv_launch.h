@@ -14,6 +14,12 @@ constexpr int kWaveCols = 64;          // output columns one wavefront owns per 
 constexpr int kTileCols = kWaves * kWaveCols;  // columns per work unit (256)
 constexpr int kTileRows = 16;          // rows per work unit (one MFMA column block)
 constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk order
+// Segment tables are ordered by adapter for batches in [min, max]: with many
+// (short) segments, neighbours that share an adapter share weight tiles; the
+// ordering costs O(batches^2 / threads) per workgroup.
+constexpr int kSortMinBatches = 128;
+constexpr int kSortMaxBatches = 512;
+static_assert(kSortMaxBatches % kThreads == 0, "segments per thread when ordering");
 
 // Bits of SliceDesc::flags: 16-byte vector access is legal for ...
 enum : int32_t {
@@ -48,6 +54,8 @@ struct Params {
   int32_t total_tiles;  // column tiles over all slices
   int32_t grid;         // workgroups launched
   int32_t band_tiles;   // row tiles per band of the fast kernels' walk
+  int32_t chunk_units;  // fast kernels: units per chunk of the strided assignment
+  int32_t sort_slots;   // order the segment table by adapter (batches <= kSortMaxBatches)
   SliceDesc s[kMaxSlices];
 };
 

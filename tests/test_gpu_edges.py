@@ -107,6 +107,43 @@ def test_many_segments_multi_chunk_scan():
     run_and_check(wl)
 
 
+def shuffled_placement(rng, lens):
+    """Start rows for segments placed in a random order with small gaps."""
+    start = np.zeros(len(lens), dtype=np.int64)
+    row = 0
+    for b in rng.permutation(len(lens)):
+        row += int(rng.integers(0, 3))
+        start[b] = row
+        row += int(lens[b])
+    return start, row
+
+
+@pytest.mark.parametrize("B", [127, 128, 300, 512, 513])
+def test_adapter_ordered_segment_table(B):
+    # Batches of 128..512 segments get a segment table ordered by adapter
+    # (neighbours share weight tiles); the result must not depend on it.
+    rng = np.random.default_rng(100 + B)
+    lens = rng.integers(0, 20, size=B)
+    idx = rng.integers(-1, 12, size=B)
+    start, T = shuffled_placement(rng, lens)
+    wl = W.custom(lens.tolist(), idx.tolist(), K=64, N=512, H=576, off=32, L=12, add=True,
+                  seed=B, start=start.tolist(), T=T)
+    run_and_check(wl)
+
+
+def test_strided_chunks_several_per_workgroup():
+    # Enough 16x256 units that every workgroup takes several strided chunks
+    # of its column group's walk; with 4 column tiles, half of the 8 column
+    # groups are empty and their workgroups do nothing.
+    rng = np.random.default_rng(7)
+    lens = rng.integers(2000, 9000, size=16)
+    idx = rng.integers(-1, 4, size=16)
+    wl = W.custom(lens.tolist(), idx.tolist(), K=8, N=1024, H=1024, off=0, L=4, add=True,
+                  out_dtype="f16", x_dtype="f16", w_dtype="f16", seed=7)
+    assert wl.T >= 90000
+    run_and_check(wl)
+
+
 @pytest.mark.parametrize("add", [False, True])
 @pytest.mark.parametrize("dts", DTYPES)
 def test_integer_cases_bit_exact(add, dts):
