@@ -102,6 +102,10 @@ typedef struct {
  *
  * Returns SGMV_OK, or a status with nothing launched.  batches == 0,
  * slice_size == 0 or total_tokens == 0 return SGMV_OK without a launch.
+ * SGMV_ERR_UNSUPPORTED for total_tokens >= 2^31 and for problems of more
+ * than 2^31 - 1 work units of 16 rows x 256 columns (neither fits in
+ * device memory).  The library keeps no device state between calls, so
+ * calls on different streams may run concurrently.
  */
 sgmv_status sgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
                               const int64_t* b_seq_start_loc, const int64_t* seq_lens,
