@@ -216,7 +216,7 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   p.out_row_bytes = out.row_stride * elem_bytes(out.dtype);
   p.band_tiles = kBandTiles;
   p.chunk_units = kChunkUnits;
-  p.sort_slots = batches >= kSortMinBatches && batches <= kSortMaxBatches;
+  p.sort_slots = batches >= kSortMinBatches && batches <= kSortMaxBatches && L <= (1 << 22);
   p.T = out.rows;
   p.batches = (int32_t)batches;
   p.L = (int32_t)L;

@@ -298,30 +298,44 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
   // the walk and its weight tiles are reused instead of re-read; otherwise
   // in index order.  Every workgroup computes the same order.
   if (p.sort_slots && B <= kSortMaxBatches) {
+    // Unique 32-bit keys (adapter << 9 | index; inactive: 1 << 31 | index;
+    // the host orders only when adapters < 2^22 and batches <= 512) in
+    // tile_start[0 .. B), padded to a multiple of 4 with 0xffffffff, which
+    // is never below a key.  The padding spills into seg_row's first words,
+    // which are written only after the ranks are taken.
     constexpr int kPer = kSortMaxBatches / kThreads;
-    int32_t row[kPer], end[kPer], a32[kPer], tiles[kPer], key[kPer];
+    int32_t row[kPer], end[kPer], a32[kPer], tiles[kPer];
+    uint32_t key[kPer];
+    uint32_t* keys = reinterpret_cast<uint32_t*>(tab.tile_start);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = tid + i * kThreads;
+      key[i] = 0xffffffffu;
       if (b < B) {
         read_segment(b, &row[i], &end[i], &a32[i], &tiles[i]);
-        key[i] = a32[i] < 0 ? INT32_MAX : a32[i];
-        tab.tile_start[b] = key[i];
+        key[i] = (a32[i] < 0 ? 0x80000000u : (uint32_t)a32[i] << 9) | (uint32_t)b;
+        keys[b] = key[i];
       }
     }
+    const int B4 = (B + 3) & ~3;
+    if (tid < B4 - B) keys[B + tid] = 0xffffffffu;
     __syncthreads();
-    int32_t slot[kPer];
+    // Slot of segment b = number of keys below its key: four keys per
+    // 16-byte LDS read (a broadcast: every lane reads the same address) and a
+    // compare and an add per key.
+    uint32_t slot[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) slot[i] = 0;
+    const uint4* keys4 = reinterpret_cast<const uint4*>(keys);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int b = tid + i * kThreads;
-      int32_t n = 0;
-      if (b < B) {
-        for (int c = 0; c < B; ++c) {
-          const int32_t kc = tab.tile_start[c];
-          n += (kc < key[i] || (kc == key[i] && c < b)) ? 1 : 0;
+      if (i * kThreads < B) {  // uniform: whether any segment has this i
+#pragma unroll 4
+        for (int c4 = 0; c4 < B4 / 4; ++c4) {
+          const uint4 k4 = keys4[c4];
+          slot[i] += (k4.x < key[i]) + (k4.y < key[i]) + (k4.z < key[i]) + (k4.w < key[i]);
         }
       }
-      slot[i] = n;
     }
     __syncthreads();  // every key read before the slots are written
 #pragma unroll
@@ -697,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   constexpr int kSteps = FastShape<KS>::kSteps;
   constexpr bool kShareX = FastShape<KS>::kShareX;
   prefetch_params(p);
-  extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
+  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kWaves];
   const SegTable tab = seg_table(lds, p.batches);
   const int32_t RT = build_tile_table(p, tab, wave_total);
@@ -947,7 +961,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 template <int XD, int WD, int OD, bool ADD>
 __global__ __launch_bounds__(kThreads) void expand_generic(const Params p) {
   prefetch_params(p);
-  extern __shared__ int32_t lds[];  // segment table, 4 * batches + 1 words
+  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kWaves];
   const SegTable tab = seg_table(lds, p.batches);
   const int32_t RT = build_tile_table(p, tab, wave_total);

@@ -19,7 +19,8 @@ constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk or
 // ordering costs O(batches^2 / threads) per workgroup.
 constexpr int kSortMinBatches = 128;
 constexpr int kSortMaxBatches = 512;
-static_assert(kSortMaxBatches % kThreads == 0, "segments per thread when ordering");
+static_assert(kSortMaxBatches % kThreads == 0 && kSortMaxBatches <= 512,
+              "segments per thread when ordering; 9-bit segment index in the sort key");
 
 // Bits of SliceDesc::flags: 16-byte vector access is legal for ...
 enum : int32_t {
