@@ -90,17 +90,18 @@ class BufferSet:
         return c
 
 
-def make_step(wl, meta, sets):
+def make_step(wl, meta, sets, split=False):
+    """One step: one call over the whole workload (the fused multi-slice call
+    for several slices), or with `split` one single-slice call per slice."""
     import segmented_gather_gemm_amd as sg
     start, lens, idx = meta
     B, M = wl.batches, wl.max_seq_len
-    if len(wl.slices) == 1:
-        s = wl.slices[0]
-
+    if len(wl.slices) == 1 or split:
         def step(i):
             bs = sets[i % len(sets)]
-            sg.sgmv_expand_slice(bs.x[0], bs.w[0], bs.out, start, lens, idx, B, M, s.offset,
-                                 s.N, wl.add)
+            for k, s in enumerate(wl.slices):
+                sg.sgmv_expand_slice(bs.x[k], bs.w[k], bs.out, start, lens, idx, B, M, s.offset,
+                                     s.N, wl.add)
     else:
         offs = [s.offset for s in wl.slices]
 
@@ -250,6 +251,9 @@ def main():
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: HIP-graph replay, eager also reported)")
+    ap.add_argument("--split-slices", action="store_true",
+                    help="multi-slice workloads: one sgmv_expand_slice call per slice per step "
+                         "instead of one fused sgmv_expand_multi_slice call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -278,7 +282,8 @@ def main():
     first = BufferSet(wl, device)
     sets = [first] + [first.clone() for _ in range(nsets - 1)]
     torch.cuda.synchronize()
-    step = make_step(wl, meta, sets)
+    split = args.split_slices and len(wl.slices) > 1
+    step = make_step(wl, meta, sets, split)
 
     log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
     ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
@@ -293,7 +298,7 @@ def main():
     gbs = model_bytes / sec / 1e9
     tokens_s = wl.T / sec
     ksha = kernel_source_hash()
-    traffic_bytes = traffic_from_profiles(args.workload, ksha)
+    traffic_bytes = None if split else traffic_from_profiles(args.workload, ksha)
     traffic = None if traffic_bytes is None else round(traffic_bytes / sec / 1e9, 2)
     log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
         f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
@@ -337,7 +342,8 @@ def main():
                        "output": wl.out_dtype, "accumulate": "f32"},
             "bytes_per_step": model_bytes,
             "rotated_buffer_sets": nsets,
-            "call": "sgmv_expand_slice" if len(wl.slices) == 1 else "sgmv_expand_multi_slice",
+            "call": ("sgmv_expand_slice" if len(wl.slices) == 1 else
+                     f"{len(wl.slices)} x sgmv_expand_slice" if split else "sgmv_expand_multi_slice"),
             "launch": mode,
             "eager_us_per_step": round(ms_eager * 1e3, 3),
         },
