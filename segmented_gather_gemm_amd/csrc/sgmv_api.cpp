@@ -34,7 +34,8 @@ constexpr int32_t kBandTiles = SGMV_BAND_TILES;
 #define SGMV_CHUNK_UNITS 32
 #endif
 constexpr int32_t kChunkUnits = SGMV_CHUNK_UNITS;
-static_assert(kChunkUnits >= 1, "chunk size");
+static_assert(kChunkUnits >= 1 && kBandTiles % kChunkUnits == 0,
+              "chunks must not straddle a column tile's run of a band");
 
 thread_local std::string g_error;
 

@@ -527,14 +527,6 @@ __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const u32x4* 
     __builtin_amdgcn_raw_buffer_store_b128(src[1], r, (int)(off + 16), 0, POLICY);
 }
 
-// Wave issue priority 0..3 (levels above 3 clamp to 3).
-__device__ __forceinline__ void set_priority(uint32_t level) {
-  if (level >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (level == 2) __builtin_amdgcn_s_setprio(2);
-  else if (level == 1) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
-
 // One unit of the fast kernel: scalar (wave-uniform) resources over the
 // unit's valid input rows and the wave's output block, and the weight tile
 // it needs.
@@ -724,12 +716,17 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // ... of `chunk` consecutive units of that group's walk.  The k workgroups
   // of an XCD thus sweep the walk side by side, within a window of about
   // k chunks, so its L2 holds the input rows and weight tiles they share;
-  // inside a chunk the weight tile stays in registers.  Otherwise one
-  // contiguous range per workgroup.
+  // inside a chunk the weight tile stays in registers.  chunk =
+  // min(chunk_units, ceil(group units / k)): a group smaller than k chunk
+  // units is cut into rounded-up shares, so some workgroups stay idle while
+  // the rest hold two units or more, whose loads then overlap the previous
+  // unit's work (faster, measured, than one unit on every workgroup).
+  // chunk_units divides the walk's band height, so chunks do not straddle a
+  // column tile's run of a band.  Otherwise one contiguous range per
+  // workgroup.
   const uint32_t G = (uint32_t)p.grid;
   uint32_t c_start, c_len;     // current chunk: [c_start, c_start + c_len)
   uint32_t g_base = 0, g_size = 0, chunk = 0, stride = 0, next_off = 0;
-  uint32_t n_total;            // units of this workgroup
   if (G >= 16 && (G & 7) == 0) {
     const int grp = blockIdx.x & 7;
     const int t_lo = column_group_tile(p, grp), t_hi = column_group_tile(p, grp + 1);
@@ -744,15 +741,11 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     c_start = g_base + s0;
     c_len = g_size - s0 < chunk ? g_size - s0 : chunk;
     next_off = s0 + stride;
-    const uint32_t n_chunks = (g_size - s0 - 1) / stride + 1;
-    const uint32_t last = s0 + (n_chunks - 1) * stride;
-    n_total = (n_chunks - 1) * chunk + (g_size - last < chunk ? g_size - last : chunk);
   } else {
     uint32_t u_end;
     unit_range(p, U, &c_start, &u_end);
     if (c_start >= u_end) return;
     c_len = u_end - c_start;
-    n_total = c_len;
   }
 
   constexpr int xb = XD == F32 ? 4 : 2;
@@ -898,7 +891,6 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   bool w_pending = false;
   load_stage(sA, cur);
 
-  uint32_t n_left = n_total;    // units of this workgroup from cur on
   // One step: publish the current unit's input tile to LDS buffer `buf`,
   // issue the next unit's loads, then compute and store the current unit.
   // The LDS buffers alternate; the barrier in publish_x also orders every
@@ -920,11 +912,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     const bool more = pos.next();
     FastUnit nxt = cur;
     if (more) nxt = next_unit();
-    // Issue priority from the share of this workgroup's range still to do:
-    // the workgroups placed first on a compute unit win issue slots and run
-    // ahead, so those that fall behind are raised until they catch up.  Only
-    // for ranges long enough to fall behind in.
-    if (n_total >= 8) set_priority(n_left * 4u / (n_total + 1));
+
     const bool wswitch = nxt.tile != w_tile || nxt.a != w_a;
     if constexpr (kDoubleW) {
       if (wswitch) {
@@ -946,7 +934,6 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       }
     }
     if (!more) return false;
-    --n_left;
     cur = nxt;
     return true;
   };
