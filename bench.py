@@ -96,7 +96,13 @@ def make_step(wl, meta, sets, split=False):
     import segmented_gather_gemm_amd as sg
     start, lens, idx = meta
     B, M = wl.batches, wl.max_seq_len
-    if len(wl.slices) == 1 or split:
+    if wl.per_token:
+        s = wl.slices[0]
+
+        def step(i):
+            bs = sets[i % len(sets)]
+            sg.bgmv_expand_slice(bs.x[0], bs.w[0], bs.out, idx, s.offset, s.N, wl.add)
+    elif len(wl.slices) == 1 or split:
         def step(i):
             bs = sets[i % len(sets)]
             for k, s in enumerate(wl.slices):
@@ -131,10 +137,13 @@ def time_steps(step, steps, warmup):
     return t0.elapsed_time(t1) / steps, wall
 
 
-def time_steps_graph(step, steps, warmup):
-    """Capture `warmup` and `steps` consecutive steps into two HIP graphs and
-    time one replay of the second: the same launches with the host's launch
-    overhead taken out of the loop."""
+def time_steps_graph(step, steps, warmup, batches=5):
+    """Capture `warmup` steps and the `steps` timed steps (as up to `batches`
+    consecutive batches) into HIP graphs and replay them back to back: the
+    same launches with the host's launch overhead taken out of the loop.
+    Returns (ms per step over all timed steps, wall seconds, median over the
+    batches of ms per step)."""
+    import statistics
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -143,26 +152,55 @@ def time_steps_graph(step, steps, warmup):
             step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    nb = max(1, min(batches, steps))
+    sizes = [steps // nb + (1 if b < steps % nb else 0) for b in range(nb)]
+    g_warm = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_warm):
         for i in range(warmup):
             step(i)
-    with torch.cuda.graph(g_timed):
-        for i in range(steps):
-            step(warmup + i)
+    graphs, first = [], warmup
+    for n in sizes:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(first + i)
+        graphs.append(g)
+        first += n
     torch.cuda.synchronize()
     g_warm.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     wall0 = time.perf_counter()
-    t0.record(stream)
-    g_timed.replay()
-    t1.record(stream)
+    ev[0].record(stream)
+    for b, g in enumerate(graphs):
+        g.replay()
+        ev[b + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    return t0.elapsed_time(t1) / steps, wall
+    per_batch = [ev[b].elapsed_time(ev[b + 1]) / sizes[b] for b in range(nb)]
+    return ev[0].elapsed_time(ev[nb]) / steps, wall, statistics.median(per_batch)
+
+
+def time_single_launches(step, reps=50, flush_bytes=1 << 30):
+    """Median time of single launches, each right after a write of
+    `flush_bytes` that evicts the caches; events bracket the launch only (it
+    is enqueued while the flush still runs, so host latency is not timed)."""
+    import statistics
+    import torch
+    flush = torch.empty(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    times = []
+    for i in range(reps):
+        flush.fill_(i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    return statistics.median(times)
 
 
 def copy_ceiling(nbytes, device, reps=20):
@@ -205,38 +243,49 @@ def traffic_from_profiles(workload, ksha):
 def cpu_baseline(wl, model_bytes, budget_s):
     """Time the CPU oracle (as it stands) on the same workload, repeating the
     whole call until about `budget_s` seconds of CPU time have been spent (a
-    bounded sample for big workloads: a prefix of the segments)."""
+    bounded sample for big workloads: a prefix of the segments), on all host
+    cores; then once on one core (a smaller prefix if needed)."""
     import numpy as np
     import oracle
     import sgmv_workloads as W
     threads = len(os.sched_getaffinity(0))
     slices = [oracle.Slice(s.x, s.x_dtype, s.w, s.w_dtype, s.offset) for s in wl.slices]
-    work_rows = int(wl.lens[wl.active_mask()].sum())
-    sample = wl
-    note = "full workload"
-    # estimate: ~1e8 fp64 multiply-adds per second per thread
-    macs = work_rows * sum(s.N for s in wl.slices) * wl.K
-    if macs / (1e8 * threads) > budget_s:
-        keep = max(1, int(len(wl.lens) * budget_s * 1e8 * threads / macs))
+
+    def sample_for(seconds, nthreads):
+        # estimate: ~1e8 fp64 multiply-adds per second per thread
+        work_rows = int(wl.lens[wl.active_mask()].sum())
+        macs = work_rows * sum(s.N for s in wl.slices) * wl.K
+        if macs / (1e8 * nthreads) <= seconds:
+            return wl, "full workload"
+        keep = max(1, int(len(wl.lens) * seconds * 1e8 * nthreads / macs))
         idx = wl.idx.copy()
         idx[keep:] = -1
-        sample = W.Workload(wl.name, wl.slices, wl.out0, wl.out_dtype, wl.start, wl.lens, idx,
-                            wl.add, wl.K, wl.L)
-        note = f"first {keep} of {len(wl.lens)} segments"
+        return (W.Workload(wl.name, wl.slices, wl.out0, wl.out_dtype, wl.start, wl.lens, idx,
+                           wl.add, wl.K, wl.L), f"first {keep} of {len(wl.lens)} segments")
+
+    def run(sample, nthreads, seconds, max_reps):
+        out = np.empty_like(sample.out0)
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < seconds and reps < max_reps):
+            out[...] = sample.out0
+            t0 = time.perf_counter()
+            oracle.expand(slices, out, sample.out_dtype, sample.start, sample.lens, sample.idx,
+                          sample.add, sample.K, sample.L, threads=nthreads)
+            spent += time.perf_counter() - t0
+            reps += 1
+        return spent / reps, reps
+
+    sample, note = sample_for(budget_s, threads)
+    secs, reps = run(sample, threads, budget_s, 1000)
     sample_bytes, _, _ = byte_model(sample)
-    out = np.empty_like(sample.out0)
-    reps, spent = 0, 0.0
-    while spent < budget_s and reps < 1000:
-        out[...] = sample.out0
-        t0 = time.perf_counter()
-        oracle.expand(slices, out, sample.out_dtype, sample.start, sample.lens, sample.idx,
-                      sample.add, sample.K, sample.L, threads=threads)
-        spent += time.perf_counter() - t0
-        reps += 1
-    secs = spent / reps
+    one, one_note = sample_for(budget_s / 4, 1)
+    secs1, _ = run(one, 1, 0.0, 1)
+    one_bytes, _, _ = byte_model(one)
     return {"value": round(sample_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds_per_call": round(secs, 4), "reps": reps,
-            "sample": f"{note} of {wl.name} seed {wl.seed}, fp64 C oracle, {reps} calls"}
+            "sample": f"{note} of {wl.name} seed {wl.seed}, fp64 C oracle, {reps} calls",
+            "single_core_gbs": round(one_bytes / secs1 / 1e9, 4),
+            "single_core_sample": f"{one_note}, one call"}
 
 
 def main():
@@ -288,12 +337,15 @@ def main():
     log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
     ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
     log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
+    ms_median = None
     if args.eager:
         ms, wall, mode = ms_eager, wall_eager, "eager"
     else:
         log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
-        ms, wall = time_steps_graph(step, args.steps, args.warmup)
+        ms, wall, ms_median = time_steps_graph(step, args.steps, args.warmup)
         mode = "hip-graph replay"
+    log("bench: single launches after a cache flush")
+    ms_single = time_single_launches(step)
     sec = ms * 1e-3
     gbs = model_bytes / sec / 1e9
     tokens_s = wl.T / sec
@@ -342,10 +394,13 @@ def main():
                        "output": wl.out_dtype, "accumulate": "f32"},
             "bytes_per_step": model_bytes,
             "rotated_buffer_sets": nsets,
-            "call": ("sgmv_expand_slice" if len(wl.slices) == 1 else
+            "call": ("sgmv_bgmv_expand_slice" if wl.per_token else
+                     "sgmv_expand_slice" if len(wl.slices) == 1 else
                      f"{len(wl.slices)} x sgmv_expand_slice" if split else "sgmv_expand_multi_slice"),
             "launch": mode,
+            "batch_median_us_per_step": None if ms_median is None else round(ms_median * 1e3, 3),
             "eager_us_per_step": round(ms_eager * 1e3, 3),
+            "single_launch_after_flush_us": round(ms_single * 1e3, 3),
         },
         "roofline": {
             "bound": "hbm",

@@ -32,11 +32,12 @@
 extern "C" {
 #endif
 
-#define SGMV_ABI_VERSION 1
+#define SGMV_ABI_VERSION 2
 #define SGMV_MAX_SLICES 8      /* slices per multi-slice call                       */
 #define SGMV_MAX_RANK 256      /* largest rank the register-tiled kernels take; larger
                                   ranks (any size) run on the generic kernel */
-#define SGMV_MAX_BATCHES 4000  /* segment table lives in on-chip memory (LDS, 64 KiB) */
+#define SGMV_MAX_BATCHES 4000  /* segment table lives in on-chip memory (LDS, 64 KiB);
+                                  also the most tokens of one per-token call */
 
 /* Element types (I/O Contract: weights float16/bfloat16; inputs
  * float16/bfloat16/float32). */
@@ -128,6 +129,30 @@ sgmv_status sgmv_expand_multi_slice(const sgmv_slice* slices, int num_slices, sg
                                     const int64_t* b_seq_start_loc, const int64_t* seq_lens,
                                     const int64_t* lora_indices, int64_t batches,
                                     int64_t max_seq_len, int add_inputs, hipStream_t stream);
+
+/*
+ * sgmv_bgmv_expand_slice -- the per-token counterpart (BGMV expand slice,
+ * which the page names as the fixed-length counterpart of this operation):
+ * every token carries its own adapter index,
+ *
+ *     out[t][slice_offset + n] = (add_inputs ? out[t][slice_offset + n] : 0)
+ *                                + sum_k inputs[t][k] * lora_b[lora_indices[t]][n][k]
+ *
+ * for t in [0, total_tokens) with lora_indices[t] != -1; -1 leaves row t
+ * untouched.  Identical to sgmv_expand_slice with batches = total_tokens,
+ * b_seq_start_loc[t] = t and seq_lens[t] = 1, but reads no segment arrays.
+ *
+ * inputs, lora_b, out, slice_offset, slice_size, add_inputs, stream: as for
+ *               sgmv_expand_slice.
+ * lora_indices  device int64[total_tokens]; read only.  total_tokens =
+ *               out.rows <= SGMV_MAX_BATCHES (else SGMV_ERR_UNSUPPORTED).
+ *
+ * Tokens are processed grouped by adapter (up to 512 tokens), so tokens that
+ * share an adapter share its weight tiles.  Returns as sgmv_expand_slice.
+ */
+sgmv_status sgmv_bgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
+                                   const int64_t* lora_indices, int64_t slice_offset,
+                                   int64_t slice_size, int add_inputs, hipStream_t stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if
  * none).  The pointer stays valid until the thread's next libsgmv call. */

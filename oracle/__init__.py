@@ -189,6 +189,17 @@ def expand(slices: Sequence[Slice], out: np.ndarray, out_dtype: str,
     return views
 
 
+def bgmv_expand(slices: Sequence[Slice], out: np.ndarray, out_dtype: str, idx,
+                add_inputs: bool, K: int, L: int, want_ref: bool = False,
+                threads: int = 0) -> Optional[list]:
+    """The per-token counterpart that the page's Description names (BGMV
+    expand slice): row t takes adapter idx[t], -1 leaves it untouched.  It is
+    the same definition with row t alone as segment t (start t, length 1)."""
+    T = out.shape[0]
+    return expand(slices, out, out_dtype, np.arange(T, dtype=np.int64),
+                  np.ones(T, dtype=np.int64), idx, add_inputs, K, L, want_ref, threads)
+
+
 @dataclass
 class Report:
     checked_values: int

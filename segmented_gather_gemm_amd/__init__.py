@@ -25,8 +25,8 @@ SGMV_OK, SGMV_ERR_INVALID_ARGUMENT, SGMV_ERR_UNSUPPORTED, SGMV_ERR_HIP = range(4
 MAX_SLICES = 8
 
 # Every symbol include/sgmv.h declares.
-EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_last_error",
-                    "sgmv_abi_version")
+EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_bgmv_expand_slice",
+                    "sgmv_last_error", "sgmv_abi_version")
 
 
 class Matrix(ctypes.Structure):
@@ -79,6 +79,8 @@ def _load_library() -> ctypes.CDLL:
     lib.sgmv_expand_multi_slice.argtypes = [ctypes.POINTER(SliceDesc), ctypes.c_int, Matrix, p, p,
                                             p, i64, i64, ctypes.c_int, p]
     lib.sgmv_expand_multi_slice.restype = ctypes.c_int
+    lib.sgmv_bgmv_expand_slice.argtypes = [Matrix, Stack, Matrix, p, i64, i64, ctypes.c_int, p]
+    lib.sgmv_bgmv_expand_slice.restype = ctypes.c_int
     lib.sgmv_last_error.argtypes = []
     lib.sgmv_last_error.restype = ctypes.c_char_p
     lib.sgmv_abi_version.argtypes = []
@@ -221,9 +223,34 @@ def sgmv_expand_multi_slice(slices: Sequence[Tuple[object, object, int]], output
     return output_tensor
 
 
+def bgmv_expand_slice(inputs, lora_b_weights, output_tensor, lora_indices_tensor, slice_offset: int,
+                      slice_size: int, add_inputs: bool = False):
+    """Per-token form: output_tensor[t, slice_offset:slice_offset + slice_size]
+    (+)= inputs[t] @ lora_b_weights[lora_indices[t]].T for every token t with
+    index != -1.  Enqueued on the current stream."""
+    import torch
+    device, (idx,) = _common(output_tensor, [(lora_indices_tensor, "lora_indices_tensor")])
+    for t, n in ((inputs, "inputs"), (lora_b_weights, "lora_b_weights")):
+        if t.device != device:
+            raise ValueError(f"{n} must be on {device}")
+    if len(idx) < output_tensor.shape[0]:
+        raise ValueError("lora_indices_tensor shorter than the number of tokens")
+    x = _matrix(inputs, "inputs")
+    w = _stack(lora_b_weights, "lora_b_weights")
+    out = _matrix(output_tensor, "output_tensor")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    with _on_device(device):
+        st = lib.sgmv_bgmv_expand_slice(x, w, out, idx.data_ptr(), int(slice_offset),
+                                        int(slice_size), int(bool(add_inputs)), stream)
+    if st != SGMV_OK:
+        _raise(st)
+    return output_tensor
+
+
 def abi_version() -> int:
     return lib.sgmv_abi_version()
 
 
-__all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "abi_version", "SgmvError", "lib",
+__all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "bgmv_expand_slice", "abi_version",
+           "SgmvError", "lib",
            "Matrix", "Stack", "SliceDesc", "EXPORTED_SYMBOLS", "LIBRARY_PATH"]

@@ -108,11 +108,13 @@ hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups
   return hipSuccess;
 }
 
-// Checks shared by both entry points.  `slices` are host descriptors.
+// Checks shared by the entry points.  `slices` are host descriptors.  With
+// `per_token` (the BGMV form) segment b is row b alone: start and lens are
+// not used and batches = the number of rows.
 sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matrix out,
                              const int64_t* start, const int64_t* lens, const int64_t* idx,
                              int64_t batches, int64_t max_seq_len, int add_inputs,
-                             hipStream_t stream) {
+                             hipStream_t stream, bool per_token = false) {
   using namespace sgmv;
   if (num_slices < 1 || num_slices > SGMV_MAX_SLICES)
     return fail(SGMV_ERR_INVALID_ARGUMENT, "num_slices must be in 1..%d, got %d",
@@ -200,7 +202,7 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   if (units > INT32_MAX)
     return fail(SGMV_ERR_UNSUPPORTED, "more than 2^31-1 work units (16-row x 256-column tiles)");
   if (!out.data) return fail(SGMV_ERR_INVALID_ARGUMENT, "output data pointer is null");
-  if (!start || !lens || !idx)
+  if ((!per_token && (!start || !lens)) || !idx)
     return fail(SGMV_ERR_INVALID_ARGUMENT, "segment metadata pointer is null");
   for (int i = 0; i < num_slices; ++i) {
     if (slices[i].slice_size == 0) continue;
@@ -217,7 +219,11 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   p.out_row_bytes = out.row_stride * elem_bytes(out.dtype);
   p.band_tiles = kBandTiles;
   p.chunk_units = kChunkUnits;
-  p.sort_slots = batches >= kSortMinBatches && batches <= kSortMaxBatches && L <= (1 << 22);
+  p.per_token = per_token ? 1 : 0;
+  // Per-token calls always order tokens by adapter (when it is cheap enough):
+  // neighbours that share an adapter then share its weight tiles.
+  p.sort_slots = (per_token || batches >= kSortMinBatches) && batches <= kSortMaxBatches &&
+                 L <= (1 << 22);
   p.T = out.rows;
   p.batches = (int32_t)batches;
   p.L = (int32_t)L;
@@ -302,6 +308,21 @@ sgmv_status sgmv_expand_multi_slice(const sgmv_slice* slices, int num_slices, sg
   if (!slices) return fail(SGMV_ERR_INVALID_ARGUMENT, "slices pointer is null");
   return check_and_launch(slices, num_slices, out, b_seq_start_loc, seq_lens, lora_indices,
                           batches, max_seq_len, add_inputs, stream);
+}
+
+sgmv_status sgmv_bgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
+                                   const int64_t* lora_indices, int64_t slice_offset,
+                                   int64_t slice_size, int add_inputs, hipStream_t stream) {
+  if (out.rows > SGMV_MAX_BATCHES)
+    return fail(SGMV_ERR_UNSUPPORTED, "per-token calls take at most %d tokens, got %lld",
+                SGMV_MAX_BATCHES, (long long)out.rows);
+  sgmv_slice s;
+  s.inputs = inputs;
+  s.lora_b = lora_b;
+  s.slice_offset = slice_offset;
+  s.slice_size = slice_size;
+  return check_and_launch(&s, 1, out, nullptr, nullptr, lora_indices, out.rows < 0 ? 0 : out.rows,
+                          1, add_inputs, stream, true);
 }
 
 const char* sgmv_last_error(void) { return g_error.c_str(); }

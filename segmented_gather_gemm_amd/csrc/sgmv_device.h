@@ -284,7 +284,9 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
   // Segment b: its row range, adapter and row-tile count (0 when inactive).
   auto read_segment = [&](int b, int32_t* row, int32_t* end, int32_t* a32,
                           int32_t* tiles) __attribute__((always_inline)) {
-    const int64_t st = p.start[b], ln = p.lens[b], a = p.idx[b];
+    const int64_t st = p.per_token ? b : p.start[b];
+    const int64_t ln = p.per_token ? 1 : p.lens[b];
+    const int64_t a = p.idx[b];
     const bool active = a >= 0 && a < p.L && ln > 0 && st >= 0 && st <= p.T - ln;
     *row = active ? (int32_t)st : 0;
     *end = active ? (int32_t)(st + ln) : 0;

@@ -57,6 +57,7 @@ struct Params {
   int32_t band_tiles;   // row tiles per band of the fast kernels' walk
   int32_t chunk_units;  // fast kernels: units per chunk of the strided assignment
   int32_t sort_slots;   // order the segment table by adapter (batches <= kSortMaxBatches)
+  int32_t per_token;    // segment b is row b alone (start and lens unused)
   SliceDesc s[kMaxSlices];
 };
 

@@ -83,6 +83,7 @@ class Workload:
     L: int
     seed: int = 0
     notes: Dict[str, object] = field(default_factory=dict)
+    per_token: bool = False   # BGMV form: segment t is row t alone (start t, length 1)
 
     @property
     def T(self) -> int:
@@ -220,12 +221,38 @@ def skewed_mixed(seed: int = 0) -> Workload:
                     exclusive_cumsum(lens), lens, idx, True, K, L, seed)
 
 
+def bgmv_decode(seed: int = 0) -> Workload:
+    """Per-token (BGMV) decode step with q_proj shapes: 256 tokens, one per
+    sequence; rank 16; hidden 4096 = slice; 32 adapters, lora_B (32, 4096, 16)
+    bf16 N(0, 0.02); input bf16 N(0, 1); indices uniform in {-1, 0..31};
+    accumulate onto a bf16 N(0, 1) output."""
+    rng = np.random.default_rng(seed)
+    T, K, N, L = 256, 16, 4096, 32
+    idx = rng.integers(-1, L, size=T).astype(np.int64)
+    w = normal(rng, (L, N, K), 0.02, "bf16")
+    x = normal(rng, (T, K), 1.0, "bf16")
+    out0 = normal(rng, (T, N), 1.0, "bf16")
+    return Workload("bgmv_decode", [SliceInput(x, "bf16", w, "bf16", 0)], out0, "bf16",
+                    np.arange(T, dtype=np.int64), np.ones(T, dtype=np.int64), idx, True, K, L,
+                    seed, per_token=True)
+
+
+def per_token(idx: Sequence[int], **kw) -> Workload:
+    """A per-token (BGMV) workload: token t alone is segment t, with adapter
+    idx[t]; other arguments as for custom()."""
+    T = len(idx)
+    wl = custom([1] * T, idx, start=list(range(T)), T=T, **kw)
+    wl.per_token = True
+    return wl
+
+
 WORKLOADS: Dict[str, Callable[..., Workload]] = {
     "tiny_ref": tiny_ref,
     "llama7b_q_proj": llama7b_q_proj,
     "gqa_qkv": gqa_qkv,
     "mlp_gate_up": mlp_gate_up,
     "skewed_mixed": skewed_mixed,
+    "bgmv_decode": bgmv_decode,
 }
 
 

@@ -68,6 +68,14 @@ class DeviceWorkload:
             self.run_single(out, i)
         return out
 
+    def run_bgmv(self, out):
+        """The per-token entry point (the workload's segments must be rows)."""
+        import segmented_gather_gemm_amd as sg
+        wl = self.wl
+        s = wl.slices[0]
+        sg.bgmv_expand_slice(self.x[0], self.w[0], out, self.idx, s.offset, s.N, wl.add)
+        return out
+
     def run_multi(self, out):
         import segmented_gather_gemm_amd as sg
         wl = self.wl

@@ -124,6 +124,36 @@ def test_multi_slice_checks():
     assert st == INVALID
 
 
+def bgmv(x=None, w=None, out=None, idx=FAKE, off=64, size=64, add=0):
+    x = x or Matrix(FAKE, F16, 10, 8, 8)
+    w = w or Stack(FAKE, F16, 2, 64, 8)
+    out = out or Matrix(FAKE, F16, 10, 192, 192)
+    st = sg.lib.sgmv_bgmv_expand_slice(x, w, out, idx, off, size, add, None)
+    return st, sg.lib.sgmv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(idx=0), INVALID, "metadata"),
+    (dict(x=Matrix(FAKE, F16, 9, 8, 8)), INVALID, "rows"),
+    (dict(x=Matrix(FAKE, F16, 10, 16, 16)), INVALID, "rank"),
+    (dict(size=32), INVALID, "slice_size"),
+    (dict(off=129), INVALID, "window"),
+    (dict(w=Stack(FAKE, F32, 2, 64, 8)), UNSUPPORTED, "float16 or bfloat16"),
+    (dict(x=Matrix(FAKE, F16, 4001, 8, 8), out=Matrix(FAKE, F16, 4001, 192, 192)),
+     UNSUPPORTED, "tokens"),
+    (dict(out=Matrix(FAKE, F16, -1, 192, 192)), INVALID, "output shape"),
+])
+def test_bgmv_invalid_arguments_rejected_before_launch(kw, status, frag):
+    st, msg = bgmv(**kw)
+    assert st == status, msg
+    assert frag in msg
+
+
+def test_bgmv_no_op_calls():
+    assert bgmv(x=Matrix(FAKE, F16, 0, 8, 8), out=Matrix(FAKE, F16, 0, 192, 192)) == (OK, "")
+    assert bgmv(size=0, w=Stack(FAKE, F16, 2, 0, 8)) == (OK, "")
+
+
 def test_python_wrapper_rejects_host_tensors():
     import torch
     x = torch.zeros(10, 8, dtype=torch.float16)

@@ -44,3 +44,14 @@ def test_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_reports_multi_and_single_core_rates():
+    import bench
+    import sgmv_workloads as W
+    wl = W.tiny_ref(0)
+    mb, _, _ = bench.byte_model(wl)
+    cpu = bench.cpu_baseline(wl, mb, 0.05)
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s"
+    assert cpu["value"] > 0 and cpu["single_core_gbs"] > 0 and cpu["reps"] >= 1
+    assert cpu["cores"] >= 1 and "tiny_ref" in cpu["sample"]

@@ -218,6 +218,45 @@ def test_brute_force_multi_slice():
 
 
 # --------------------------------------------------------------------------
+# The per-token (BGMV) form.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,add,dts", [(31, False, ("bf16", "bf16", "bf16")),
+                                          (32, True, ("f16", "f16", "f32")),
+                                          (33, True, ("f32", "bf16", "f16"))])
+def test_bgmv_per_token_brute_force(seed, add, dts):
+    # Every row takes its own adapter; checked through the masked reference,
+    # which reads the per-row adapters from (start t, length 1) segments.
+    x_dt, w_dt, o_dt = dts
+    idx = np.random.default_rng(seed).integers(-1, 4, size=23)
+    wl = W.per_token(idx.tolist(), K=11, N=13, H=30, off=9, L=4, x_dtype=x_dt, w_dtype=w_dt,
+                     out_dtype=o_dt, add=add, seed=seed)
+    out = wl.out0.copy()
+    slices = [oracle.Slice(s.x, s.x_dtype, s.w, s.w_dtype, s.offset) for s in wl.slices]
+    ref = oracle.bgmv_expand(slices, out, wl.out_dtype, wl.idx, wl.add, wl.K, wl.L,
+                             want_ref=True)
+    assert_matches_reference(wl, out, ref)
+
+
+def test_bgmv_row_by_row_matrix_vector():
+    # Token t's slice equals x[t] @ W[idx[t]]^T computed on its own (a plain
+    # matrix-vector product per row), exactly for integer values.
+    idx = [2, 0, -1, 2, 1, 0]
+    wl = W.per_token(idx, K=5, N=7, H=7, off=0, L=3, x_dtype="f16", w_dtype="f16",
+                     out_dtype="f32", values="int", seed=34)
+    out = wl.out0.copy()
+    slices = [oracle.Slice(s.x, s.x_dtype, s.w, s.w_dtype, s.offset) for s in wl.slices]
+    oracle.bgmv_expand(slices, out, "f32", wl.idx, False, wl.K, wl.L)
+    x = np_values(wl.slices[0].x, "f16").astype(np.int64)
+    w = np_values(wl.slices[0].w, "f16").astype(np.int64)
+    for t, a in enumerate(idx):
+        if a < 0:
+            assert np.array_equal(out[t], wl.out0[t])
+        else:
+            assert np.array_equal(out[t].astype(np.int64), w[a] @ x[t])
+
+
+# --------------------------------------------------------------------------
 # Invariants.
 # --------------------------------------------------------------------------
 
