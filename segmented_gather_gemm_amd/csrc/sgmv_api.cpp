@@ -61,17 +61,20 @@ int ksteps_for(int64_t rank) {
   return 8;  // rank <= SGMV_MAX_RANK
 }
 
+bool fast_rank(int64_t K) { return K % 8 == 0 && K <= SGMV_MAX_RANK; }
+
 // The kernel for a call: a fast (pipelined) kernel when rank, slice widths
-// and alignment allow it, else the generic one.
-const void* pick_kernel(int xd, int wd, int od, bool add, int64_t K, bool fast_shapes) {
+// and alignment allow it (`fast`), with gathered row tiles for `gather`
+// (per-token calls only), else the generic one.
+const void* pick_kernel(int xd, int wd, int od, bool add, int64_t K, bool fast, bool gather) {
   using namespace sgmv;
-  if (fast_shapes && K % 8 == 0 && K <= SGMV_MAX_RANK) {
+  if (fast) {
     switch (ksteps_for(K)) {
-      case 0: return fast_kernel_ks0(xd, wd, od, add);
-      case 1: return fast_kernel_ks1(xd, wd, od, add);
-      case 2: return fast_kernel_ks2(xd, wd, od, add);
-      case 4: return fast_kernel_ks4(xd, wd, od, add);
-      default: return fast_kernel_ks8(xd, wd, od, add);
+      case 0: return fast_kernel_ks0(xd, wd, od, add, gather);
+      case 1: return fast_kernel_ks1(xd, wd, od, add, gather);
+      case 2: return fast_kernel_ks2(xd, wd, od, add, gather);
+      case 4: return fast_kernel_ks4(xd, wd, od, add, gather);
+      default: return fast_kernel_ks8(xd, wd, od, add, gather);
     }
   }
   return generic_kernel(xd, wd, od, add);
@@ -220,10 +223,6 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   p.band_tiles = kBandTiles;
   p.chunk_units = kChunkUnits;
   p.per_token = per_token ? 1 : 0;
-  // Per-token calls always order tokens by adapter (when it is cheap enough):
-  // neighbours that share an adapter then share its weight tiles.
-  p.sort_slots = (per_token || batches >= kSortMinBatches) && batches <= kSortMaxBatches &&
-                 L <= (1 << 22);
   p.T = out.rows;
   p.batches = (int32_t)batches;
   p.L = (int32_t)L;
@@ -262,8 +261,21 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
         16 * p.s[i].x_row_bytes >= (int64_t(1) << 31))
       fast_shapes = false;
   }
+  const bool fast = fast_shapes && fast_rank(K);
+  // Per-token calls always order tokens by adapter (when it is cheap enough):
+  // neighbours that share an adapter then share its weight tiles; the fast
+  // kernels then also gather each adapter's tokens into common row tiles,
+  // when T rows of the inputs and of the output span less than 2 GiB (32-bit
+  // row offsets).
+  const bool sort = (per_token || batches >= kSortMinBatches) && batches <= kSortMaxBatches &&
+                    L <= (1 << 22);
+  bool gather = fast && per_token && sort && out.rows * p.out_row_bytes < (int64_t(1) << 31);
+  for (int i = 0; i < num_slices && gather; ++i)
+    if (out.rows * p.s[i].x_row_bytes >= (int64_t(1) << 31)) gather = false;
+  p.sort_slots = sort;
+  p.gather = gather;
   const void* kernel =
-      pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast_shapes);
+      pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast, gather);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no kernel for this dtype combination");
 
   const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);  // segment table

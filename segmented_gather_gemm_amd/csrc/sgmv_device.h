@@ -350,6 +350,40 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
         tab.seg_lora[slot[i]] = a32[i] < 0 ? 0 : a32[i];
       }
     }
+    if (p.gather) {
+      // Per-token table ordered by adapter: cut the active slots (first in
+      // the order) into row tiles of up to 16 slots that share an adapter,
+      // starting a new tile at every adapter change and every 16th slot.  A
+      // tile's first slot gets one row tile and seg_end = its one-past-last
+      // slot; the other slots get none; seg_row keeps every slot's token row.
+      // A wave holds 64 consecutive slots, so a tile never leaves its wave.
+      __syncthreads();
+      int32_t tiles_g[kPer], end_g[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int sl = tid + i * kThreads;
+        const bool act = sl < B && tab.tile_start[sl] > 0;
+        const bool first = act && ((sl & 15) == 0 || tab.seg_lora[sl] != tab.seg_lora[sl - 1]);
+        const uint64_t starts = __ballot(first);
+        const uint64_t actives = __ballot(act);
+        // next tile start or inactive slot after this lane, else the end of
+        // its 16-slot block
+        const uint64_t stop = (starts | ~actives) & ~((2ull << lane) - 1);
+        const int block_end = (lane & ~15) + 16;
+        const int next = stop ? __builtin_ctzll(stop) : 64;
+        end_g[i] = (sl - lane) + (next < block_end ? next : block_end);
+        tiles_g[i] = first ? 1 : 0;
+      }
+      __syncthreads();  // every neighbour read before the counts change
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int sl = tid + i * kThreads;
+        if (sl < B) {
+          tab.tile_start[sl] = tiles_g[i];
+          tab.seg_end[sl] = tiles_g[i] ? end_g[i] : 0;
+        }
+      }
+    }
   } else {
     for (int b = tid; b < B; b += kThreads) {
       int32_t row, end, a32, tiles;
@@ -538,6 +572,7 @@ __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const u32x4* 
 struct FastUnit {
   rsrc_t x;       // inputs: the tile's valid rows (rows past the segment read zero)
   rsrc_t o;       // output: from (row0, off + col0) to the end of the last valid row's block
+  uint32_t lx, lo;  // gathered tiles: this lane's row offset in x and o (kOut: none)
   int32_t a;      // adapter
   int32_t col0;   // first of the wave's 64 columns, within the slice
   int32_t n_rem;  // slice columns left from col0 (<= 0: the wave has none)
@@ -550,6 +585,7 @@ struct FastUnit {
 // of band_tiles row tiles, then column tile, then row tile.  Within a run of
 // row tiles of one segment under one column tile, a step only advances row
 // offsets; segment, tile and band changes re-read the LDS table.
+template <bool GATHER>
 struct Walk {
   const Params& p;
   const SegTable& tab;
@@ -574,6 +610,20 @@ struct Walk {
   int32_t n_rem;
 
   __device__ __forceinline__ int group_tile(int g) const { return column_group_tile(p, g); }
+
+  // Table slot holding row tile r, searching forward from slot `from` (a slot
+  // at or before it).  Slots without tiles come before the slot that holds
+  // the tile, so the last slot whose prefix is <= r is the one.  Gathered
+  // tables have many tile-less slots: a binary search there.
+  __device__ __forceinline__ int slot_of(int32_t r, int from) const {
+    if constexpr (GATHER) {
+      return last_at_most(tab.tile_start, p.batches + 1, r);
+    } else {
+      int s = from;
+      while (uniform(tab.tile_start[s + 1]) <= r) ++s;
+      return s;
+    }
+  }
 
   __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, int32_t rt_total,
                                   int wave_, int ob_, uint32_t u)
@@ -620,9 +670,7 @@ struct Walk {
     tile = tile_lo + (int)wq;
     rt = band_lo + (int32_t)(w - wq * rb);
     band_b = last_at_most(tab.tile_start, p.batches + 1, band_lo);
-    while (uniform(tab.tile_start[band_b + 1]) <= band_lo) ++band_b;
-    b = band_b;
-    while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+    b = slot_of(rt, band_b);
     si = slice_of(p, tile);
     new_run();
   }
@@ -632,6 +680,16 @@ struct Walk {
     col0 = (int64_t)(tile - S.tile_begin) * kTileCols + wave * kWaveCols;
     const int64_t n_left = S.n - col0;
     n_rem = n_left <= 0 ? 0 : (n_left > kWaveCols ? kWaveCols : (int32_t)n_left);
+    if constexpr (GATHER) {
+      // slot b opens a gathered tile of slots [b, seg_end[b]); each lane
+      // finds its token row in seg_row (see the fast kernel)
+      rows_left = uniform(tab.seg_end[b]) - b;
+      a = uniform(tab.seg_lora[b]);
+      seg_tile_end = rt + 1;
+      x_row = static_cast<const char*>(S.x);
+      o_row = static_cast<const char*>(p.out) + (S.offset + col0) * ob;
+      return;
+    }
     const int64_t seg_row = uniform(tab.seg_row[b]);
     const int64_t seg_end = uniform(tab.seg_end[b]);
     a = uniform(tab.seg_lora[b]);
@@ -659,17 +717,19 @@ struct Walk {
         }
         band_hi = band_lo + p.band_tiles < RT ? band_lo + p.band_tiles : RT;
         tile = tile_lo;
-        while (uniform(tab.tile_start[b + 1]) <= band_lo) ++b;
-        band_b = b;
+        band_b = slot_of(band_lo, b);
       }
       rt = band_lo;
       b = band_b;
       si = slice_of(p, tile);
-      while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
       new_run();
     } else if (rt == seg_tile_end) {
-      ++b;
-      while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+      if constexpr (GATHER) {
+        b = uniform(tab.seg_end[b]);  // the next tile opens where this one ends
+      } else {
+        ++b;
+        while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
+      }
       new_run();
     } else {
       x_row += kTileRows * p.s[si].x_row_bytes;
@@ -700,7 +760,9 @@ struct Stage {
   u32x4 o[2 * raw_vecs<OD>()];    // prior output: two 8-column groups
 };
 
-template <int XD, int WD, int OD, bool ADD, int KS>
+// GATHER: per-token calls whose row tiles gather up to 16 tokens of one
+// adapter (rows not contiguous): each lane's row offset comes from the table.
+template <int XD, int WD, int OD, bool ADD, int KS, bool GATHER>
 __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   constexpr int kSteps = FastShape<KS>::kSteps;
   constexpr bool kShareX = FastShape<KS>::kShareX;
@@ -766,7 +828,8 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // the wave's block) and weights (row weight_row(0, s, j) of the tile).
   uint32_t o_off[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) o_off[q] = (uint32_t)(j * os_bytes) + (32 * q + 8 * g) * ob;
+  for (int q = 0; q < 2; ++q)
+    o_off[q] = (uint32_t)(GATHER ? 0 : j * os_bytes) + (32 * q + 8 * g) * ob;
   auto w_off = [&](int s, int ks) __attribute__((always_inline)) -> uint32_t {
     const int kb = 32 * ks + 8 * g;
     return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
@@ -787,12 +850,12 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int kb = 32 * x_chunk(i) + 8 * g;
-      x_off[i] = kb < K ? (uint32_t)(j * xs_bytes + kb * xb) : kOut;
+      x_off[i] = kb < K ? (uint32_t)((GATHER ? 0 : j * xs_bytes) + kb * xb) : kOut;
     }
     x_si = si;
   };
 
-  Walk pos(p, tab, RT, wave, ob, c_start);
+  Walk<GATHER> pos(p, tab, RT, wave, ob, c_start);
   pos.c_left = c_len - 1;
   pos.next_off = next_off;
   pos.g_base = g_base;
@@ -807,8 +870,21 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     u.a = pos.a;
     u.col0 = pos.col0;
     u.n_rem = pos.n_rem;
-    u.x = make_rsrc(pos.x_row, rows * p.s[pos.si].x_row_bytes);
-    u.o = make_rsrc(pos.o_row, u.n_rem > 0 ? (rows - 1) * p.out_row_bytes + (int64_t)u.n_rem * ob : 0);
+    if constexpr (GATHER) {
+      // Token j of the tile: this lane's row (the host keeps T rows of x and
+      // of the output within 2 GiB, so row offsets fit 32 bits).
+      const int64_t row = j < pos.rows_left ? tab.seg_row[pos.b + j] : -1;
+      u.lx = row >= 0 ? (uint32_t)(row * p.s[pos.si].x_row_bytes) : kOut;
+      u.lo = row >= 0 ? (uint32_t)(row * p.out_row_bytes) : kOut;
+      u.x = make_rsrc(pos.x_row, p.T * p.s[pos.si].x_row_bytes);
+      u.o = make_rsrc(pos.o_row,
+                      u.n_rem > 0 ? (p.T - 1) * p.out_row_bytes + (int64_t)u.n_rem * ob : 0);
+    } else {
+      u.lx = u.lo = 0;
+      u.x = make_rsrc(pos.x_row, rows * p.s[pos.si].x_row_bytes);
+      u.o = make_rsrc(pos.o_row,
+                      u.n_rem > 0 ? (rows - 1) * p.out_row_bytes + (int64_t)u.n_rem * ob : 0);
+    }
     return u;
   };
 
@@ -825,10 +901,10 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     if (u.si != x_si) set_x_off(u.si);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
-      if (x_chunk(i) < kSteps) buf_load8<XD>(u.x, x_off[i], &st.x[i * raw_vecs<XD>()]);
+      if (x_chunk(i) < kSteps) buf_load8<XD>(u.x, u.lx + x_off[i], &st.x[i * raw_vecs<XD>()]);
     if constexpr (ADD) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, o_off[q], &st.o[q * raw_vecs<OD>()]);
+      for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, u.lo + o_off[q], &st.o[q * raw_vecs<OD>()]);
     }
   };
   // Publish this wave's chunks of a unit's input tile to LDS buffer `buf`
@@ -871,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       // Column groups past the slice (only in a slice's last column tile)
       // take an out-of-range offset; rows past the segment already lie
       // outside the resource.
-      const uint32_t off = 32 * q + 8 * g < u.n_rem ? o_off[q] : kOut;
+      const uint32_t off = 32 * q + 8 * g < u.n_rem ? u.lo + o_off[q] : kOut;
       // An overwrite writes each output line once and never reads it: stream
       // it.  An accumulation has just read the line into L2; keep the default.
       buf_store8<OD, ADD ? 0 : kStream>(u.o, off, raw);
@@ -1025,27 +1101,30 @@ __global__ __launch_bounds__(kThreads) void expand_generic(const Params p) {
 // ---------------------------------------------------------------------------
 
 template <int XD, int WD, int OD, int KS>
-const void* fast_entry(bool add) {
-  return add ? reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, true, KS>)
-             : reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, false, KS>);
+const void* fast_entry(bool add, bool gather) {
+  if (gather)
+    return add ? reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, true, KS, true>)
+               : reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, false, KS, true>);
+  return add ? reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, true, KS, false>)
+             : reinterpret_cast<const void*>(&expand_fast<XD, WD, OD, false, KS, false>);
 }
 
 template <int XD, int WD, int KS>
-const void* fast_by_out(int od, bool add) {
+const void* fast_by_out(int od, bool add, bool gather) {
   switch (od) {
-    case F16: return fast_entry<XD, WD, F16, KS>(add);
-    case BF16: return fast_entry<XD, WD, BF16, KS>(add);
-    case F32: return fast_entry<XD, WD, F32, KS>(add);
+    case F16: return fast_entry<XD, WD, F16, KS>(add, gather);
+    case BF16: return fast_entry<XD, WD, BF16, KS>(add, gather);
+    case F32: return fast_entry<XD, WD, F32, KS>(add, gather);
     default: return nullptr;
   }
 }
 
 template <int KS>
-const void* fast_table(int xd, int wd, int od, bool add) {
-  if (wd == BF16 && xd == BF16) return fast_by_out<BF16, BF16, KS>(od, add);
-  if (wd == BF16 && xd == F32) return fast_by_out<F32, BF16, KS>(od, add);
-  if (wd == F16 && xd == F16) return fast_by_out<F16, F16, KS>(od, add);
-  if (wd == F16 && xd == F32) return fast_by_out<F32, F16, KS>(od, add);
+const void* fast_table(int xd, int wd, int od, bool add, bool gather) {
+  if (wd == BF16 && xd == BF16) return fast_by_out<BF16, BF16, KS>(od, add, gather);
+  if (wd == BF16 && xd == F32) return fast_by_out<F32, BF16, KS>(od, add, gather);
+  if (wd == F16 && xd == F16) return fast_by_out<F16, F16, KS>(od, add, gather);
+  if (wd == F16 && xd == F32) return fast_by_out<F32, F16, KS>(od, add, gather);
   return nullptr;
 }
 

@@ -4,8 +4,8 @@
 
 namespace sgmv {
 
-const void* fast_kernel_ks1(int xd, int wd, int od, bool add) {
-  return dev::fast_table<1>(xd, wd, od, add);
+const void* fast_kernel_ks1(int xd, int wd, int od, bool add, bool gather) {
+  return dev::fast_table<1>(xd, wd, od, add, gather);
 }
 
 }  // namespace sgmv

@@ -4,8 +4,8 @@
 
 namespace sgmv {
 
-const void* fast_kernel_ks2(int xd, int wd, int od, bool add) {
-  return dev::fast_table<2>(xd, wd, od, add);
+const void* fast_kernel_ks2(int xd, int wd, int od, bool add, bool gather) {
+  return dev::fast_table<2>(xd, wd, od, add, gather);
 }
 
 }  // namespace sgmv

@@ -4,8 +4,8 @@
 
 namespace sgmv {
 
-const void* fast_kernel_ks4(int xd, int wd, int od, bool add) {
-  return dev::fast_table<4>(xd, wd, od, add);
+const void* fast_kernel_ks4(int xd, int wd, int od, bool add, bool gather) {
+  return dev::fast_table<4>(xd, wd, od, add, gather);
 }
 
 }  // namespace sgmv

@@ -58,22 +58,24 @@ struct Params {
   int32_t chunk_units;  // fast kernels: units per chunk of the strided assignment
   int32_t sort_slots;   // order the segment table by adapter (batches <= kSortMaxBatches)
   int32_t per_token;    // segment b is row b alone (start and lens unused)
+  int32_t gather;       // per-token table cut into gathered row tiles (fast kernels <..., true>)
   SliceDesc s[kMaxSlices];
 };
 
 // Kernel entries, by dtype codes (F16 = 0, BF16 = 1, F32 = 2), accumulate
 // flag and, for the fast kernels, the number of 32-wide rank steps they hold
 // in registers (rank <= 32 * steps; ks0: rank <= 16, one step, input tile not
-// shared between waves).  nullptr: no such kernel.
+// shared between waves) and whether row tiles gather per-token rows (the
+// caller sets Params::gather to match).  nullptr: no such kernel.
 //
 // Fast kernels need rank % 8 == 0, every slice width % 8 == 0 and 16-byte
 // aligned input rows, weight rows and output column groups; the generic
 // kernel takes any shape, stride and alignment.
-const void* fast_kernel_ks0(int xd, int wd, int od, bool add);
-const void* fast_kernel_ks1(int xd, int wd, int od, bool add);
-const void* fast_kernel_ks2(int xd, int wd, int od, bool add);
-const void* fast_kernel_ks4(int xd, int wd, int od, bool add);
-const void* fast_kernel_ks8(int xd, int wd, int od, bool add);
+const void* fast_kernel_ks0(int xd, int wd, int od, bool add, bool gather);
+const void* fast_kernel_ks1(int xd, int wd, int od, bool add, bool gather);
+const void* fast_kernel_ks2(int xd, int wd, int od, bool add, bool gather);
+const void* fast_kernel_ks4(int xd, int wd, int od, bool add, bool gather);
+const void* fast_kernel_ks8(int xd, int wd, int od, bool add, bool gather);
 const void* generic_kernel(int xd, int wd, int od, bool add);
 
 }  // namespace sgmv
