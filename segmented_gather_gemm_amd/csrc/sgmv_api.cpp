@@ -34,6 +34,13 @@ constexpr int32_t kBandTiles = SGMV_BAND_TILES;
 #define SGMV_CHUNK_UNITS 32
 #endif
 constexpr int32_t kChunkUnits = SGMV_CHUNK_UNITS;
+
+// Smallest number of work units per workgroup the grid is sized for (from the
+// host's upper bound on units; large problems run at full occupancy anyway).
+#ifndef SGMV_UNITS_PER_WORKGROUP
+#define SGMV_UNITS_PER_WORKGROUP 3
+#endif
+constexpr int64_t kUnitsPerWorkgroup = SGMV_UNITS_PER_WORKGROUP;
 static_assert(kChunkUnits >= 1 && kBandTiles % kChunkUnits == 0,
               "chunks must not straddle a column tile's run of a band");
 
@@ -283,7 +290,11 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   hipError_t e = device_capacity(kernel, lds, &capacity);
   if (e != hipSuccess)
     return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
-  int64_t grid = units < capacity ? units : capacity;
+  // About kUnitsPerWorkgroup units per workgroup at least: a workgroup that
+  // holds several units overlaps each one's loads with the previous one's
+  // work, and idle workgroups still pay for the segment table.
+  const int64_t want = (units + kUnitsPerWorkgroup - 1) / kUnitsPerWorkgroup;
+  int64_t grid = want < capacity ? want : capacity;
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
