@@ -15,7 +15,7 @@
  * are left untouched, as is every column outside the window.  Products are
  * accumulated in fp32 and rounded once (nearest even) to the output dtype.
  * float32 inputs are first rounded to the 16-bit weight dtype (the page's
- * CAST_TYPE, "mixed-precision type casting").
+ * CAST_TYPE mixed-precision cast).
  *
  * Every call enqueues GPU work on `stream` and returns; nothing here
  * synchronises, copies device data to the host or allocates memory.  All

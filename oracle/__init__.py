@@ -1,4 +1,5 @@
-"""CPU oracle for SGMV expand-slice -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for SGMV expand-slice and its LoRA-A projection -- TEST
+INFRASTRUCTURE ONLY.
 
 A ctypes binding over ``libsgmv_oracle.so`` (plain C, fp64, see
 ``sgmv_oracle.h``).  Only the tests, ``__graft_entry__.smoke()`` and the
@@ -13,8 +14,13 @@ adapter a = idx[b] != -1 and every row t in [start_b, start_b + len_b),
 
 in fp64 with a single round-to-nearest-even into the output dtype; every
 other element of ``out`` keeps its bits.  float32 inputs are first rounded
-to the 16-bit weight dtype (the page's CAST_TYPE, "mixed-precision type
-casting").
+to the 16-bit weight dtype (the page's CAST_TYPE mixed-precision cast).
+
+``shrink`` is the LoRA-A projection that produces the expand's inputs (the
+page describes them as that projection's low-rank activations):
+``y[t][k] = rne(scale * sum_h x[t][h] * A[a][k][h])`` for rows of active
+segments, lora_A stacked (lora_num, rank, hidden); see ``sgmv_oracle.h``
+for the readings it takes where the page is silent.
 
 Arrays are numpy: 16-bit storage as ``uint16`` bit patterns, float32 as
 ``float32``.  Dtype names are "f16", "bf16", "f32".
@@ -50,6 +56,10 @@ class _Slice(ctypes.Structure):
                 ("offset", ctypes.c_int64)]
 
 
+class _ShrinkSlice(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64)]
+
+
 class _Report(ctypes.Structure):
     _fields_ = [("checked_values", ctypes.c_int64), ("checked_untouched", ctypes.c_int64),
                 ("bad_values", ctypes.c_int64), ("bad_untouched", ctypes.c_int64),
@@ -79,6 +89,9 @@ def _load():
         lib.orc_check.argtypes = [p, i, i64, i64, p, p, i, i64, i64, i64, p, p, p, i64, i,
                                   ctypes.c_double, ctypes.c_double, p, i64, i, p]
         lib.orc_check.restype = i
+        lib.orc_shrink.argtypes = [p, i, i64, i64, i64, p, i, i, i64, i64, i, p, p, p, i64,
+                                   ctypes.c_double, p, i64, p, i]
+        lib.orc_shrink.restype = i
         lib.orc_threads.argtypes = [i]
         lib.orc_threads.restype = i
         _lib = lib
@@ -242,3 +255,48 @@ def check(slices: Sequence[Slice], prior: np.ndarray, cand: np.ndarray, out_dtyp
     first = None if rep.first_bad_row < 0 else (rep.first_bad_row, rep.first_bad_col)
     return Report(rep.checked_values, rep.checked_untouched, rep.bad_values, rep.bad_untouched,
                   rep.max_abs_err, rep.max_tol_ratio, first)
+
+
+def shrink(x: np.ndarray, x_dtype: str, lora_a: Sequence[np.ndarray], a_dtype: str,
+           outs: Sequence[np.ndarray], out_dtype: str, start, lens, idx, scale: float = 1.0,
+           rows: Optional[np.ndarray] = None, want_ref: bool = False,
+           threads: int = 0) -> Optional[list]:
+    """LoRA-A projection into ``outs`` (one (T, K) array per lora_A stack
+    (L, K, H)), in place: row t of an active segment with adapter a gets
+    ``rne(scale * sum_h x[t][h] * A[a][k][h])``; other rows keep their bits
+    (see orc_shrink for the readings).  ``rows`` restricts the work to those
+    rows.  Returns, if ``want_ref``, one (T, K) fp64 array per slice of the
+    exact pre-rounding values (NaN where not computed)."""
+    lib = _load()
+    _check_storage(x, x_dtype, "x")
+    if x.ndim != 2 or x.strides[1] != x.itemsize:
+        raise ValueError("x must be 2-D with unit column stride")
+    T, H = x.shape
+    if len(lora_a) != len(outs) or not lora_a:
+        raise ValueError("one output per lora_A stack")
+    keep = [np.ascontiguousarray(a) for a in lora_a]
+    L, K = keep[0].shape[0], keep[0].shape[1]
+    arr = (_ShrinkSlice * len(keep))()
+    for i, (a, o) in enumerate(zip(keep, outs)):
+        _check_storage(a, a_dtype, "lora_a")
+        _check_storage(o, out_dtype, "out")
+        if a.shape != (L, K, H):
+            raise ValueError(f"lora_a shape {a.shape} is not ({L}, {K}, {H})")
+        if o.ndim != 2 or o.shape != (T, K) or o.strides[1] != o.itemsize:
+            raise ValueError(f"out must be ({T}, {K}) with unit column stride")
+        arr[i] = _ShrinkSlice(_ptr(a), _ptr(o), o.strides[0] // o.itemsize)
+    start, lens, idx = _meta(start, lens, idx)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    ref = np.full(len(keep) * T * K, np.nan, dtype=np.float64) if want_ref else None
+    rc = lib.orc_shrink(_ptr(x), DTYPE_CODES[x_dtype], x.strides[0] // x.itemsize, T, H, arr,
+                        len(keep), DTYPE_CODES[a_dtype], K, L, DTYPE_CODES[out_dtype],
+                        _ptr(start), _ptr(lens), _ptr(idx), len(start), float(scale),
+                        _ptr(rows_arr) if rows_arr is not None else None,
+                        len(rows_arr) if rows_arr is not None else 0,
+                        _ptr(ref) if want_ref else None, threads)
+    del keep
+    if rc != OK:
+        raise OracleError(rc, "shrink")
+    if not want_ref:
+        return None
+    return [ref[i * T * K:(i + 1) * T * K].reshape(T, K) for i in range(len(outs))]

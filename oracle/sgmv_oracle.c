@@ -15,7 +15,7 @@
  *     b_seq_start_loc gives each segment's first row, seq_len_tensor its
  *     length; lora index -1 means no LoRA is applied (rows untouched);
  *     add_inputs=false (default) overwrites, true accumulates.
- *   - Description / Signature (CAST_TYPE, "mixed-precision type casting"):
+ *   - Description / Signature (CAST_TYPE, the mixed-precision cast):
  *     float32 inputs are rounded to the 16-bit weight type before the
  *     products.
  * Readings where the page is silent are listed beside the code below.
@@ -477,6 +477,112 @@ int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
   free(wval);
   free(col_slice);
   free(part);
+  free(owner);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------- */
+/* LoRA-A projection (shrink), see sgmv_oracle.h.                           */
+/* ---------------------------------------------------------------------- */
+typedef struct {
+  const void* x;
+  int x_dtype, a_dtype, out_dtype;
+  int64_t x_stride, H, K, T;
+  const orc_shrink_slice* s;
+  int ns;
+  const double* a_tab;   /* exact value of every 16-bit weight pattern */
+  const double* x_tab;   /* same for 16-bit inputs (NULL for float32)   */
+  const int64_t* owner;
+  const int64_t* idx;
+  const int64_t* rows;
+  double scale;
+  double* ref;
+  int failed;
+} shrink_ctx;
+
+/* Exact values of all 2^16 patterns of a 16-bit format (from orc_decode). */
+static double* decode_table16(int dtype) {
+  double* t = (double*)malloc(sizeof(double) * 65536);
+  if (!t) return NULL;
+  for (uint32_t b = 0; b < 65536; ++b) t[b] = orc_decode(dtype, b);
+  return t;
+}
+
+static void shrink_rows(void* p, int worker, int64_t begin, int64_t end) {
+  (void)worker;
+  shrink_ctx* c = (shrink_ctx*)p;
+  double* xrow = (double*)malloc(sizeof(double) * (size_t)c->H);
+  if (!xrow) {
+    __atomic_store_n(&c->failed, 1, __ATOMIC_RELAXED);
+    return;
+  }
+  for (int64_t i = begin; i < end; ++i) {
+    const int64_t t = c->rows ? c->rows[i] : i;
+    const int64_t b = c->owner[t];
+    if (b < 0) continue;  /* no active segment holds row t: untouched */
+    const int64_t a = c->idx[b];
+    /* Input row as it enters the products (float32 rounded to the weight
+     * type, as in the expand). */
+    for (int64_t h = 0; h < c->H; ++h) {
+      const uint32_t bits = load_bits(c->x_dtype, c->x, t * c->x_stride + h);
+      if (c->x_dtype == ORC_F32) {
+        const double v = orc_decode(ORC_F32, bits);
+        xrow[h] = c->a_tab[orc_encode(c->a_dtype, v)];
+      } else {
+        xrow[h] = c->x_tab[bits];
+      }
+    }
+    for (int si = 0; si < c->ns; ++si) {
+      const orc_shrink_slice* s = &c->s[si];
+      for (int64_t k = 0; k < c->K; ++k) {
+        const int64_t row_a = (a * c->K + k) * c->H;  /* A[a][k][:] */
+        double r = 0.0;
+        for (int64_t h = 0; h < c->H; ++h)
+          r += xrow[h] * c->a_tab[load_bits(c->a_dtype, s->a, row_a + h)];
+        r *= c->scale;
+        if (c->ref) c->ref[(si * c->T + t) * c->K + k] = r;
+        store_bits(c->out_dtype, s->out, t * s->out_stride + k, orc_encode(c->out_dtype, r));
+      }
+    }
+  }
+  free(xrow);
+}
+
+int orc_shrink(const void* x, int x_dtype, int64_t x_stride, int64_t T, int64_t H,
+               const orc_shrink_slice* slices, int num_slices, int a_dtype, int64_t K,
+               int64_t L, int out_dtype, const int64_t* start, const int64_t* lens,
+               const int64_t* idx, int64_t batches, double scale, const int64_t* rows,
+               int64_t num_rows, double* ref, int threads) {
+  int eb, mb;
+  if (!slices || num_slices < 1 || K < 1 || H < 1 || L < 0 || T < 0 || batches < 0 ||
+      x_stride < H || num_rows < 0)
+    return ORC_BAD_ARGUMENT;
+  if (!format_of(out_dtype, &eb, &mb) || !format_of(x_dtype, &eb, &mb)) return ORC_BAD_ARGUMENT;
+  /* Same dtype rules as the expand: 16-bit weights, inputs of the weight
+   * type or float32. */
+  if (a_dtype != ORC_F16 && a_dtype != ORC_BF16) return ORC_BAD_ARGUMENT;
+  if (x_dtype != a_dtype && x_dtype != ORC_F32) return ORC_BAD_ARGUMENT;
+  for (int si = 0; si < num_slices; ++si)
+    if (slices[si].out_stride < K) return ORC_BAD_ARGUMENT;
+  if (rows)
+    for (int64_t i = 0; i < num_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= T) return ORC_BAD_ARGUMENT;
+  int64_t* owner = NULL;
+  int rc = build_owner(T, L, start, lens, idx, batches, &owner);
+  if (rc != ORC_OK) return rc;
+  double* a_tab = decode_table16(a_dtype);
+  double* x_tab = x_dtype == ORC_F32 ? NULL : decode_table16(x_dtype);
+  if (!a_tab || (x_dtype != ORC_F32 && !x_tab)) {
+    free(a_tab); free(x_tab); free(owner);
+    return ORC_NO_MEMORY;
+  }
+  const int64_t n = rows ? num_rows : T;
+  shrink_ctx c = {x, x_dtype, a_dtype, out_dtype, x_stride, H, K, T, slices, num_slices,
+                  a_tab, x_tab, owner, idx, rows, scale, ref, 0};
+  rc = run_chunks(workers_for(threads, n), n, shrink_rows, &c);
+  if (rc == ORC_OK && c.failed) rc = ORC_NO_MEMORY;
+  free(a_tab);
+  free(x_tab);
   free(owner);
   return rc;
 }

@@ -107,6 +107,45 @@ int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
               const int64_t* rows, int64_t num_rows, int threads,
               orc_report* report);
 
+/*
+ * LoRA-A projection (shrink): the step that produces the expand's `inputs`.
+ *
+ * The wiki page "Implementation: Predibase Lorax SGMV Expand Slice Kernel"
+ * (I/O Contract, Inputs; Usage Examples) describes `inputs` as the low-rank
+ * activations of the LoRA A projection, packed across sequences, shape
+ * (total_tokens, rank).  The page does not print the projection itself;
+ * this oracle takes the plainest reading consistent with it and with the
+ * expand's conventions:
+ *   - lora_A is stacked (lora_num, rank, hidden), out-by-in like lora_B;
+ *   - for each segment b with adapter a = idx[b] != -1 and each row t of
+ *     the segment, y[t][k] = scale * sum_h x[t][h] * A[a][k][h];
+ *   - float32 inputs are rounded to the 16-bit weight type first (the same
+ *     CAST_TYPE rule as the expand);
+ *   - the result overwrites y (one rounding to the output dtype); rows of
+ *     inactive segments, and rows outside every segment, are untouched.
+ * Several slices (lora_A stacks with one output each, same rank) share the
+ * input, as the fused QKV and gate/up layers do.
+ */
+typedef struct {
+  const void* a;       /* lora_A stack, (L, K, H) contiguous, a_dtype      */
+  void* out;           /* (T, K) rows, row stride out_stride elements      */
+  int64_t out_stride;
+} orc_shrink_slice;
+
+/*
+ * Project rows of x (T rows of H elements, row stride x_stride) into every
+ * slice's output.  If `rows` is not NULL only those `num_rows` rows are
+ * computed (each listed once).  If `ref` is not NULL it receives, per slice
+ * in order, a (T, K) fp64 array of the exact pre-rounding values of the
+ * computed active rows (other entries untouched).  Returns an ORC_* code;
+ * after an argument, segment or index error no output is changed.
+ */
+int orc_shrink(const void* x, int x_dtype, int64_t x_stride, int64_t T, int64_t H,
+               const orc_shrink_slice* slices, int num_slices, int a_dtype, int64_t K,
+               int64_t L, int out_dtype, const int64_t* start, const int64_t* lens,
+               const int64_t* idx, int64_t batches, double scale, const int64_t* rows,
+               int64_t num_rows, double* ref, int threads);
+
 /* Worker threads a call with `threads` uses at most (<= 0: the CPUs in the
  * process's affinity mask). */
 int orc_threads(int threads);

@@ -310,3 +310,155 @@ def custom(lens: Sequence[int], idx: Sequence[int], *, K: int, N: int, H: int, o
     ofull = draw((T, H + out_pad), 1.0, -8, 8, out_dtype)
     out0 = ofull[:, :H] if out_pad else ofull
     return Workload(name, slices, out0, out_dtype, start, lens, idx, add, K, L, seed)
+
+
+# ---------------------------------------------------------------------------
+# LoRA-A projection (shrink) workloads: the step that produces the expand's
+# ``inputs`` (total_tokens, rank).  Same segment draws as the expand
+# workload they feed; lora_A is (L, K, H_in); one (T, K) output per slice,
+# prefilled so that rows the call must leave alone are checked.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ShrinkWorkload:
+    name: str
+    x: np.ndarray          # (T, H_in) or wider rows
+    x_dtype: str
+    lora_a: List[np.ndarray]   # per slice (L, K, H_in) contiguous
+    a_dtype: str
+    outs0: List[np.ndarray]    # per slice (T, K) prior output
+    out_dtype: str
+    start: np.ndarray
+    lens: np.ndarray
+    idx: np.ndarray
+    scale: float
+    K: int
+    L: int
+    seed: int = 0
+    notes: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def batches(self) -> int:
+        return int(len(self.lens))
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.lens.max()) if len(self.lens) else 0
+
+    def active_mask(self) -> np.ndarray:
+        return (self.idx != -1) & (self.lens > 0)
+
+
+def _shrink_parts(rng, T, H, K, L, n_slices, x_dtype, a_dtype, out_dtype, values="normal",
+                  x_pad=0, out_pad=0):
+    def draw(shape, sigma, lo, hi, dtype):
+        if values == "int":
+            return integers_as(rng, shape, lo, hi, dtype)
+        return normal(rng, shape, sigma, dtype)
+
+    # lora_A ~ N(0, 1/H) keeps the projection ~ N(0, 1) for x ~ N(0, 1).
+    sigma_a = 1.0 / math.sqrt(max(H, 1))
+    lora_a = [draw((L, K, H), sigma_a, -3, 3, a_dtype) for _ in range(n_slices)]
+    xfull = draw((T, H + x_pad), 1.0, -3, 3, x_dtype)
+    x = xfull[:, :H] if x_pad else xfull
+    outs0 = []
+    for _ in range(n_slices):
+        o = draw((T, K + out_pad), 1.0, -8, 8, out_dtype)
+        outs0.append(o[:, :K] if out_pad else o)
+    return x, lora_a, outs0
+
+
+def shrink_q_proj(seed: int = 0) -> ShrinkWorkload:
+    """LoRA-A projection feeding llama7b_q_proj: its 8 segments and indices;
+    hidden 4096 -> rank 16; 4 adapters, bf16 in, weights and out; scale 2
+    (alpha 32 over rank 16)."""
+    base = llama7b_q_proj(seed)
+    rng = np.random.default_rng(seed + 1000)
+    H, K, L = 4096, 16, 4
+    x, lora_a, outs0 = _shrink_parts(rng, base.T, H, K, L, 1, "bf16", "bf16", "bf16")
+    return ShrinkWorkload("shrink_q_proj", x, "bf16", lora_a, "bf16", outs0, "bf16",
+                          base.start, base.lens, base.idx, 2.0, K, L, seed)
+
+
+def shrink_qkv(seed: int = 0) -> ShrinkWorkload:
+    """Fused QKV LoRA-A projection feeding gqa_qkv: its 32 segments; hidden
+    4096 -> 3 slices of rank 32 from one shared input; 16 adapters; bf16."""
+    base = gqa_qkv(seed)
+    rng = np.random.default_rng(seed + 1000)
+    H, K, L = 4096, 32, 16
+    x, lora_a, outs0 = _shrink_parts(rng, base.T, H, K, L, 3, "bf16", "bf16", "bf16")
+    return ShrinkWorkload("shrink_qkv", x, "bf16", lora_a, "bf16", outs0, "bf16",
+                          base.start, base.lens, base.idx, 1.0, K, L, seed)
+
+
+def shrink_gate_up(seed: int = 0) -> ShrinkWorkload:
+    """Gate/up LoRA-A projection feeding mlp_gate_up: its 64 segments (about
+    16k tokens); hidden 4096 -> 2 slices of rank 64; 64 adapters; bf16 input
+    and weights, float32 output (the expand's float32 inputs)."""
+    base = mlp_gate_up(seed)
+    rng = np.random.default_rng(seed + 1000)
+    H, K, L = 4096, 64, 64
+    x, lora_a, outs0 = _shrink_parts(rng, base.T, H, K, L, 2, "bf16", "bf16", "f32")
+    return ShrinkWorkload("shrink_gate_up", x, "bf16", lora_a, "bf16", outs0, "f32",
+                          base.start, base.lens, base.idx, 1.0, K, L, seed)
+
+
+def shrink_skewed(seed: int = 0) -> ShrinkWorkload:
+    """LoRA-A projection feeding skewed_mixed: its 256 segments (one of 8192
+    tokens, 255 short, 64 without adapter); hidden 8192 -> rank 128; 128
+    adapters; fp16."""
+    base = skewed_mixed(seed)
+    rng = np.random.default_rng(seed + 1000)
+    H, K, L = 8192, 128, 128
+    x, lora_a, outs0 = _shrink_parts(rng, base.T, H, K, L, 1, "f16", "f16", "f16")
+    return ShrinkWorkload("shrink_skewed", x, "f16", lora_a, "f16", outs0, "f16",
+                          base.start, base.lens, base.idx, 1.0, K, L, seed)
+
+
+def shrink_tiny(seed: int = 0) -> ShrinkWorkload:
+    """The page's worked example segments (lengths [4, 6] at starts [0, 4],
+    indices [1, -1]) through a LoRA-A projection: hidden 64 -> rank 8, 2
+    adapters, fp16."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([4, 6], dtype=np.int64)
+    idx = np.array([1, -1], dtype=np.int64)
+    x, lora_a, outs0 = _shrink_parts(rng, 10, 64, 8, 2, 1, "f16", "f16", "f16")
+    return ShrinkWorkload("shrink_tiny", x, "f16", lora_a, "f16", outs0, "f16",
+                          exclusive_cumsum(lens), lens, idx, 1.0, 8, 2, seed)
+
+
+def shrink_custom(lens: Sequence[int], idx: Sequence[int], *, H: int, K: int, L: int,
+                  slices: int = 1, x_dtype: str = "bf16", a_dtype: str = "bf16",
+                  out_dtype: str = "bf16", scale: float = 1.0, seed: int = 0,
+                  start: Optional[Sequence[int]] = None, T: Optional[int] = None,
+                  values: str = "normal", x_pad: int = 0, out_pad: int = 0,
+                  name: str = "shrink_custom") -> ShrinkWorkload:
+    """A shrink workload with explicit segments (see custom() for ``values``,
+    ``x_pad`` and ``out_pad``)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    start = exclusive_cumsum(lens) if start is None else np.asarray(start, dtype=np.int64)
+    if T is None:
+        T = int((start + lens).max()) if len(lens) else 0
+    x, lora_a, outs0 = _shrink_parts(rng, T, H, K, L, slices, x_dtype, a_dtype, out_dtype,
+                                     values, x_pad, out_pad)
+    return ShrinkWorkload(name, x, x_dtype, lora_a, a_dtype, outs0, out_dtype, start, lens, idx,
+                          float(scale), K, L, seed)
+
+
+SHRINK_WORKLOADS: Dict[str, Callable[..., ShrinkWorkload]] = {
+    "shrink_tiny": shrink_tiny,
+    "shrink_q_proj": shrink_q_proj,
+    "shrink_qkv": shrink_qkv,
+    "shrink_gate_up": shrink_gate_up,
+    "shrink_skewed": shrink_skewed,
+}
