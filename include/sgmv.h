@@ -2,7 +2,8 @@
  * sgmv.h -- C ABI of libsgmv: SGMV expand-slice on AMD Instinct MI355X (gfx950).
  *
  * Operation (wiki page "Implementation: Predibase Lorax SGMV Expand Slice
- * Kernel", Description and I/O Contract): for each segment b of a packed
+ * Kernel", Description and I/O Contract), and the LoRA-A projection that
+ * produces its inputs (sgmv_shrink, below): for each segment b of a packed
  * batch and each token m of that segment, row t = b_seq_start_loc[b] + m of
  * the output gets, in its column window [slice_offset, slice_offset +
  * slice_size),
@@ -32,7 +33,7 @@
 extern "C" {
 #endif
 
-#define SGMV_ABI_VERSION 2
+#define SGMV_ABI_VERSION 3
 #define SGMV_MAX_SLICES 8      /* slices per multi-slice call                       */
 #define SGMV_MAX_RANK 256      /* largest rank the register-tiled kernels take; larger
                                   ranks (any size) run on the generic kernel */
@@ -153,6 +154,63 @@ sgmv_status sgmv_expand_multi_slice(const sgmv_slice* slices, int num_slices, sg
 sgmv_status sgmv_bgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
                                    const int64_t* lora_indices, int64_t slice_offset,
                                    int64_t slice_size, int add_inputs, hipStream_t stream);
+
+/* One slice of a fused LoRA-A projection for sgmv_shrink_multi_slice. */
+typedef struct {
+  sgmv_stack lora_a;      /* (lora_num, rank, hidden)                     */
+  sgmv_matrix out;        /* (total_tokens, rank)                         */
+} sgmv_shrink_slice;
+
+/*
+ * sgmv_shrink -- the LoRA-A projection that produces sgmv_expand_slice's
+ * `inputs`.  The page (I/O Contract, Inputs; Usage Examples) describes those
+ * inputs as the low-rank activations of the LoRA A projection, packed across
+ * sequences, (total_tokens, rank); it prints no formula for the projection,
+ * so this takes the plainest reading consistent with the expand:
+ *
+ *     out[t][k] = scale * sum_h inputs[t][h] * lora_a[a][k][h],   k < rank,
+ *
+ * for each segment b with a = lora_indices[b] != -1 and each row t of the
+ * segment.  lora_a is stored (lora_num, rank, hidden) -- out-by-in, like
+ * lora_b -- so the product is inputs . lora_a[a]^T.  Products are accumulated
+ * in fp32, multiplied by `scale` and rounded once (nearest even) to the
+ * output dtype; float32 inputs are first rounded to the 16-bit weight dtype.
+ * The call overwrites: rows of index -1 segments and rows outside every
+ * segment are left untouched.
+ *
+ * inputs        device (total_tokens, hidden) f16/bf16/f32; read only.
+ * lora_a        device (lora_num, rank, hidden) f16/bf16, contiguous; read
+ *               only.  inputs must be lora_a's dtype or f32.
+ *               rank <= SGMV_MAX_RANK (else SGMV_ERR_UNSUPPORTED).
+ * out           device (total_tokens, rank) f16/bf16/f32, row_stride >= rank;
+ *               written only at rows of active segments.  Must not overlap
+ *               inputs, lora_a or the metadata.
+ * b_seq_start_loc, seq_lens, lora_indices, batches, max_seq_len, stream:
+ *               as for sgmv_expand_slice, with the same device-side
+ *               preconditions.
+ * scale         fp32 factor applied to every sum (1 for the plain product).
+ *
+ * Returns SGMV_OK, or a status with nothing launched; batches == 0 or
+ * total_tokens == 0 return SGMV_OK without a launch.
+ */
+sgmv_status sgmv_shrink(sgmv_matrix inputs, sgmv_stack lora_a, sgmv_matrix out,
+                        const int64_t* b_seq_start_loc, const int64_t* seq_lens,
+                        const int64_t* lora_indices, int64_t batches, int64_t max_seq_len,
+                        float scale, hipStream_t stream);
+
+/*
+ * sgmv_shrink_multi_slice -- several LoRA-A projections of the same inputs
+ * (the Q, K and V, or gate and up, adapters of a fused layer) in one call
+ * that reads the inputs once.  Equal, bit for bit, to calling sgmv_shrink
+ * once per slice.  slices: host array of 1..SGMV_MAX_SLICES descriptors,
+ * read during the call only; all share rank, lora_num, the lora_a dtype and
+ * the output dtype; outputs must not overlap each other.
+ */
+sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice* slices,
+                                    int num_slices, const int64_t* b_seq_start_loc,
+                                    const int64_t* seq_lens, const int64_t* lora_indices,
+                                    int64_t batches, int64_t max_seq_len, float scale,
+                                    hipStream_t stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if
  * none).  The pointer stays valid until the thread's next libsgmv call. */

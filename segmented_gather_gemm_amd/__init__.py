@@ -11,6 +11,9 @@ Lorax SGMV Expand Slice Kernel" (Signature; I/O Contract):
     sgmv_expand_slice(inputs, lora_b_weights, output_tensor, b_seq_start_loc,
                       seq_len_tensor, lora_indices_tensor, batches,
                       max_seq_length, slice_offset, slice_size, add_inputs=False)
+
+plus the LoRA-A projection that produces those inputs (sgmv_shrink) and the
+per-token and multi-slice forms.
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ MAX_SLICES = 8
 
 # Every symbol include/sgmv.h declares.
 EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_bgmv_expand_slice",
-                    "sgmv_last_error", "sgmv_abi_version")
+                    "sgmv_shrink", "sgmv_shrink_multi_slice", "sgmv_last_error",
+                    "sgmv_abi_version")
 
 
 class Matrix(ctypes.Structure):
@@ -42,6 +46,10 @@ class Stack(ctypes.Structure):
 class SliceDesc(ctypes.Structure):
     _fields_ = [("inputs", Matrix), ("lora_b", Stack), ("slice_offset", ctypes.c_int64),
                 ("slice_size", ctypes.c_int64)]
+
+
+class ShrinkSliceDesc(ctypes.Structure):
+    _fields_ = [("lora_a", Stack), ("out", Matrix)]
 
 
 def _hip_runtimes_mapped():
@@ -81,6 +89,11 @@ def _load_library() -> ctypes.CDLL:
     lib.sgmv_expand_multi_slice.restype = ctypes.c_int
     lib.sgmv_bgmv_expand_slice.argtypes = [Matrix, Stack, Matrix, p, i64, i64, ctypes.c_int, p]
     lib.sgmv_bgmv_expand_slice.restype = ctypes.c_int
+    lib.sgmv_shrink.argtypes = [Matrix, Stack, Matrix, p, p, p, i64, i64, ctypes.c_float, p]
+    lib.sgmv_shrink.restype = ctypes.c_int
+    lib.sgmv_shrink_multi_slice.argtypes = [Matrix, ctypes.POINTER(ShrinkSliceDesc), ctypes.c_int,
+                                            p, p, p, i64, i64, ctypes.c_float, p]
+    lib.sgmv_shrink_multi_slice.restype = ctypes.c_int
     lib.sgmv_last_error.argtypes = []
     lib.sgmv_last_error.restype = ctypes.c_char_p
     lib.sgmv_abi_version.argtypes = []
@@ -247,10 +260,59 @@ def bgmv_expand_slice(inputs, lora_b_weights, output_tensor, lora_indices_tensor
     return output_tensor
 
 
+def _stack_a(w, what: str) -> Stack:
+    if w.dim() != 3:
+        raise ValueError(f"{what} must be (lora_num, rank, hidden), got {tuple(w.shape)}")
+    if not w.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return Stack(w.data_ptr(), _dtype_code(w), w.shape[0], w.shape[1], w.shape[2])
+
+
+def sgmv_shrink(inputs, lora_a_weights, output_tensor, b_seq_start_loc, seq_len_tensor,
+                lora_indices_tensor, batches: int, max_seq_length: int, scaling: float = 1.0):
+    """LoRA-A projection, in place: output_tensor[start_b + m] =
+    scaling * inputs[start_b + m] @ lora_a_weights[lora_indices[b]].T for every
+    segment b with index != -1 (other rows untouched); lora_a_weights is
+    (lora_num, rank, hidden).  Enqueued on the current stream."""
+    return sgmv_shrink_multi_slice(inputs, [(lora_a_weights, output_tensor)], b_seq_start_loc,
+                                   seq_len_tensor, lora_indices_tensor, batches, max_seq_length,
+                                   scaling)
+
+
+def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_seq_start_loc,
+                            seq_len_tensor, lora_indices_tensor, batches: int,
+                            max_seq_length: int, scaling: float = 1.0):
+    """Several LoRA-A projections of the same inputs (e.g. Q, K, V) reading
+    the inputs once.  ``slices``: sequence of (lora_a_weights, output_tensor).
+    Bit-identical to one sgmv_shrink call per slice."""
+    import torch
+    if not 1 <= len(slices) <= MAX_SLICES:
+        raise ValueError(f"1..{MAX_SLICES} slices, got {len(slices)}")
+    device, (start, lens, idx) = _common(inputs, [
+        (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
+        (lora_indices_tensor, "lora_indices_tensor")])
+    if len(start) < batches or len(lens) < batches or len(idx) < batches:
+        raise ValueError("segment metadata shorter than batches")
+    arr = (ShrinkSliceDesc * len(slices))()
+    for i, (w, o) in enumerate(slices):
+        if w.device != device or o.device != device:
+            raise ValueError(f"slice {i} must be on {device}")
+        arr[i] = ShrinkSliceDesc(_stack_a(w, f"slice {i} lora_a"), _matrix(o, f"slice {i} output"))
+    x = _matrix(inputs, "inputs")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    with _on_device(device):
+        rc = lib.sgmv_shrink_multi_slice(x, arr, len(slices), start.data_ptr(), lens.data_ptr(),
+                                         idx.data_ptr(), int(batches), int(max_seq_length),
+                                         float(scaling), stream)
+    if rc != SGMV_OK:
+        _raise(rc)
+    return [o for _, o in slices]
+
+
 def abi_version() -> int:
     return lib.sgmv_abi_version()
 
 
-__all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "bgmv_expand_slice", "abi_version",
-           "SgmvError", "lib",
-           "Matrix", "Stack", "SliceDesc", "EXPORTED_SYMBOLS", "LIBRARY_PATH"]
+__all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "bgmv_expand_slice", "sgmv_shrink",
+           "sgmv_shrink_multi_slice", "abi_version", "SgmvError", "lib",
+           "Matrix", "Stack", "SliceDesc", "ShrinkSliceDesc", "EXPORTED_SYMBOLS", "LIBRARY_PATH"]

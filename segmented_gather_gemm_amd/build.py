@@ -1,8 +1,9 @@
 """Build libsgmv.so in-tree with hipcc for gfx950 (MI355X).
 
 The library holds the C entry points (csrc/sgmv_api.cpp) and the gfx950
-kernels (csrc/sgmv_fast_ks*.hip, csrc/sgmv_generic.hip, all built from
-csrc/sgmv_device.h) with the code object embedded; nothing is
+kernels (csrc/sgmv_fast_ks*.hip, csrc/sgmv_generic.hip, built from
+csrc/sgmv_device.h; csrc/sgmv_shrink_*.hip, built from csrc/sgmv_shrink.h)
+with the code object embedded; nothing is
 compiled at run time.  Packed-fp32 VALU instructions are disabled for every
 HIP translation unit.
 """
@@ -18,7 +19,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libsgmv.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("sgmv_api.cpp", "sgmv_generic.hip", "sgmv_fast_ks0.hip", "sgmv_fast_ks1.hip",
-            "sgmv_fast_ks2.hip", "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip")]
+            "sgmv_fast_ks2.hip", "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip",
+            "sgmv_shrink_generic.hip", "sgmv_shrink_kt1.hip", "sgmv_shrink_kt2.hip",
+            "sgmv_shrink_kt4.hip", "sgmv_shrink_kt8.hip", "sgmv_shrink_kt16.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

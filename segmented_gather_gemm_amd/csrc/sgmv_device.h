@@ -252,10 +252,11 @@ struct SegTable {
 // trip per field.  Touch every 64-byte line of the argument block at kernel
 // entry so all of them are fetched together; later reads hit the scalar
 // cache.
-__device__ __forceinline__ void prefetch_params(const Params& p) {
+template <typename P>
+__device__ __forceinline__ void prefetch_params(const P& p) {
   const uint32_t* w = reinterpret_cast<const uint32_t*>(&p);
-  constexpr int kLast = (int)(sizeof(Params) / 4) - 1;
-  static_assert(sizeof(Params) <= 576, "touch list below covers 9 lines");
+  constexpr int kLast = (int)(sizeof(P) / 4) - 1;
+  static_assert(sizeof(P) <= 576, "touch list below covers 9 lines");
   asm volatile("" ::"s"(w[0]), "s"(w[16 < kLast ? 16 : kLast]), "s"(w[32 < kLast ? 32 : kLast]),
                "s"(w[48 < kLast ? 48 : kLast]), "s"(w[64 < kLast ? 64 : kLast]),
                "s"(w[80 < kLast ? 80 : kLast]), "s"(w[96 < kLast ? 96 : kLast]),
@@ -273,10 +274,13 @@ __device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
 }
 
 
-// Fill the table (every thread of the workgroup takes part); returns the
-// total number of row tiles (wave-uniform).
-__device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTable& tab,
-                                                    int32_t* wave_total) {
+// Fill the table (every thread of the workgroup takes part) with row tiles
+// of `tile_rows` rows; returns the total number of row tiles (wave-uniform).
+// P: the kernel's argument block (segment metadata fields as in Params).
+template <typename P>
+__device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& tab,
+                                                    int32_t* wave_total,
+                                                    int32_t tile_rows = kTileRows) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -291,7 +295,7 @@ __device__ __forceinline__ int32_t build_tile_table(const Params& p, const SegTa
     *row = active ? (int32_t)st : 0;
     *end = active ? (int32_t)(st + ln) : 0;
     *a32 = active ? (int32_t)a : -1;
-    *tiles = active ? (int32_t)((ln + kTileRows - 1) / kTileRows) : 0;
+    *tiles = active ? (int32_t)((ln + tile_rows - 1) / tile_rows) : 0;
   };
   // First pass: table slot of every segment; tile_start[slot] temporarily
   // holds the segment's tile count.
@@ -437,7 +441,8 @@ __device__ __forceinline__ int column_group_tile(const Params& p, int g) {
 // This workgroup's contiguous range [begin, end) of the U units (sizes differ
 // by at most one); workgroup ids are remapped so each XCD gets one contiguous
 // eighth of the range.
-__device__ __forceinline__ void unit_range(const Params& p, uint32_t U, uint32_t* begin,
+template <typename P>
+__device__ __forceinline__ void unit_range(const P& p, uint32_t U, uint32_t* begin,
                                            uint32_t* end) {
   const uint32_t bid = blockIdx.x;
   const uint32_t G = (uint32_t)p.grid;
@@ -1125,30 +1130,6 @@ const void* fast_table(int xd, int wd, int od, bool add, bool gather) {
   if (wd == BF16 && xd == F32) return fast_by_out<F32, BF16, KS>(od, add, gather);
   if (wd == F16 && xd == F16) return fast_by_out<F16, F16, KS>(od, add, gather);
   if (wd == F16 && xd == F32) return fast_by_out<F32, F16, KS>(od, add, gather);
-  return nullptr;
-}
-
-template <int XD, int WD, int OD>
-const void* generic_entry(bool add) {
-  return add ? reinterpret_cast<const void*>(&expand_generic<XD, WD, OD, true>)
-             : reinterpret_cast<const void*>(&expand_generic<XD, WD, OD, false>);
-}
-
-template <int XD, int WD>
-const void* generic_by_out(int od, bool add) {
-  switch (od) {
-    case F16: return generic_entry<XD, WD, F16>(add);
-    case BF16: return generic_entry<XD, WD, BF16>(add);
-    case F32: return generic_entry<XD, WD, F32>(add);
-    default: return nullptr;
-  }
-}
-
-inline const void* generic_table(int xd, int wd, int od, bool add) {
-  if (wd == BF16 && xd == BF16) return generic_by_out<BF16, BF16>(od, add);
-  if (wd == BF16 && xd == F32) return generic_by_out<F32, BF16>(od, add);
-  if (wd == F16 && xd == F16) return generic_by_out<F16, F16>(od, add);
-  if (wd == F16 && xd == F32) return generic_by_out<F32, F16>(od, add);
   return nullptr;
 }
 

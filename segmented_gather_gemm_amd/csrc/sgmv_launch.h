@@ -62,6 +62,61 @@ struct Params {
   SliceDesc s[kMaxSlices];
 };
 
+// ---------------------------------------------------------------------------
+// LoRA-A projection (shrink): y_s[t][k] = scale * sum_h x[t][h] * A_s[a][k][h]
+// for the rows t of active segments, for every slice s (lora_A stack A_s
+// (L, K, H) and output y_s (T, K)); the slices share the input.
+// ---------------------------------------------------------------------------
+
+struct ShrinkSliceDesc {
+  const void* a;          // lora_A (L, K, H) contiguous
+  void* out;              // (T, K), row stride out_row_bytes
+  int64_t out_row_bytes;
+};
+
+// Field names of the segment metadata match Params (the segment-table
+// builder takes either).
+struct ShrinkParams {
+  const void* x;          // inputs (T, H), row stride x_row_bytes
+  const int64_t* start;
+  const int64_t* lens;
+  const int64_t* idx;
+  int64_t x_row_bytes;
+  int64_t T;
+  int32_t H;              // hidden size (< 2^26)
+  int32_t batches;
+  int32_t L;
+  int32_t K;              // rank, the same for every slice
+  int32_t num_slices;
+  int32_t k_tiles;        // 16-row tiles of K per slice, ceil(K / 16)
+  int32_t grid;
+  int32_t wave_steps;     // fast kernels: 32-wide hidden steps per wavefront
+  int32_t sort_slots;
+  int32_t per_token;
+  int32_t gather;         // always 0 (no gathered row tiles here)
+  float scale;
+  ShrinkSliceDesc s[kMaxSlices];
+};
+
+// Hidden steps (32 wide) a fast shrink kernel loads per pipeline block: as
+// many as keep about 64 registers of loads in flight per block.  `ktt` =
+// 16-row tiles of K over all slices (a power of two), `rt` = 16-row token
+// tiles per unit.
+constexpr int shrink_block_steps(int xd, int ktt, int rt) {
+  const int regs = 4 * ((xd == 2 ? 2 : 1) * rt + ktt);
+  return regs <= 8 ? 8 : regs <= 16 ? 4 : regs <= 32 ? 2 : 1;
+}
+
+// Shrink kernels by dtype codes; the fast ones by ktt (1, 2, 4, 8, 16).
+// Fast kernels need K % 8 == 0, H % 8 == 0, 16-byte aligned rows and
+// H < 2^26; the generic one takes any shape, stride and alignment.
+const void* shrink_kernel_kt1(int xd, int wd, int od);
+const void* shrink_kernel_kt2(int xd, int wd, int od);
+const void* shrink_kernel_kt4(int xd, int wd, int od);
+const void* shrink_kernel_kt8(int xd, int wd, int od);
+const void* shrink_kernel_kt16(int xd, int wd, int od);
+const void* shrink_generic_kernel(int xd, int wd, int od);
+
 // Kernel entries, by dtype codes (F16 = 0, BF16 = 1, F32 = 2), accumulate
 // flag and, for the fast kernels, the number of 32-wide rank steps they hold
 // in registers (rank <= 32 * steps; ks0: rank <= 16, one step, input tile not

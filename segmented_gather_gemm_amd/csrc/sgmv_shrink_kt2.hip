@@ -1,0 +1,9 @@
+// Fast LoRA-A projection (shrink) kernels with 2 k tile(s) of 16 rows over
+// all slices.  Device code and design notes: sgmv_shrink.h.
+#include "sgmv_shrink.h"
+
+namespace sgmv {
+
+const void* shrink_kernel_kt2(int xd, int wd, int od) { return dev::shrink_table<2>(xd, wd, od); }
+
+}  // namespace sgmv

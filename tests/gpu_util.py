@@ -100,3 +100,122 @@ def assert_parity(wl, cand_bits, rows=None):
                     f"{rep.max_abs_err:.3g}, worst err/tol {rep.max_tol_ratio:.3g}")
     assert rep.checked_values > 0 or not wl.active_mask().any()
     return rep
+
+
+# --------------------------------------------------------------------------
+# LoRA-A projection (shrink).
+# --------------------------------------------------------------------------
+
+def _device_clone(t):
+    """Clone keeping a strided view's row stride (padding zeroed)."""
+    import torch
+    if t.is_contiguous():
+        return t.clone()
+    full = torch.zeros((t.shape[0], t.stride(0)), dtype=t.dtype, device=t.device)
+    full[:, :t.shape[1]] = t
+    return full[:, :t.shape[1]]
+
+
+class DeviceShrink:
+    """A shrink workload's tensors on the GPU."""
+
+    def __init__(self, wl, device="cuda"):
+        import torch
+        self.wl = wl
+        self.start = torch.from_numpy(wl.start).to(device)
+        self.lens = torch.from_numpy(wl.lens).to(device)
+        self.idx = torch.from_numpy(wl.idx).to(device)
+        self.x = to_device(wl.x, wl.x_dtype, device)
+        self.a = [to_device(np.ascontiguousarray(a).reshape(a.shape[0], -1), wl.a_dtype,
+                            device).view(a.shape) for a in wl.lora_a]
+        self.outs0 = [to_device(o, wl.out_dtype, device) for o in wl.outs0]
+
+    def fresh_outs(self):
+        return [_device_clone(o) for o in self.outs0]
+
+    def run(self, outs=None, multi=True, idx=None):
+        """One multi-slice call, or one sgmv_shrink call per slice."""
+        import segmented_gather_gemm_amd as sg
+        wl = self.wl
+        outs = self.fresh_outs() if outs is None else outs
+        idx = self.idx if idx is None else idx
+        if multi:
+            sg.sgmv_shrink_multi_slice(self.x, list(zip(self.a, outs)), self.start, self.lens,
+                                       idx, wl.batches, wl.max_seq_len, wl.scale)
+        else:
+            for a, o in zip(self.a, outs):
+                sg.sgmv_shrink(self.x, a, o, self.start, self.lens, idx, wl.batches,
+                               wl.max_seq_len, wl.scale)
+        return outs
+
+
+# Unit roundoff of fp32, the accumulation type.
+U_FP32 = 2.0 ** -24
+
+
+def shrink_abs_dot(wl, si, rows, ra):
+    """sum_h |x[t][h] * A[a][k][h]| for the given rows (numpy, from the stored
+    values; float32 inputs cast to the weight dtype as the products see them)."""
+    from oracle_pins_util import np_cast_input, np_values
+    x = np_cast_input(np.ascontiguousarray(wl.x[rows]), wl.x_dtype, wl.a_dtype)
+    av = np.abs(np_values(wl.lora_a[si], wl.a_dtype))
+    out = np.zeros((len(rows), wl.K))
+    for a in np.unique(ra[rows]):
+        m = ra[rows] == a
+        out[m] = np.abs(x[m]) @ av[a].T
+    return out
+
+
+def assert_shrink_parity(wl, cand_bits, rows=None, idx=None, exact=False):
+    """GPU outputs (one bits array per slice) vs the oracle: every computed
+    value of an active row within tolerance of the exact value (non-finite
+    exactly where the rounded exact value is), every other row bit-identical
+    to the prior output.  ``rows`` samples the rows whose values are checked
+    (the untouched check always covers every row).  ``exact``: the bits must
+    equal the oracle's (integer data, where every fp32 partial sum is exact).
+
+    Tolerance: the output dtype's atol + rtol * |ref| (which covers the final
+    rounding and the scale's rounding), plus the bound on fp32 summation of
+    the H exact 16-bit products in any order, gamma_H * |scale| * sum_h
+    |x_h a_h| with gamma_H = H u / (1 - H u), u = 2^-24 (the recursive
+    summation bound, which holds for every order and tree of additions).
+    Returns the number of values checked."""
+    atol, rtol = TOLERANCE[wl.out_dtype]
+    gamma = wl.H * U_FP32 / (1.0 - wl.H * U_FP32)
+    idx = wl.idx if idx is None else idx
+    outs = [o.copy() for o in wl.outs0]
+    refs = oracle.shrink(wl.x, wl.x_dtype, wl.lora_a, wl.a_dtype, outs, wl.out_dtype, wl.start,
+                         wl.lens, idx, wl.scale, rows=rows, want_ref=True)
+    active = np.zeros(wl.T, dtype=bool)
+    for s, n, a in zip(wl.start, wl.lens, idx):
+        if 0 <= a < wl.L and n > 0:
+            active[s:s + n] = True
+    checked = np.zeros(wl.T, dtype=bool)
+    checked[np.arange(wl.T) if rows is None else np.asarray(rows)] = True
+    ra = np.full(wl.T, -1, dtype=np.int64)
+    for s, n, a in zip(wl.start, wl.lens, idx):
+        if 0 <= a < wl.L and n > 0:
+            ra[s:s + n] = a
+    from oracle_pins_util import np_values
+    n_checked = 0
+    for si, (cand, ref, rounded) in enumerate(zip(cand_bits, refs, outs)):
+        assert np.array_equal(cand[~active], wl.outs0[si][~active]), \
+            f"{wl.name} slice {si}: rows without an adapter changed"
+        m = active & checked
+        if exact:
+            assert np.array_equal(cand[m], rounded[m]), f"{wl.name} slice {si}: bits differ"
+            n_checked += int(m.sum()) * wl.K
+            continue
+        got = np_values(np.ascontiguousarray(cand[m]), wl.out_dtype)
+        exp = ref[m]
+        exp_rounded = np_values(np.ascontiguousarray(rounded[m]), wl.out_dtype)
+        finite = np.isfinite(exp_rounded)
+        assert np.array_equal(np.isfinite(got), finite), f"{wl.name} slice {si}: non-finite mismatch"
+        err = np.abs(got[finite] - exp[finite])
+        acc = gamma * abs(wl.scale) * shrink_abs_dot(wl, si, np.nonzero(m)[0], ra)
+        tol = atol + rtol * np.abs(exp[finite]) + acc[finite]
+        bad = np.nonzero(err > tol)[0]
+        assert bad.size == 0, (f"{wl.name} slice {si}: {bad.size} values out of tolerance, worst "
+                               f"err/tol {float(np.max(err / tol)):.3g}")
+        n_checked += int(m.sum()) * wl.K
+    return n_checked

@@ -167,3 +167,71 @@ def test_python_wrapper_rejects_host_tensors():
 def test_one_hip_runtime_in_process():
     """libsgmv resolves to the HIP runtime PyTorch already mapped."""
     assert len(sg._hip_runtimes_mapped()) == 1
+
+
+# --------------------------------------------------------------------------
+# LoRA-A projection (shrink).
+# --------------------------------------------------------------------------
+
+def shrink(x=None, a=None, out=None, meta=(FAKE, FAKE, FAKE), batches=2, max_len=6, scale=1.0):
+    x = x or Matrix(FAKE, F16, 10, 64, 64)
+    a = a or Stack(FAKE, F16, 2, 8, 64)
+    out = out or Matrix(FAKE, F16, 10, 8, 8)
+    st = sg.lib.sgmv_shrink(x, a, out, *meta, batches, max_len, scale, None)
+    return st, sg.lib.sgmv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(a=Stack(FAKE, F16, 2, 8, 32)), INVALID, "hidden"),
+    (dict(out=Matrix(FAKE, F16, 10, 16, 16)), INVALID, "output"),
+    (dict(out=Matrix(FAKE, F16, 9, 8, 8)), INVALID, "output"),
+    (dict(out=Matrix(FAKE, F16, 10, 8, 7)), INVALID, "output"),
+    (dict(x=Matrix(FAKE, F16, 10, 64, 63)), INVALID, "row stride"),
+    (dict(x=Matrix(FAKE, F16, 10, 0, 0), a=Stack(FAKE, F16, 2, 8, 0)), INVALID, "inputs shape"),
+    (dict(a=Stack(FAKE, F16, 2, 0, 64), out=Matrix(FAKE, F16, 10, 0, 0)), INVALID, "lora_a shape"),
+    (dict(batches=-1), INVALID, "batches"),
+    (dict(max_len=-1), INVALID, "max_seq_len"),
+    (dict(batches=1 << 20), UNSUPPORTED, "batches"),
+    (dict(x=Matrix(FAKE, 7, 10, 64, 64)), INVALID, "dtype"),
+    (dict(a=Stack(FAKE, F32, 2, 8, 64)), UNSUPPORTED, "float16 or bfloat16"),
+    (dict(x=Matrix(FAKE, BF16, 10, 64, 64)), UNSUPPORTED, "dtype"),
+    (dict(a=Stack(FAKE, F16, 2, 264, 64), out=Matrix(FAKE, F16, 10, 264, 264)), UNSUPPORTED,
+     "rank"),
+    (dict(x=Matrix(FAKE, F16, 1 << 31, 64, 64), out=Matrix(FAKE, F16, 1 << 31, 8, 8)),
+     UNSUPPORTED, "tokens"),
+    (dict(meta=(FAKE, 0, FAKE)), INVALID, "metadata"),
+    (dict(x=Matrix(0, F16, 10, 64, 64)), INVALID, "inputs data"),
+    (dict(out=Matrix(0, F16, 10, 8, 8)), INVALID, "null data"),
+])
+def test_shrink_invalid_arguments_rejected_before_launch(kw, status, frag):
+    st, msg = shrink(**kw)
+    assert st == status, msg
+    assert frag in msg
+
+
+def test_shrink_no_op_calls():
+    assert shrink(batches=0) == (OK, "")
+    assert shrink(x=Matrix(FAKE, F16, 0, 64, 64), out=Matrix(FAKE, F16, 0, 8, 8)) == (OK, "")
+    assert shrink(meta=(0, 0, 0), batches=0) == (OK, "")
+
+
+def test_shrink_multi_slice_checks():
+    def sl(rank=8, num=2, dt=F16, odt=F16):
+        return sg.ShrinkSliceDesc(Stack(FAKE, dt, num, rank, 64), Matrix(FAKE, odt, 10, rank, rank))
+
+    def multi_shrink(slices, n=None, batches=2):
+        arr = (sg.ShrinkSliceDesc * max(len(slices), 1))(*slices)
+        st = sg.lib.sgmv_shrink_multi_slice(Matrix(FAKE, F16, 10, 64, 64), arr,
+                                            len(slices) if n is None else n, FAKE, FAKE, FAKE,
+                                            batches, 6, 1.0, None)
+        return st, sg.lib.sgmv_last_error().decode()
+
+    assert multi_shrink([sl(), sl(rank=16)])[0] == INVALID
+    assert multi_shrink([sl(), sl(num=3)])[0] == INVALID
+    assert multi_shrink([sl(), sl(odt=F32)])[0] == INVALID
+    assert multi_shrink([sl()] * 9)[0] == INVALID
+    assert multi_shrink([sl()], n=0)[0] == INVALID
+    assert multi_shrink([sl(), sl()], batches=0) == (OK, "")
+    st = sg.lib.sgmv_shrink_multi_slice(Matrix(FAKE, F16, 10, 64, 64), None, 1, FAKE, FAKE, FAKE,
+                                        2, 6, 1.0, None)
+    assert st == INVALID
