@@ -288,6 +288,214 @@ def cpu_baseline(wl, model_bytes, budget_s):
             "single_core_sample": f"{one_note}, one call"}
 
 
+# ---------------------------------------------------------------------------
+# LoRA-A projection (shrink) workloads.
+# ---------------------------------------------------------------------------
+
+def shrink_byte_model(wl, rows=None):
+    """Algorithmic bytes of one shrink call: the input rows of active
+    segments, each distinct adapter's lora_A rows once per slice, and the
+    projected rows written.  `rows`: count only these (active) rows."""
+    import numpy as np
+    from sgmv_workloads import DTYPE_BYTES
+    ra = np.full(wl.T, -1, dtype=np.int64)
+    for s, n, a in zip(wl.start, wl.lens, wl.idx):
+        if a >= 0 and n > 0:
+            ra[s:s + n] = a
+    act = np.nonzero(ra >= 0)[0] if rows is None else np.asarray(rows)
+    t_act = len(act)
+    distinct = len(set(ra[act].tolist()))
+    ns = len(wl.lora_a)
+    total = t_act * wl.H * DTYPE_BYTES[wl.x_dtype]
+    total += ns * distinct * wl.K * wl.H * DTYPE_BYTES[wl.a_dtype]
+    total += ns * t_act * wl.K * DTYPE_BYTES[wl.out_dtype]
+    return total, t_act, distinct
+
+
+class ShrinkBufferSet:
+    def __init__(self, wl, device):
+        import numpy as np
+        from sgmv_workloads import to_torch
+        self.x = to_torch(wl.x, wl.x_dtype, device)
+        self.a = [to_torch(np.ascontiguousarray(a).reshape(a.shape[0], -1), wl.a_dtype,
+                           device).view(a.shape) for a in wl.lora_a]
+        self.outs = [to_torch(o, wl.out_dtype, device) for o in wl.outs0]
+
+    def clone(self):
+        c = object.__new__(ShrinkBufferSet)
+        c.x = self.x.clone()
+        c.a = [t.clone() for t in self.a]
+        c.outs = [t.clone() for t in self.outs]
+        return c
+
+
+def make_shrink_step(wl, meta, sets, split=False):
+    """One step: one sgmv_shrink_multi_slice call over every slice (with
+    `split`, one sgmv_shrink call per slice)."""
+    import segmented_gather_gemm_amd as sg
+    start, lens, idx = meta
+    B, M = wl.batches, wl.max_seq_len
+
+    if split:
+        def step(i):
+            bs = sets[i % len(sets)]
+            for a, o in zip(bs.a, bs.outs):
+                sg.sgmv_shrink(bs.x, a, o, start, lens, idx, B, M, wl.scale)
+    else:
+        def step(i):
+            bs = sets[i % len(sets)]
+            sg.sgmv_shrink_multi_slice(bs.x, list(zip(bs.a, bs.outs)), start, lens, idx, B, M,
+                                       wl.scale)
+    return step
+
+
+def shrink_cpu_baseline(wl, budget_s):
+    """Time the CPU oracle's shrink (as it stands) on a bounded sample of the
+    workload: the first active rows, as many as about `budget_s` seconds of
+    work on all host cores allow; then a smaller sample on one core."""
+    import numpy as np
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    ra = np.full(wl.T, -1, dtype=np.int64)
+    for s, n, a in zip(wl.start, wl.lens, wl.idx):
+        if a >= 0 and n > 0:
+            ra[s:s + n] = a
+    active = np.nonzero(ra >= 0)[0]
+    macs_per_row = wl.H * wl.K * len(wl.lora_a)
+
+    def sample_for(seconds, nthreads):
+        # estimate: ~2e8 fp64 multiply-adds per second per thread
+        keep = int(seconds * 2e8 * nthreads / macs_per_row)
+        keep = max(1, min(len(active), keep))
+        note = "all active rows" if keep == len(active) else f"first {keep} of {len(active)} active rows"
+        return active[:keep], note
+
+    def run(rows, nthreads, seconds, max_reps):
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < seconds and reps < max_reps):
+            outs = [o.copy() for o in wl.outs0]
+            t0 = time.perf_counter()
+            oracle.shrink(wl.x, wl.x_dtype, wl.lora_a, wl.a_dtype, outs, wl.out_dtype, wl.start,
+                          wl.lens, wl.idx, wl.scale, rows=rows, threads=nthreads)
+            spent += time.perf_counter() - t0
+            reps += 1
+        return spent / reps, reps
+
+    rows, note = sample_for(budget_s, threads)
+    secs, reps = run(rows, threads, budget_s, 1000)
+    sample_bytes, _, _ = shrink_byte_model(wl, rows)
+    rows1, note1 = sample_for(budget_s / 4, 1)
+    secs1, _ = run(rows1, 1, 0.0, 1)
+    one_bytes, _, _ = shrink_byte_model(wl, rows1)
+    return {"value": round(sample_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_call": round(secs, 4), "reps": reps,
+            "sample": f"{note} of {wl.name} seed {wl.seed}, fp64 C oracle, {reps} calls",
+            "single_core_gbs": round(one_bytes / secs1 / 1e9, 4),
+            "single_core_sample": f"{note1}, one call"}
+
+
+def run_shrink(args):
+    import math as _m
+    import torch
+    import sgmv_workloads as W
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    log(f"bench: generating {args.workload} seed {args.seed}")
+    wl = W.SHRINK_WORKLOADS[args.workload](args.seed)
+    model_bytes, t_act, distinct = shrink_byte_model(wl)
+    fp = wl.x.nbytes + sum(a.nbytes for a in wl.lora_a) + sum(o.nbytes for o in wl.outs0)
+    nsets = max(2, _m.ceil((1 << 30) / fp))
+    log(f"bench: {len(wl.lora_a)} slice(s), T={wl.T} (active {t_act}), hidden {wl.H} -> rank "
+        f"{wl.K}, {distinct} distinct adapters, {model_bytes / 1e6:.2f} MB per call, {nsets} "
+        f"rotated buffer sets of {fp / 1e6:.1f} MB")
+    meta = tuple(torch.from_numpy(a).to(device) for a in (wl.start, wl.lens, wl.idx))
+    first = ShrinkBufferSet(wl, device)
+    sets = [first] + [first.clone() for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+    split = args.split_slices and len(wl.lora_a) > 1
+    step = make_shrink_step(wl, meta, sets, split)
+
+    log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
+    ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
+    log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
+    ms_median = None
+    if args.eager:
+        ms, wall, mode = ms_eager, wall_eager, "eager"
+    else:
+        log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
+        ms, wall, ms_median = time_steps_graph(step, args.steps, args.warmup)
+        mode = "hip-graph replay"
+    log("bench: single launches after a cache flush")
+    ms_single = time_single_launches(step)
+    sec = ms * 1e-3
+    gbs = model_bytes / sec / 1e9
+    tokens_s = wl.T / sec
+    ksha = kernel_source_hash()
+    traffic_bytes = None if split else traffic_from_profiles(args.workload, ksha)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / sec / 1e9, 2)
+    log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
+        f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
+    ceiling = None if args.no_copy_ceiling else round(copy_ceiling(model_bytes // 2, device), 1)
+    del sets, first
+    torch.cuda.empty_cache()
+    cpu = None
+    if args.cpu_budget > 0:
+        log("bench: timing the CPU oracle baseline")
+        cpu = shrink_cpu_baseline(wl, args.cpu_budget)
+    result = {
+        "metric": "effective HBM GB/s (% of MI355X peak) and tokens/s for sgmv_shrink",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.a_dtype,
+        "data": "synthetic",
+        "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(tokens_s, 1),
+        "config": {
+            "workload": args.workload,
+            "seed": args.seed,
+            "hidden": wl.H,
+            "rank": wl.K,
+            "slices": len(wl.lora_a),
+            "batches": wl.batches,
+            "total_tokens": wl.T,
+            "active_tokens": t_act,
+            "distinct_adapters": distinct,
+            "scale": wl.scale,
+            "dtypes": {"inputs": wl.x_dtype, "lora_a": wl.a_dtype, "output": wl.out_dtype,
+                       "accumulate": "f32"},
+            "bytes_per_step": model_bytes,
+            "rotated_buffer_sets": nsets,
+            "call": (f"{len(wl.lora_a)} x sgmv_shrink" if split else
+                     "sgmv_shrink_multi_slice"),
+            "launch": mode,
+            "batch_median_us_per_step": None if ms_median is None else round(ms_median * 1e3, 3),
+            "eager_us_per_step": round(ms_eager * 1e3, 3),
+            "single_launch_after_flush_us": round(ms_single * 1e3, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "traffic_bytes_per_launch": traffic_bytes,
+            "kernel": "shrink_fast",
+            "kernel_source_sha256_16": ksha,
+        },
+        "copy_ceiling_gbs": ceiling,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,8 +509,8 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: HIP-graph replay, eager also reported)")
     ap.add_argument("--split-slices", action="store_true",
-                    help="multi-slice workloads: one sgmv_expand_slice call per slice per step "
-                         "instead of one fused sgmv_expand_multi_slice call")
+                    help="multi-slice workloads: one single-slice call per slice per step "
+                         "instead of one fused multi-slice call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -315,8 +523,11 @@ def main():
     import sgmv_workloads as W
     import segmented_gather_gemm_amd  # noqa: F401  (fails loudly if libsgmv.so is missing)
 
+    if args.workload in W.SHRINK_WORKLOADS:
+        return run_shrink(args)
     if args.workload not in W.WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; choose from {sorted(W.WORKLOADS)}")
+        sys.exit(f"unknown workload {args.workload}; choose from "
+                 f"{sorted(W.WORKLOADS) + sorted(W.SHRINK_WORKLOADS)}")
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     log(f"bench: generating {args.workload} seed {args.seed}")

@@ -20,8 +20,8 @@ LIBRARY = os.path.join(HERE, "libsgmv.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("sgmv_api.cpp", "sgmv_generic.hip", "sgmv_fast_ks0.hip", "sgmv_fast_ks1.hip",
             "sgmv_fast_ks2.hip", "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip",
-            "sgmv_shrink_generic.hip", "sgmv_shrink_kt1.hip", "sgmv_shrink_kt2.hip",
-            "sgmv_shrink_kt4.hip", "sgmv_shrink_kt8.hip", "sgmv_shrink_kt16.hip")]
+            "sgmv_shrink_generic.hip", "sgmv_shrink_k1.hip", "sgmv_shrink_k2.hip",
+            "sgmv_shrink_k4.hip", "sgmv_shrink_k8.hip", "sgmv_shrink_k16.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

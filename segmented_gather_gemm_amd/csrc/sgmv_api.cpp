@@ -310,15 +310,15 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
 // LoRA-A projection (shrink).
 // ---------------------------------------------------------------------------
 
-// Fast shrink kernel for `ktt` k tiles (a power of two, 1..16).
-const void* pick_shrink_kernel(int xd, int wd, int od, int ktt) {
+// Fast shrink kernel for k16 tiles of 16 rows per slice and ns slices.
+const void* pick_shrink_kernel(int xd, int wd, int od, int k16, int ns, bool split_t) {
   using namespace sgmv;
-  switch (ktt) {
-    case 1: return shrink_kernel_kt1(xd, wd, od);
-    case 2: return shrink_kernel_kt2(xd, wd, od);
-    case 4: return shrink_kernel_kt4(xd, wd, od);
-    case 8: return shrink_kernel_kt8(xd, wd, od);
-    default: return shrink_kernel_kt16(xd, wd, od);
+  switch (k16) {
+    case 1: return shrink_kernel_k1(xd, wd, od, ns, split_t);
+    case 2: return shrink_kernel_k2(xd, wd, od, ns, split_t);
+    case 4: return shrink_kernel_k4(xd, wd, od, ns, split_t);
+    case 8: return shrink_kernel_k8(xd, wd, od, ns, split_t);
+    default: return shrink_kernel_k16(xd, wd, od, ns, split_t);
   }
 }
 
@@ -328,17 +328,23 @@ int next_pow2(int v) {
   return p;
 }
 
+// Split-T (64-token units, lora_A shared through LDS) once the batch has at
+// least this many 64-token units; split-H (16-token units) below, where it
+// keeps more compute units busy.
+#ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS
+#define SGMV_SHRINK_SPLIT_T_MIN_UNITS 64
+#endif
+
 // One launch over slices [first, first + count) of `slices` (already checked).
 sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices, int first,
                           int count, const int64_t* start, const int64_t* lens,
                           const int64_t* idx, int64_t batches, float scale, bool fast,
-                          hipStream_t stream) {
+                          bool split_t, hipStream_t stream) {
   using namespace sgmv;
   const sgmv_shrink_slice& s0 = slices[first];
   const int64_t K = s0.lora_a.rows;
   const int64_t H = x.cols;
-  const int32_t k_tiles = (int32_t)((K + 15) / 16);
-  const int ktt = next_pow2(k_tiles * count);
+  const int k16 = next_pow2((int)((K + 15) / 16));
   ShrinkParams p{};
   p.x = x.data;
   p.start = start;
@@ -351,7 +357,6 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
   p.L = (int32_t)s0.lora_a.num;
   p.K = (int32_t)K;
   p.num_slices = count;
-  p.k_tiles = k_tiles;
   p.scale = scale;
   p.sort_slots = batches >= kSortMinBatches && batches <= kSortMaxBatches &&
                  s0.lora_a.num <= (1 << 22);
@@ -361,25 +366,35 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
     p.s[i].out = s.out.data;
     p.s[i].out_row_bytes = s.out.row_stride * elem_bytes(s.out.dtype);
   }
-  const void* kernel = fast ? pick_shrink_kernel(x.dtype, s0.lora_a.dtype, s0.out.dtype, ktt)
-                            : shrink_generic_kernel(x.dtype, s0.lora_a.dtype, s0.out.dtype);
+  const void* kernel =
+      fast ? pick_shrink_kernel(x.dtype, s0.lora_a.dtype, s0.out.dtype, k16, count, split_t)
+           : shrink_generic_kernel(x.dtype, s0.lora_a.dtype, s0.out.dtype);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no shrink kernel for this dtype combination");
-  if (fast) {
-    // Each wave takes a quarter of the 32-wide hidden steps, rounded up to
-    // whole pairs of pipeline blocks.
-    const int64_t steps = (H + 31) / 32;
+  const int64_t steps = (H + 31) / 32;  // 32-wide hidden steps
+  if (fast && split_t) {
+    // every wave runs all steps; loop positions in whole turns of the ring
+    // of blocks
+    const int64_t turn = shrink_ring(shrink_block_loads_t(x.dtype, k16, count)) *
+                         shrink_block_steps_t(k16 * count);
+    p.steps = (int32_t)((steps + turn - 1) / turn * turn);
+  } else if (fast) {
+    // each wave takes a quarter of the steps; loop positions in whole turns
+    // of the ring
     const int64_t per_wave = (steps + kWaves - 1) / kWaves;
-    const int64_t pair = 2 * shrink_block_steps(x.dtype, ktt, 1);
-    p.wave_steps = (int32_t)((per_wave + pair - 1) / pair * pair);
+    const int64_t turn = shrink_ring(shrink_block_loads_h(x.dtype, k16 * count)) *
+                         shrink_block_steps_h(x.dtype, k16 * count);
+    p.steps = (int32_t)((per_wave + turn - 1) / turn * turn);
   }
   const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);
   int capacity = 0;
   hipError_t e = device_capacity(kernel, lds, &capacity);
   if (e != hipSuccess)
     return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
-  // Units are 16-row tiles of active segments: at most ceil(T / 16) +
-  // min(batches, T) of them.  One per workgroup while they fit on the chip.
-  const int64_t units = (x.rows + kTileRows - 1) / kTileRows + (batches < x.rows ? batches : x.rows);
+  // Units are tiles of active segments: at most ceil(T / rows) + min(batches,
+  // T) of them.  One per workgroup while they fit on the chip.
+  const int64_t tile_rows = fast && split_t ? kShrinkTokensSplitT : kTileRows;
+  const int64_t units =
+      (x.rows + tile_rows - 1) / tile_rows + (batches < x.rows ? batches : x.rows);
   int64_t grid = units < capacity ? units : capacity;
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
@@ -453,26 +468,39 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
     if (!slices[i].out.data || (!slices[i].lora_a.data && L > 0))
       return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: null data pointer", i);
 
-  // Fast kernels: 16-byte blocks everywhere, hidden < 2^26 and 16 rows of
-  // inputs or outputs spanning less than 2 GiB (32-bit buffer offsets).
+  // Fast kernels: 16-byte blocks everywhere, hidden < 2^26 and a unit's rows
+  // (64) of inputs or outputs spanning less than 2 GiB (32-bit buffer
+  // offsets).  Decided for the inputs, then per slice; slices are launched
+  // in runs that take the same kernel family (so a slice's result does not
+  // depend on the others in the call).
   const int64_t xb = elem_bytes(x.dtype), ob = elem_bytes(s0.out.dtype);
-  bool fast = K % 8 == 0 && x.cols % 8 == 0 && x.cols < (int64_t(1) << 26) &&
-              aligned16(x.data) && (x.row_stride * xb) % 16 == 0 &&
-              16 * x.row_stride * xb < (int64_t(1) << 31);
-  for (int i = 0; i < num_slices && fast; ++i) {
+  const int64_t span = kShrinkTokensSplitT;
+  const bool fast_x = K % 8 == 0 && x.cols % 8 == 0 && x.cols < (int64_t(1) << 26) &&
+                      aligned16(x.data) && (x.row_stride * xb) % 16 == 0 &&
+                      span * x.row_stride * xb < (int64_t(1) << 31);
+  auto fast_slice = [&](int i) {
     const sgmv_shrink_slice& s = slices[i];
-    if (!aligned16(s.lora_a.data) || !aligned16(s.out.data) || (s.out.row_stride * ob) % 16 != 0 ||
-        16 * s.out.row_stride * ob >= (int64_t(1) << 31))
-      fast = false;
-  }
-  // The fast kernels hold up to 16 k tiles of 16 rows: slices that need more
-  // go in several launches (each reads the inputs again).
-  const int per_launch = fast ? (int)(16 / ((K + 15) / 16)) : num_slices;
-  for (int first = 0; first < num_slices; first += per_launch) {
-    const int count = num_slices - first < per_launch ? num_slices - first : per_launch;
-    const sgmv_status st =
-        shrink_launch(x, slices, first, count, start, lens, idx, batches, scale, fast, stream);
+    return fast_x && aligned16(s.lora_a.data) && aligned16(s.out.data) &&
+           (s.out.row_stride * ob) % 16 == 0 && span * s.out.row_stride * ob < (int64_t(1) << 31);
+  };
+  // The fast kernels take up to kShrinkMaxSlicesPerLaunch slices and 16 k
+  // tiles of 16 rows per launch: more slices go in several launches (each
+  // reads the inputs again).
+  const int k16 = next_pow2((int)((K + 15) / 16));
+  int fast_per_launch = 16 / k16;
+  if (fast_per_launch > kShrinkMaxSlicesPerLaunch) fast_per_launch = kShrinkMaxSlicesPerLaunch;
+  const bool split_t =
+      (x.rows + kShrinkTokensSplitT - 1) / kShrinkTokensSplitT >= SGMV_SHRINK_SPLIT_T_MIN_UNITS;
+  for (int first = 0; first < num_slices;) {
+    const bool fast = fast_slice(first);
+    const int limit = fast ? fast_per_launch : num_slices;
+    int count = 1;
+    while (first + count < num_slices && count < limit && fast_slice(first + count) == fast)
+      ++count;
+    const sgmv_status st = shrink_launch(x, slices, first, count, start, lens, idx, batches,
+                                         scale, fast, split_t, stream);
     if (st != SGMV_OK) return st;
+    first += count;
   }
   g_error.clear();
   return SGMV_OK;

@@ -274,13 +274,16 @@ __device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
 }
 
 
-// Fill the table (every thread of the workgroup takes part) with row tiles
-// of `tile_rows` rows; returns the total number of row tiles (wave-uniform).
-// P: the kernel's argument block (segment metadata fields as in Params).
-template <typename P>
+// Fill the table (all NT threads of the workgroup take part; wave_total
+// holds NT / 64 words) with row tiles of `tile_rows` rows; returns the total
+// number of row tiles (wave-uniform).  P: the kernel's argument block
+// (segment metadata fields as in Params).
+template <int NT = kThreads, typename P>
 __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& tab,
                                                     int32_t* wave_total,
                                                     int32_t tile_rows = kTileRows) {
+  constexpr int kThreads = NT;         // shadows the default block size below
+  constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -309,7 +312,7 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
     // tile_start[0 .. B), padded to a multiple of 4 with 0xffffffff, which
     // is never below a key.  The padding spills into seg_row's first words,
     // which are written only after the ranks are taken.
-    constexpr int kPer = kSortMaxBatches / kThreads;
+    constexpr int kPer = (kSortMaxBatches + kThreads - 1) / kThreads;
     int32_t row[kPer], end[kPer], a32[kPer], tiles[kPer];
     uint32_t key[kPer];
     uint32_t* keys = reinterpret_cast<uint32_t*>(tab.tile_start);

@@ -30,23 +30,17 @@
 // with 4 consecutive k of one token per k tile.  Loads go through buffer
 // resources bounded by the tile's valid rows and the slice's K rows, so rows
 // past the segment and k past K read zero and store nothing; hidden blocks
-// past H take an offset outside every resource.  The step loop is double
-// buffered in blocks of shrink_block_steps() steps, every block issuing the
-// same load instructions (blocks past the wave's quarter read nothing), so
-// the compiler waits for one block with a nonzero vmcnt.
+// past H take an offset outside every resource.  The step loop runs over a
+// ring of blocks in registers, issuing each block several blocks ahead of
+// its use; every block issues the same load instructions (blocks past the
+// end read nothing), so the compiler waits for one block with a nonzero
+// vmcnt.
 #pragma once
 
 #include "sgmv_device.h"
 
 namespace sgmv {
 namespace dev {
-
-// This workgroup's contiguous range of the U units, the grid's XCD-aware
-// remap as in the expand (each XCD owns one contiguous eighth).
-__device__ __forceinline__ void shrink_units(const ShrinkParams& p, uint32_t U, uint32_t* begin,
-                                             uint32_t* end) {
-  unit_range(p, U, begin, end);
-}
 
 // Four consecutive outputs at byte offset `off` of resource r.
 template <int OD>
@@ -63,144 +57,357 @@ __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, f32x4 v) {
   }
 }
 
-template <int XD, int KTT, int RT>
-struct ShrinkBlock {
-  static constexpr int kSteps = shrink_block_steps(XD, KTT, RT);
-  u32x4 x[kSteps][RT][raw_vecs<XD>()];
-  u32x4 a[kSteps][KTT];
+// Compile-time shape: K16 16-row k tiles per slice, NS slices; k tile i of
+// the launch is tile i % K16 of slice i / K16.
+template <int XD, int K16, int NS>
+struct ShrinkShape {
+  static constexpr int kTiles = K16 * NS;
+  static constexpr int kNV = raw_vecs<XD>();
+  static constexpr int kBlockH = shrink_block_steps_h(XD, kTiles);
+  static constexpr int kBlockT = shrink_block_steps_t(kTiles);
+  // split-T: lora_A loads of one slice's block that each wave issues (one
+  // load = 8 rows x 128 bytes, i.e. half a k tile over two steps)
+  static constexpr int kPairs = K16 * kBlockT / kWaves;
+  // blocks in flight
+  static constexpr int kRingH = shrink_ring(shrink_block_loads_h(XD, kTiles));
+  static constexpr int kRingT = shrink_ring(shrink_block_loads_t(XD, K16, NS));
+  static_assert(kTiles <= 16 && NS <= kShrinkMaxSlicesPerLaunch, "shape");
+  static_assert(K16 * kBlockT % kWaves == 0, "split-T loads divide among the waves");
+  static_assert(kBlockT % 2 == 0, "split-T lora_A loads cover two steps");
 };
 
-// KTT: 16-row k tiles over all slices (a power of two >= the slices' total;
-// tiles past it are dead: they read zero and store nothing).  RT: 16-row
-// token tiles per unit.
-template <int XD, int WD, int OD, int KTT, int RT>
-__global__ __launch_bounds__(kThreads) void shrink_fast(const ShrinkParams p) {
-  using Block = ShrinkBlock<XD, KTT, RT>;
-  constexpr int kB = Block::kSteps;
-  constexpr int kFrags = RT * KTT;
-  constexpr int kRound = kFrags < 8 ? kFrags : 8;  // fragments added per LDS round
-  constexpr int xb = XD == F32 ? 4 : 2;
+// One unit as the kernels see it: first row, valid rows, adapter, and the
+// resources over the unit's input rows and each slice's lora_A[a].
+template <int NS>
+struct ShrinkUnit {
+  int32_t row0, rows;
+  rsrc_t x;
+  rsrc_t a[NS];
+};
+
+template <int NS>
+__device__ __forceinline__ ShrinkUnit<NS> shrink_unit(const ShrinkParams& p, const SegTable& tab,
+                                                      int b, uint32_t u, int32_t tile_rows) {
+  ShrinkUnit<NS> su;
+  su.row0 = uniform(tab.seg_row[b]) + ((int32_t)u - uniform(tab.tile_start[b])) * tile_rows;
+  const int32_t left = uniform(tab.seg_end[b]) - su.row0;
+  su.rows = left < tile_rows ? left : tile_rows;
+  const int64_t a = uniform(tab.seg_lora[b]);
+  su.x = make_rsrc(static_cast<const char*>(p.x) + (int64_t)su.row0 * p.x_row_bytes,
+                   (int64_t)su.rows * p.x_row_bytes);
+  const int64_t a_bytes = (int64_t)p.K * p.H * 2;  // one adapter's (K, H) block
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    su.a[s] = make_rsrc(static_cast<const char*>(p.s[s].a) + a * a_bytes, a_bytes);
+  return su;
+}
+
+// Store a wave's 16 x 16 fragment i (k tile i % K16 of slice i / K16) of the
+// token tile starting `trow` rows into the unit: lane (j, g) holds k = 16 kt +
+// 4 g .. + 3 of token trow + j.
+template <int OD, int K16>
+__device__ __forceinline__ void shrink_store(const ShrinkParams& p, int i, int32_t row0,
+                                             int32_t rows, int trow, int j, int g, f32x4 v) {
   constexpr int ob = OD == F32 ? 4 : 2;
+  const int si = i / K16, kt = i % K16;
+  const ShrinkSliceDesc& S = p.s[si];
+  const rsrc_t orc = make_rsrc(static_cast<char*>(S.out) + (int64_t)row0 * S.out_row_bytes,
+                               (int64_t)rows * S.out_row_bytes);
+  const int32_t k = 16 * kt + 4 * g;
+  const uint32_t off =
+      k < p.K ? (uint32_t)(trow + j) * (uint32_t)S.out_row_bytes + (uint32_t)(k * ob) : kOut;
+  store4<OD>(orc, off, v * p.scale);
+}
+
+// ---------------------------------------------------------------------------
+// Split-H: 16 tokens per unit; the four waves of the workgroup split the
+// hidden steps and add their partial sums through LDS.
+// ---------------------------------------------------------------------------
+
+template <int XD, int K16, int NS>
+struct SplitHBlock {
+  using Sh = ShrinkShape<XD, K16, NS>;
+  u32x4 x[Sh::kBlockH][Sh::kNV];
+  u32x4 a[Sh::kBlockH][Sh::kTiles];
+};
+
+template <int XD, int WD, int OD, int K16, int NS>
+__global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p) {
+  using Sh = ShrinkShape<XD, K16, NS>;
+  using Block = SplitHBlock<XD, K16, NS>;
+  constexpr int kW = kWaves;
+  constexpr int kT = Sh::kTiles;
+  constexpr int kB = Sh::kBlockH;
+  // fragments added per LDS round: kW x kRound fragments of 1 KiB <= 32 KiB
+  constexpr int kRound = kT < 32 / kW ? kT : 32 / kW;
+  constexpr int xb = XD == F32 ? 4 : 2;
   prefetch_params(p);
   extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
-  __shared__ int32_t wave_total[kWaves];
-  __shared__ f32x4 red[kWaves][kRound][64];
+  __shared__ int32_t wave_total[kW];
+  __shared__ f32x4 red[kW][kRound][64];
   const SegTable tab = seg_table(lds, p.batches);
-  const int32_t U = build_tile_table(p, tab, wave_total, kTileRows * RT);
+  const int32_t U = build_tile_table(p, tab, wave_total, kTileRows);
   if (U == 0) return;
   uint32_t u, u_end;
-  shrink_units(p, (uint32_t)U, &u, &u_end);
+  unit_range(p, (uint32_t)U, &u, &u_end);
   if (u >= u_end) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4;  // lane group: hidden block 8 g of a step / k rows 4 g.. of a tile
-  const int j = lane & 15;  // token of a tile / lora_A row of a k tile
+  const int j = lane & 15;  // token of the tile / lora_A row of a k tile
   const int32_t H = p.H;
-  const int32_t K = p.K;
-  const int32_t kt_n = p.k_tiles;
-  const uint32_t xrb = (uint32_t)p.x_row_bytes;  // 16 RT rows span < 2 GiB (host)
-  const int32_t s_beg = wave * p.wave_steps;
-  const int32_t s_end = s_beg + p.wave_steps;
-  // lane parts of the load offsets: row j, hidden block 8 g
+  const uint32_t xrb = (uint32_t)p.x_row_bytes;  // 16 rows span < 2 GiB (host)
+  // The wave's hidden steps: [wave q, wave q + q) with q = ceil(steps / kW),
+  // run over p.steps >= q loop positions (the rest read nothing).
+  const int32_t q_steps = (((H + 31) >> 5) + kW - 1) / kW;
+  const int32_t s_beg = wave * q_steps;
   const uint32_t x_lane = (uint32_t)j * xrb + (uint32_t)(8 * g * xb);
-  const uint32_t a_lane = (uint32_t)j * (uint32_t)H * 2u + (uint32_t)(16 * g);
+  uint32_t a_lane[K16];  // row 16 kt + j of a slice's lora_A[a], hidden block 8 g
+#pragma unroll
+  for (int kt = 0; kt < K16; ++kt)
+    a_lane[kt] = (uint32_t)(16 * kt + j) * (uint32_t)H * 2u + (uint32_t)(16 * g);
 
   int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
   for (; u < u_end; ++u) {
     while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
-    const int32_t row0 =
-        uniform(tab.seg_row[b]) + ((int32_t)u - uniform(tab.tile_start[b])) * (kTileRows * RT);
-    const int32_t left = uniform(tab.seg_end[b]) - row0;
-    const int32_t rows = left < kTileRows * RT ? left : kTileRows * RT;
-    const int64_t a = uniform(tab.seg_lora[b]);
-    const rsrc_t xr = make_rsrc(static_cast<const char*>(p.x) + (int64_t)row0 * p.x_row_bytes,
-                                (int64_t)rows * p.x_row_bytes);
-    // k tile i: slice i / kt_n, rows 16 (i % kt_n) .. of A_s[a]
-    auto a_rsrc = [&](int i) __attribute__((always_inline)) -> rsrc_t {
-      const int si = i / kt_n;
-      const int kt = i - si * kt_n;
-      if (si >= p.num_slices) return make_rsrc(p.x, 0);
-      const int32_t kr = K - 16 * kt < 16 ? K - 16 * kt : 16;
-      return make_rsrc(static_cast<const char*>(p.s[si].a) + (a * K + 16 * kt) * H * 2,
-                       (int64_t)kr * H * 2);
-    };
+    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kTileRows);
 
-    auto load_block = [&](Block& blk, int32_t s0) __attribute__((always_inline)) {
+    auto load_block = [&](Block& blk, int32_t v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int st = 0; st < kB; ++st) {
-        const int32_t step = s0 + st;
-        const bool ok = step < s_end && 32 * step + 8 * g < H;
+        const int32_t v = v0 + st;
+        const int32_t step = s_beg + v;
+        const bool ok = v < q_steps && 32 * step + 8 * g < H;
+        buf_load8<XD>(su.x, ok ? x_lane + (uint32_t)(32 * step * xb) : kOut, blk.x[st]);
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
-          buf_load8<XD>(xr, ok ? x_lane + (uint32_t)r * 16u * xrb + (uint32_t)(32 * step * xb)
-                               : kOut,
-                        blk.x[st][r]);
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int i = 0; i < KTT; ++i)
-          buf_load8<WD>(a_rsrc(i), ok ? a_lane + (uint32_t)(64 * step) : kOut, &blk.a[st][i]);
+          for (int kt = 0; kt < K16; ++kt)
+            buf_load8<WD>(su.a[s], ok ? a_lane[kt] + (uint32_t)(64 * step) : kOut,
+                          &blk.a[st][s * K16 + kt]);
+      }
+    };
+    f32x4 acc[kT];
+#pragma unroll
+    for (int i = 0; i < kT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute_block = [&](const Block& blk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int st = 0; st < kB; ++st) {
+        const u32x4 xo = x_operand<XD, WD>(blk.x[st]);
+#pragma unroll
+        for (int i = 0; i < kT; ++i) acc[i] = mfma<WD>(blk.a[st][i], xo, acc[i]);
       }
     };
 
-    f32x4 acc[RT][KTT];
+    // Loop positions [0, p.steps) (a multiple of kD kB): a ring of kD blocks
+    // in registers, block n + kD - 1 issued before block n computes.
+    // Scheduling barriers keep each block's loads in issue order, which the
+    // in-order vmcnt wait relies on.
+    constexpr int kD = Sh::kRingH;
+    Block ring[kD];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int d = 0; d + 1 < kD; ++d) {
+      load_block(ring[d], d * kB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int32_t s = 0; s < p.steps; s += kD * kB) {
 #pragma unroll
-      for (int i = 0; i < KTT; ++i) acc[r][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute_block = [&](const Block& blk) __attribute__((always_inline)) {
-#pragma unroll
-      for (int st = 0; st < kB; ++st)
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const u32x4 xo = x_operand<XD, WD>(blk.x[st][r]);
-#pragma unroll
-          for (int i = 0; i < KTT; ++i) acc[r][i] = mfma<WD>(blk.a[st][i], xo, acc[r][i]);
-        }
-    };
-
-    // The wave's steps [s_beg, s_end) (a multiple of 2 kB), two blocks per
-    // iteration; the last iteration's third load lies past s_end.
-    Block b0, b1;
-    load_block(b0, s_beg);
-    for (int32_t s = s_beg; s < s_end; s += 2 * kB) {
-      load_block(b1, s + kB);
-      compute_block(b0);
-      load_block(b0, s + 2 * kB);
-      compute_block(b1);
+      for (int d = 0; d < kD; ++d) {
+        load_block(ring[(d + kD - 1) % kD], s + (d + kD - 1) * kB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_block(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
-    // Add the four waves' partial sums through LDS, kRound fragments at a
-    // time; wave w finishes fragments w, w + 4, ...  The first barrier of a
-    // round also orders the previous round's (or unit's) reads before the
-    // writes.
+    // Add the waves' partial sums through LDS, kRound fragments at a time;
+    // wave w finishes fragments w, w + kW, ... of the round.  The first
+    // barrier of a round also orders the previous round's (or unit's) reads
+    // before the writes.
 #pragma unroll
-    for (int f0 = 0; f0 < kFrags; f0 += kRound) {
+    for (int f0 = 0; f0 < kT; f0 += kRound) {
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < kRound; ++q)
-        if (f0 + q < kFrags) red[wave][q][lane] = acc[(f0 + q) / KTT][(f0 + q) % KTT];
+        if (f0 + q < kT) red[wave][q][lane] = acc[f0 + q];
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < kRound; ++q) {
-        const int f = f0 + q;
-        if (f >= kFrags || (q & (kWaves - 1)) != wave) continue;
-        const int r = f / KTT, i = f % KTT;
-        const int si = i / kt_n;
-        if (si >= p.num_slices) continue;
-        const int kt = i - si * kt_n;
+        if (f0 + q >= kT || q % kW != wave) continue;
         f32x4 v = red[0][q][lane];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += red[w][q][lane];
-        v *= p.scale;
-        const ShrinkSliceDesc& S = p.s[si];
-        const rsrc_t orc = make_rsrc(static_cast<char*>(S.out) + (int64_t)row0 * S.out_row_bytes,
-                                     (int64_t)rows * S.out_row_bytes);
-        const int32_t k = 16 * kt + 4 * g;
-        const uint32_t off =
-            k < K ? (uint32_t)(16 * r + j) * (uint32_t)S.out_row_bytes + (uint32_t)(k * ob) : kOut;
-        store4<OD>(orc, off, v);
+        for (int w = 1; w < kW; ++w) v += red[w][q][lane];
+        shrink_store<OD, K16>(p, f0 + q, su.row0, su.rows, 0, j, g, v);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-T: 64 tokens per unit; wave t owns tokens 16 t .. 16 t + 15 and runs
+// all hidden steps, with the lora_A blocks shared through LDS.
+// ---------------------------------------------------------------------------
+
+template <int XD, int K16, int NS>
+struct SplitTBlock {
+  using Sh = ShrinkShape<XD, K16, NS>;
+  u32x4 x[Sh::kBlockT][Sh::kNV];     // this wave's input rows
+  u32x4 a[NS][Sh::kPairs];           // this wave's share of the block's lora_A tiles
+};
+
+// LDS layout of a split-T operand fragment (16 rows x 32 hidden, 1 KiB in
+// MFMA operand order, lora_A or input): lane (j, g)'s 16 bytes sit in slot
+// 16 g + (j ^ 4 g) of the fragment, and fragments are kFragSlots = 66 slots
+// apart.  The loads that fill it read 8 rows x 64 contiguous elements each
+// (lane l: row l / 8, elements 8 (l % 8) .. of the row's two-step span), so
+// the 16 lanes the LDS serves together write 16 different bank groups, and
+// the MFMA reads (16 lanes of one g) do as well.
+constexpr int kFragSlots = 66;
+__device__ __forceinline__ int frag_slot(int j, int g) { return 16 * g + (j ^ (4 * g)); }
+
+template <int XD, int WD, int OD, int K16, int NS>
+__global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p) {
+  using Sh = ShrinkShape<XD, K16, NS>;
+  using Block = SplitTBlock<XD, K16, NS>;
+  constexpr int kT = Sh::kTiles;
+  constexpr int kB = Sh::kBlockT;
+  constexpr int kP = Sh::kPairs;
+  constexpr int xb = XD == F32 ? 4 : 2;
+  constexpr int kBuf = kT * kB;  // fragments of one block
+  prefetch_params(p);
+  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
+  __shared__ int32_t wave_total[kWaves];
+  // lora_A fragments of a block per buffer: [buffer][tile i * kB + step]
+  // [slot] (see frag_slot)
+  __shared__ u32x4 a_lds[2][kBuf][kFragSlots];
+  // each wave's input fragments of the block being computed (private to
+  // the wave, so one buffer)
+  __shared__ u32x4 x_lds[kWaves][kB][kFragSlots];
+  const SegTable tab = seg_table(lds, p.batches);
+  const int32_t U = build_tile_table(p, tab, wave_total, kShrinkTokensSplitT);
+  if (U == 0) return;
+  uint32_t u, u_end;
+  unit_range(p, (uint32_t)U, &u, &u_end);
+  if (u >= u_end) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int tw = wave;  // token tile
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int32_t H = p.H;
+  const int32_t n_steps = p.steps;  // loop positions per unit, a multiple of kD kB
+  const int32_t h_steps = (H + 31) >> 5;  // hidden steps
+  const uint32_t xrb = (uint32_t)p.x_row_bytes;  // 64 rows span < 2 GiB (host)
+  // Input loads of a block, xq < kB: rows 16 tw + 8 (xq & 1) .. + 7 over steps
+  // 2 (xq >> 1), + 1; lane l reads row + l / 8, elements 8 (l % 8) .. of the
+  // span (hidden block l % 4 of step 2 (xq >> 1) + (l % 8) / 4).
+  const int lr = lane >> 3, lb = lane & 7;
+  uint32_t x_lane[2];  // by xq & 1: row offset + the lane's element offset in the span
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+    x_lane[h2] = (uint32_t)(16 * tw + 8 * h2 + lr) * xrb + (uint32_t)(8 * lb * xb);
+  const int x_slot[2] = {frag_slot(lr, lb & 3), frag_slot(8 + lr, lb & 3)};
+  // This wave's lora_A loads of every slice's block: load pr = 4 q + tw
+  // covers rows 16 kt + 8 half .. + 7 over steps 2 sp, 2 sp + 1 of the block
+  // (kt = pr / kB, half and sp from pr % kB); lane l reads row + l / 8,
+  // bytes 16 (l % 8) of the 128-byte span, which is hidden block l % 4 of
+  // step 2 sp + (l % 8) / 4.
+  uint32_t a_lane[kP];  // row offset + byte offset within the span
+  int a_step[kP];       // step of this lane's 16 bytes within the block
+  int a_frag[kP];       // fragment within a slice's part of the block, and slot
+  int a_slot[kP];
+#pragma unroll
+  for (int q = 0; q < kP; ++q) {
+    const int pr = kWaves * q + tw;
+    const int kt = pr / kB, r = pr % kB;
+    const int half = r & 1, sp = r >> 1;
+    const int row = 16 * kt + 8 * half + lr;
+    a_lane[q] = (uint32_t)row * (uint32_t)H * 2u + (uint32_t)(16 * lb);
+    a_step[q] = 2 * sp + (lb >> 2);
+    a_frag[q] = kt * kB + a_step[q];
+    a_slot[q] = frag_slot(8 * half + lr, lb & 3);
+  }
+  const int r_slot = frag_slot(j, g);  // this lane's slot when reading a fragment
+
+  int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
+  for (; u < u_end; ++u) {
+    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
+    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kShrinkTokensSplitT);
+
+    auto load_block = [&](Block& blk, int32_t v0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int xq = 0; xq < kB; ++xq) {
+        // the lane's 8 elements: step 2 (xq >> 1) + lb / 4 of the block
+        const int32_t step = v0 + 2 * (xq >> 1) + (lb >> 2);
+        const bool ok = step < h_steps && 32 * step + 8 * (lb & 3) < H;
+        const uint32_t span = (uint32_t)(32 * (step - (lb >> 2)) * xb);
+        buf_load8<XD>(su.x, ok ? x_lane[xq & 1] + span : kOut, blk.x[xq]);
+      }
+#pragma unroll
+      for (int q = 0; q < kP; ++q) {
+        // the 128-byte span starts at the block's step 2 sp (even)
+        const int32_t step = v0 + a_step[q];
+        const bool ok = step < h_steps && 32 * step + 8 * (lb & 3) < H;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          buf_load8<WD>(su.a[s], ok ? a_lane[q] + (uint32_t)(64 * (step - (lb >> 2))) : kOut,
+                        &blk.a[s][q]);
+      }
+    };
+    auto publish = [&](const Block& blk, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int q = 0; q < kP; ++q)
+          a_lds[buf][s * K16 * kB + a_frag[q]][a_slot[q]] = blk.a[s][q];
+      // float32 inputs are rounded to the weight dtype here
+#pragma unroll
+      for (int xq = 0; xq < kB; ++xq)
+        x_lds[wave][2 * (xq >> 1) + (lb >> 2)][x_slot[xq & 1]] = x_operand<XD, WD>(blk.x[xq]);
+      __syncthreads();
+    };
+    f32x4 acc[kT];
+#pragma unroll
+    for (int i = 0; i < kT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute_block = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int st = 0; st < kB; ++st) {
+        const u32x4 xo = x_lds[wave][st][r_slot];
+#pragma unroll
+        for (int i = 0; i < kT; ++i)
+          acc[i] = mfma<WD>(a_lds[buf][i * kB + st][r_slot], xo, acc[i]);
+      }
+    };
+
+    // A ring of kD blocks in registers: block n + kD - 1 is issued, then
+    // block n is published to LDS buffer n % 2 (kD is even) and computed.
+    // The barrier in publish also orders every wave's reads of a buffer
+    // (block n - 2) before it is written again.  Loads past the hidden
+    // steps read nothing.
+    constexpr int kD = Sh::kRingT;
+    static_assert(kD % 2 == 0, "LDS buffers alternate with the ring");
+    Block ring[kD];
+#pragma unroll
+    for (int d = 0; d + 1 < kD; ++d) {
+      load_block(ring[d], d * kB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int32_t s = 0; s < n_steps; s += kD * kB) {
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        load_block(ring[(d + kD - 1) % kD], s + (d + kD - 1) * kB);
+        __builtin_amdgcn_sched_barrier(0);
+        publish(ring[d], d & 1);
+        compute_block(d & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < kT; ++i)
+      shrink_store<OD, K16>(p, i, su.row0, su.rows, 16 * tw, j, g, acc[i]);
   }
 }
 
@@ -254,22 +461,42 @@ __global__ __launch_bounds__(kThreads) void shrink_generic(const ShrinkParams p)
 // Kernel tables.
 // ---------------------------------------------------------------------------
 
-template <int XD, int WD, int KTT>
-const void* shrink_by_out(int od) {
-  switch (od) {
-    case F16: return reinterpret_cast<const void*>(&shrink_fast<XD, WD, F16, KTT, 1>);
-    case BF16: return reinterpret_cast<const void*>(&shrink_fast<XD, WD, BF16, KTT, 1>);
-    case F32: return reinterpret_cast<const void*>(&shrink_fast<XD, WD, F32, KTT, 1>);
+template <int XD, int WD, int OD, int K16, int NS>
+const void* shrink_entry(bool split_t) {
+  if constexpr (K16 * NS > 16) {
+    return nullptr;
+  } else {
+    return split_t ? reinterpret_cast<const void*>(&shrink_split_t<XD, WD, OD, K16, NS>)
+                   : reinterpret_cast<const void*>(&shrink_split_h<XD, WD, OD, K16, NS>);
+  }
+}
+
+template <int XD, int WD, int OD, int K16>
+const void* shrink_by_ns(int ns, bool split_t) {
+  switch (ns) {
+    case 1: return shrink_entry<XD, WD, OD, K16, 1>(split_t);
+    case 2: return shrink_entry<XD, WD, OD, K16, 2>(split_t);
+    case 3: return shrink_entry<XD, WD, OD, K16, 3>(split_t);
     default: return nullptr;
   }
 }
 
-template <int KTT>
-const void* shrink_table(int xd, int wd, int od) {
-  if (wd == BF16 && xd == BF16) return shrink_by_out<BF16, BF16, KTT>(od);
-  if (wd == BF16 && xd == F32) return shrink_by_out<F32, BF16, KTT>(od);
-  if (wd == F16 && xd == F16) return shrink_by_out<F16, F16, KTT>(od);
-  if (wd == F16 && xd == F32) return shrink_by_out<F32, F16, KTT>(od);
+template <int XD, int WD, int K16>
+const void* shrink_by_out(int od, int ns, bool split_t) {
+  switch (od) {
+    case F16: return shrink_by_ns<XD, WD, F16, K16>(ns, split_t);
+    case BF16: return shrink_by_ns<XD, WD, BF16, K16>(ns, split_t);
+    case F32: return shrink_by_ns<XD, WD, F32, K16>(ns, split_t);
+    default: return nullptr;
+  }
+}
+
+template <int K16>
+const void* shrink_table(int xd, int wd, int od, int ns, bool split_t) {
+  if (wd == BF16 && xd == BF16) return shrink_by_out<BF16, BF16, K16>(od, ns, split_t);
+  if (wd == BF16 && xd == F32) return shrink_by_out<F32, BF16, K16>(od, ns, split_t);
+  if (wd == F16 && xd == F16) return shrink_by_out<F16, F16, K16>(od, ns, split_t);
+  if (wd == F16 && xd == F32) return shrink_by_out<F32, F16, K16>(od, ns, split_t);
   return nullptr;
 }
 

@@ -55,3 +55,25 @@ def test_cpu_baseline_reports_multi_and_single_core_rates():
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s"
     assert cpu["value"] > 0 and cpu["single_core_gbs"] > 0 and cpu["reps"] >= 1
     assert cpu["cores"] >= 1 and "tiny_ref" in cpu["sample"]
+
+
+def test_shrink_byte_model_hand_count():
+    # segments: 5 rows adapter 1, 7 rows index -1, 2 rows adapter 0; hidden 64
+    # bf16 -> rank 16, two slices, float32 output: 7 active rows, 2 adapters.
+    wl = W.shrink_custom([5, 7, 2], [1, -1, 0], H=64, K=16, L=2, slices=2, out_dtype="f32")
+    total, t_act, distinct = bench.shrink_byte_model(wl)
+    assert (t_act, distinct) == (7, 2)
+    assert total == 7 * 64 * 2 + 2 * 2 * 16 * 64 * 2 + 2 * 7 * 16 * 4
+
+
+def test_shrink_named_workload_byte_counts():
+    total, t_act, distinct = bench.shrink_byte_model(W.shrink_q_proj(0))
+    assert (t_act, distinct) == (1279, 3)
+    assert total == 1279 * 4096 * 2 + 3 * 16 * 4096 * 2 + 1279 * 16 * 2
+
+
+def test_shrink_cpu_baseline():
+    wl = W.shrink_tiny(0)
+    cpu = bench.shrink_cpu_baseline(wl, 0.05)
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["single_core_gbs"] > 0
+    assert "shrink_tiny" in cpu["sample"]

@@ -158,3 +158,68 @@ def test_shrink_named_workloads(name, sample):
         rows = np.sort(rng.choice(wl.T, size=sample, replace=False))
         rows = np.unique(np.concatenate([rows, [0, wl.T - 1]]))
     assert run_and_check(wl, rows=rows) > 0
+
+
+# Batches of at least 256 64-token units take the split-T kernels (64-token
+# units, lora_A shared through LDS); smaller ones the split-H kernels.
+SPLIT_T_LENS = [5000, 3, 7000, 17, 0, 4500, 1, 64, 65]
+SPLIT_T_IDX = [1, 0, 2, -1, 1, 0, 2, 1, -1]
+
+
+@pytest.mark.parametrize("H,K,slices,dts,scale", [
+    (256, 16, 1, ("bf16", "bf16", "bf16"), 1.0),
+    (1000, 24, 2, ("f16", "f16", "f32"), 0.5),     # partial hidden step, partial k tile
+    (64, 128, 1, ("f32", "bf16", "bf16"), 1.0),
+    (512, 32, 3, ("bf16", "bf16", "bf16"), 2.0),   # fused QKV shape
+    (96, 256, 1, ("f16", "f16", "f16"), 1.0),      # 16 k tiles
+    (40, 8, 3, ("f32", "f16", "f32"), 1.0),
+    (128, 64, 5, ("bf16", "bf16", "f32"), 1.0),    # 5 slices: launches of 2 and 3
+])
+def test_shrink_split_t_parity(H, K, slices, dts, scale):
+    x_dt, a_dt, o_dt = dts
+    wl = W.shrink_custom(SPLIT_T_LENS, SPLIT_T_IDX, H=H, K=K, L=3, slices=slices, x_dtype=x_dt,
+                         a_dtype=a_dt, out_dtype=o_dt, scale=scale, seed=H * K + slices)
+    assert -(-wl.T // 64) >= 256
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.choice(wl.T, size=3000, replace=False),
+                                     np.arange(0, 200), np.arange(wl.T - 200, wl.T)]))
+    assert run_and_check(wl, rows=rows) > 0
+
+
+@pytest.mark.parametrize("H,K,slices,dts", [
+    (256, 16, 1, ("bf16", "bf16", "f32")),
+    (1000, 24, 3, ("f16", "f16", "bf16")),
+    (72, 128, 2, ("f32", "bf16", "f32")),
+])
+def test_shrink_split_t_integer_data_bit_exact(H, K, slices, dts):
+    x_dt, a_dt, o_dt = dts
+    wl = W.shrink_custom(SPLIT_T_LENS, SPLIT_T_IDX, H=H, K=K, L=3, slices=slices, x_dtype=x_dt,
+                         a_dtype=a_dt, out_dtype=o_dt, values="int", seed=H + K)
+    assert run_and_check(wl, exact=True) > 0
+
+
+def test_shrink_multi_slice_with_a_misaligned_output_equals_single_calls():
+    """A slice whose output rows are not 16-byte aligned runs on the generic
+    kernel; the other slices of the same call keep their fast kernel, so
+    every slice equals its own single call bit for bit."""
+    import torch
+    import segmented_gather_gemm_amd as sg
+    lens, idx = ragged(21, 14, 80, 4)
+    wl = W.shrink_custom(lens, idx, H=1024, K=32, L=4, slices=3, seed=21)
+    dw = DeviceShrink(wl)
+    wide = torch.zeros((wl.T, wl.K + 3), dtype=torch.bfloat16, device="cuda")
+    outs = dw.fresh_outs()
+    wide[:, :wl.K] = outs[1]
+    outs[1] = wide[:, :wl.K]                       # row stride 35 elements: misaligned
+    sg.sgmv_shrink_multi_slice(dw.x, list(zip(dw.a, outs)), dw.start, dw.lens, dw.idx,
+                               wl.batches, wl.max_seq_len, wl.scale)
+    for i in range(3):
+        alone = dw.fresh_outs()[i]
+        if i == 1:
+            w2 = torch.zeros_like(wide)
+            w2[:, :wl.K] = alone
+            alone = w2[:, :wl.K]
+        sg.sgmv_shrink(dw.x, dw.a[i], alone, dw.start, dw.lens, dw.idx, wl.batches,
+                       wl.max_seq_len, wl.scale)
+        assert np.array_equal(to_host_bits(outs[i]), to_host_bits(alone)), i
+    assert assert_shrink_parity(wl, [to_host_bits(o) for o in outs]) > 0
