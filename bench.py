@@ -40,14 +40,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of every library source file (kernels, launch and entry points)."""
+def kernel_source_hash(family: str = "expand") -> str:
+    """Hash of the library sources a kernel family is built from (kernels,
+    launch and entry points): the expand's files are every source not named
+    sgmv_shrink*; the shrink (LoRA-A projection) uses all of them."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+        if not name.endswith((".hip", ".h", ".cpp")):
+            continue
+        if family == "expand" and name.startswith("sgmv_shrink"):
+            continue
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -430,7 +435,7 @@ def run_shrink(args):
     sec = ms * 1e-3
     gbs = model_bytes / sec / 1e9
     tokens_s = wl.T / sec
-    ksha = kernel_source_hash()
+    ksha = kernel_source_hash("shrink")
     traffic_bytes = None if split else traffic_from_profiles(args.workload, ksha)
     traffic = None if traffic_bytes is None else round(traffic_bytes / sec / 1e9, 2)
     log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "

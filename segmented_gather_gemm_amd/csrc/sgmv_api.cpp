@@ -15,34 +15,11 @@
 #include <tuple>
 
 #include "sgmv.h"
+#include "sgmv_host.h"
 #include "sgmv_launch.h"
 
-namespace {
-
-// Row tiles (16 rows each) per band of the fast kernels' walk: each XCD
-// covers its column group band by band, so a band's input rows and weight
-// tiles are re-read from its L2 rather than from memory.
-#ifndef SGMV_BAND_TILES
-#define SGMV_BAND_TILES 64
-#endif
-constexpr int32_t kBandTiles = SGMV_BAND_TILES;
-
-// Units per chunk of the fast kernels' strided assignment: a workgroup keeps
-// its weight tile in registers over a chunk, and the workgroups of an XCD
-// stay within about (workgroups per XCD) chunks of each other in the walk.
-#ifndef SGMV_CHUNK_UNITS
-#define SGMV_CHUNK_UNITS 32
-#endif
-constexpr int32_t kChunkUnits = SGMV_CHUNK_UNITS;
-
-// Smallest number of work units per workgroup the grid is sized for (from the
-// host's upper bound on units; large problems run at full occupancy anyway).
-#ifndef SGMV_UNITS_PER_WORKGROUP
-#define SGMV_UNITS_PER_WORKGROUP 3
-#endif
-constexpr int64_t kUnitsPerWorkgroup = SGMV_UNITS_PER_WORKGROUP;
-static_assert(kChunkUnits >= 1 && kBandTiles % kChunkUnits == 0,
-              "chunks must not straddle a column tile's run of a band");
+namespace sgmv {
+namespace host {
 
 thread_local std::string g_error;
 
@@ -54,37 +31,6 @@ sgmv_status fail(sgmv_status status, const char* fmt, ...) {
   va_end(ap);
   g_error = buf;
   return status;
-}
-
-bool known_dtype(int32_t d) { return d == SGMV_F16 || d == SGMV_BF16 || d == SGMV_F32; }
-int64_t elem_bytes(int32_t d) { return d == SGMV_F32 ? 4 : 2; }
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int ksteps_for(int64_t rank) {
-  if (rank <= 16) return 0;
-  if (rank <= 32) return 1;
-  if (rank <= 64) return 2;
-  if (rank <= 128) return 4;
-  return 8;  // rank <= SGMV_MAX_RANK
-}
-
-bool fast_rank(int64_t K) { return K % 8 == 0 && K <= SGMV_MAX_RANK; }
-
-// The kernel for a call: a fast (pipelined) kernel when rank, slice widths
-// and alignment allow it (`fast`), with gathered row tiles for `gather`
-// (per-token calls only), else the generic one.
-const void* pick_kernel(int xd, int wd, int od, bool add, int64_t K, bool fast, bool gather) {
-  using namespace sgmv;
-  if (fast) {
-    switch (ksteps_for(K)) {
-      case 0: return fast_kernel_ks0(xd, wd, od, add, gather);
-      case 1: return fast_kernel_ks1(xd, wd, od, add, gather);
-      case 2: return fast_kernel_ks2(xd, wd, od, add, gather);
-      case 4: return fast_kernel_ks4(xd, wd, od, add, gather);
-      default: return fast_kernel_ks8(xd, wd, od, add, gather);
-    }
-  }
-  return generic_kernel(xd, wd, od, add);
 }
 
 // Per-device compute-unit counts and per-(device, kernel, LDS bucket)
@@ -117,6 +63,68 @@ hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups
   *workgroups = cu->second * occ->second;
   return hipSuccess;
 }
+
+}  // namespace host
+}  // namespace sgmv
+
+namespace {
+
+using namespace sgmv::host;
+
+// Row tiles (16 rows each) per band of the fast kernels' walk: each XCD
+// covers its column group band by band, so a band's input rows and weight
+// tiles are re-read from its L2 rather than from memory.
+#ifndef SGMV_BAND_TILES
+#define SGMV_BAND_TILES 64
+#endif
+constexpr int32_t kBandTiles = SGMV_BAND_TILES;
+
+// Units per chunk of the fast kernels' strided assignment: a workgroup keeps
+// its weight tile in registers over a chunk, and the workgroups of an XCD
+// stay within about (workgroups per XCD) chunks of each other in the walk.
+#ifndef SGMV_CHUNK_UNITS
+#define SGMV_CHUNK_UNITS 32
+#endif
+constexpr int32_t kChunkUnits = SGMV_CHUNK_UNITS;
+
+// Smallest number of work units per workgroup the grid is sized for (from the
+// host's upper bound on units; large problems run at full occupancy anyway).
+#ifndef SGMV_UNITS_PER_WORKGROUP
+#define SGMV_UNITS_PER_WORKGROUP 3
+#endif
+constexpr int64_t kUnitsPerWorkgroup = SGMV_UNITS_PER_WORKGROUP;
+static_assert(kChunkUnits >= 1 && kBandTiles % kChunkUnits == 0,
+              "chunks must not straddle a column tile's run of a band");
+
+
+
+int ksteps_for(int64_t rank) {
+  if (rank <= 16) return 0;
+  if (rank <= 32) return 1;
+  if (rank <= 64) return 2;
+  if (rank <= 128) return 4;
+  return 8;  // rank <= SGMV_MAX_RANK
+}
+
+bool fast_rank(int64_t K) { return K % 8 == 0 && K <= SGMV_MAX_RANK; }
+
+// The kernel for a call: a fast (pipelined) kernel when rank, slice widths
+// and alignment allow it (`fast`), with gathered row tiles for `gather`
+// (per-token calls only), else the generic one.
+const void* pick_kernel(int xd, int wd, int od, bool add, int64_t K, bool fast, bool gather) {
+  using namespace sgmv;
+  if (fast) {
+    switch (ksteps_for(K)) {
+      case 0: return fast_kernel_ks0(xd, wd, od, add, gather);
+      case 1: return fast_kernel_ks1(xd, wd, od, add, gather);
+      case 2: return fast_kernel_ks2(xd, wd, od, add, gather);
+      case 4: return fast_kernel_ks4(xd, wd, od, add, gather);
+      default: return fast_kernel_ks8(xd, wd, od, add, gather);
+    }
+  }
+  return generic_kernel(xd, wd, od, add);
+}
+
 
 // Checks shared by the entry points.  `slices` are host descriptors.  With
 // `per_token` (the BGMV form) segment b is row b alone: start and lens are
@@ -306,206 +314,6 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   return SGMV_OK;
 }
 
-// ---------------------------------------------------------------------------
-// LoRA-A projection (shrink).
-// ---------------------------------------------------------------------------
-
-// Fast shrink kernel for k16 tiles of 16 rows per slice and ns slices.
-const void* pick_shrink_kernel(int xd, int wd, int od, int k16, int ns, bool split_t) {
-  using namespace sgmv;
-  switch (k16) {
-    case 1: return shrink_kernel_k1(xd, wd, od, ns, split_t);
-    case 2: return shrink_kernel_k2(xd, wd, od, ns, split_t);
-    case 4: return shrink_kernel_k4(xd, wd, od, ns, split_t);
-    case 8: return shrink_kernel_k8(xd, wd, od, ns, split_t);
-    default: return shrink_kernel_k16(xd, wd, od, ns, split_t);
-  }
-}
-
-int next_pow2(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
-
-// Split-T (64-token units, lora_A shared through LDS) once the batch has at
-// least this many 64-token units; split-H (16-token units) below, where it
-// keeps more compute units busy.
-#ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS
-#define SGMV_SHRINK_SPLIT_T_MIN_UNITS 64
-#endif
-
-// One launch over slices [first, first + count) of `slices` (already checked).
-sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices, int first,
-                          int count, const int64_t* start, const int64_t* lens,
-                          const int64_t* idx, int64_t batches, float scale, bool fast,
-                          bool split_t, hipStream_t stream) {
-  using namespace sgmv;
-  const sgmv_shrink_slice& s0 = slices[first];
-  const int64_t K = s0.lora_a.rows;
-  const int64_t H = x.cols;
-  const int k16 = next_pow2((int)((K + 15) / 16));
-  ShrinkParams p{};
-  p.x = x.data;
-  p.start = start;
-  p.lens = lens;
-  p.idx = idx;
-  p.x_row_bytes = x.row_stride * elem_bytes(x.dtype);
-  p.T = x.rows;
-  p.H = (int32_t)H;
-  p.batches = (int32_t)batches;
-  p.L = (int32_t)s0.lora_a.num;
-  p.K = (int32_t)K;
-  p.num_slices = count;
-  p.scale = scale;
-  p.sort_slots = batches >= kSortMinBatches && batches <= kSortMaxBatches &&
-                 s0.lora_a.num <= (1 << 22);
-  for (int i = 0; i < count; ++i) {
-    const sgmv_shrink_slice& s = slices[first + i];
-    p.s[i].a = s.lora_a.data;
-    p.s[i].out = s.out.data;
-    p.s[i].out_row_bytes = s.out.row_stride * elem_bytes(s.out.dtype);
-  }
-  const void* kernel =
-      fast ? pick_shrink_kernel(x.dtype, s0.lora_a.dtype, s0.out.dtype, k16, count, split_t)
-           : shrink_generic_kernel(x.dtype, s0.lora_a.dtype, s0.out.dtype);
-  if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no shrink kernel for this dtype combination");
-  const int64_t steps = (H + 31) / 32;  // 32-wide hidden steps
-  if (fast && split_t) {
-    // every wave runs all steps; loop positions in whole turns of the ring
-    // of blocks
-    const int64_t turn = shrink_ring(shrink_block_loads_t(x.dtype, k16, count)) *
-                         shrink_block_steps_t(k16 * count);
-    p.steps = (int32_t)((steps + turn - 1) / turn * turn);
-  } else if (fast) {
-    // each wave takes a quarter of the steps; loop positions in whole turns
-    // of the ring
-    const int64_t per_wave = (steps + kWaves - 1) / kWaves;
-    const int64_t turn = shrink_ring(shrink_block_loads_h(x.dtype, k16 * count)) *
-                         shrink_block_steps_h(x.dtype, k16 * count);
-    p.steps = (int32_t)((per_wave + turn - 1) / turn * turn);
-  }
-  const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);
-  int capacity = 0;
-  hipError_t e = device_capacity(kernel, lds, &capacity);
-  if (e != hipSuccess)
-    return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
-  // Units are tiles of active segments: at most ceil(T / rows) + min(batches,
-  // T) of them.  One per workgroup while they fit on the chip.
-  const int64_t tile_rows = fast && split_t ? kShrinkTokensSplitT : kTileRows;
-  const int64_t units =
-      (x.rows + tile_rows - 1) / tile_rows + (batches < x.rows ? batches : x.rows);
-  int64_t grid = units < capacity ? units : capacity;
-  if (grid > 8) grid -= grid % 8;
-  if (grid < 1) grid = 1;
-  p.grid = (int32_t)grid;
-  void* args[] = {&p};
-  e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
-  if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return SGMV_OK;
-}
-
-sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slices,
-                                    int num_slices, const int64_t* start, const int64_t* lens,
-                                    const int64_t* idx, int64_t batches, int64_t max_seq_len,
-                                    float scale, hipStream_t stream) {
-  using namespace sgmv;
-  if (num_slices < 1 || num_slices > SGMV_MAX_SLICES)
-    return fail(SGMV_ERR_INVALID_ARGUMENT, "num_slices must be in 1..%d, got %d",
-                SGMV_MAX_SLICES, num_slices);
-  if (!known_dtype(x.dtype)) return fail(SGMV_ERR_INVALID_ARGUMENT, "unknown inputs dtype %d", x.dtype);
-  if (x.rows < 0 || x.cols < 1 || x.row_stride < x.cols)
-    return fail(SGMV_ERR_INVALID_ARGUMENT,
-                "inputs shape (%lld, %lld) with row stride %lld is invalid", (long long)x.rows,
-                (long long)x.cols, (long long)x.row_stride);
-  if (x.rows > INT32_MAX)
-    return fail(SGMV_ERR_UNSUPPORTED, "more than 2^31-1 tokens (%lld)", (long long)x.rows);
-  if (x.cols > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "hidden size exceeds 2^31-1");
-  if (batches < 0) return fail(SGMV_ERR_INVALID_ARGUMENT, "batches must be >= 0");
-  if (batches > SGMV_MAX_BATCHES)
-    return fail(SGMV_ERR_UNSUPPORTED, "batches %lld exceeds %d", (long long)batches,
-                SGMV_MAX_BATCHES);
-  if (max_seq_len < 0) return fail(SGMV_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
-  const sgmv_shrink_slice& s0 = slices[0];
-  const int64_t K = s0.lora_a.rows;
-  const int64_t L = s0.lora_a.num;
-  for (int i = 0; i < num_slices; ++i) {
-    const sgmv_shrink_slice& s = slices[i];
-    if (!known_dtype(s.lora_a.dtype) || !known_dtype(s.out.dtype))
-      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: unknown dtype", i);
-    if (s.lora_a.dtype == SGMV_F32)
-      return fail(SGMV_ERR_UNSUPPORTED, "slice %d: lora_a must be float16 or bfloat16", i);
-    if (x.dtype != s.lora_a.dtype && x.dtype != SGMV_F32)
-      return fail(SGMV_ERR_UNSUPPORTED,
-                  "slice %d: inputs must have lora_a's dtype or float32 (got %d with %d)", i,
-                  x.dtype, s.lora_a.dtype);
-    if (s.lora_a.num < 0 || s.lora_a.rows < 1 || s.lora_a.cols < 1)
-      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: lora_a shape is invalid", i);
-    if (s.lora_a.cols != x.cols)
-      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: lora_a hidden %lld != inputs hidden %lld",
-                  i, (long long)s.lora_a.cols, (long long)x.cols);
-    if (s.out.rows != x.rows || s.out.cols != s.lora_a.rows || s.out.row_stride < s.out.cols)
-      return fail(SGMV_ERR_INVALID_ARGUMENT,
-                  "slice %d: output (%lld, %lld) with row stride %lld must be (%lld, %lld)", i,
-                  (long long)s.out.rows, (long long)s.out.cols, (long long)s.out.row_stride,
-                  (long long)x.rows, (long long)s.lora_a.rows);
-    if (i > 0 && (s.lora_a.rows != K || s.lora_a.num != L || s.lora_a.dtype != s0.lora_a.dtype ||
-                  s.out.dtype != s0.out.dtype))
-      return fail(SGMV_ERR_INVALID_ARGUMENT,
-                  "slice %d: rank, lora_num and dtypes must match slice 0", i);
-  }
-  if (K > SGMV_MAX_RANK)
-    return fail(SGMV_ERR_UNSUPPORTED, "rank %lld exceeds %d", (long long)K, SGMV_MAX_RANK);
-  if (L > INT32_MAX) return fail(SGMV_ERR_UNSUPPORTED, "lora_num exceeds 2^31-1");
-  if (batches == 0 || x.rows == 0) {
-    g_error.clear();
-    return SGMV_OK;  // nothing to do
-  }
-  if (!x.data) return fail(SGMV_ERR_INVALID_ARGUMENT, "inputs data pointer is null");
-  if (!start || !lens || !idx)
-    return fail(SGMV_ERR_INVALID_ARGUMENT, "segment metadata pointer is null");
-  for (int i = 0; i < num_slices; ++i)
-    if (!slices[i].out.data || (!slices[i].lora_a.data && L > 0))
-      return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: null data pointer", i);
-
-  // Fast kernels: 16-byte blocks everywhere, hidden < 2^26 and a unit's rows
-  // (64) of inputs or outputs spanning less than 2 GiB (32-bit buffer
-  // offsets).  Decided for the inputs, then per slice; slices are launched
-  // in runs that take the same kernel family (so a slice's result does not
-  // depend on the others in the call).
-  const int64_t xb = elem_bytes(x.dtype), ob = elem_bytes(s0.out.dtype);
-  const int64_t span = kShrinkTokensSplitT;
-  const bool fast_x = K % 8 == 0 && x.cols % 8 == 0 && x.cols < (int64_t(1) << 26) &&
-                      aligned16(x.data) && (x.row_stride * xb) % 16 == 0 &&
-                      span * x.row_stride * xb < (int64_t(1) << 31);
-  auto fast_slice = [&](int i) {
-    const sgmv_shrink_slice& s = slices[i];
-    return fast_x && aligned16(s.lora_a.data) && aligned16(s.out.data) &&
-           (s.out.row_stride * ob) % 16 == 0 && span * s.out.row_stride * ob < (int64_t(1) << 31);
-  };
-  // The fast kernels take up to kShrinkMaxSlicesPerLaunch slices and 16 k
-  // tiles of 16 rows per launch: more slices go in several launches (each
-  // reads the inputs again).
-  const int k16 = next_pow2((int)((K + 15) / 16));
-  int fast_per_launch = 16 / k16;
-  if (fast_per_launch > kShrinkMaxSlicesPerLaunch) fast_per_launch = kShrinkMaxSlicesPerLaunch;
-  const bool split_t =
-      (x.rows + kShrinkTokensSplitT - 1) / kShrinkTokensSplitT >= SGMV_SHRINK_SPLIT_T_MIN_UNITS;
-  for (int first = 0; first < num_slices;) {
-    const bool fast = fast_slice(first);
-    const int limit = fast ? fast_per_launch : num_slices;
-    int count = 1;
-    while (first + count < num_slices && count < limit && fast_slice(first + count) == fast)
-      ++count;
-    const sgmv_status st = shrink_launch(x, slices, first, count, start, lens, idx, batches,
-                                         scale, fast, split_t, stream);
-    if (st != SGMV_OK) return st;
-    first += count;
-  }
-  g_error.clear();
-  return SGMV_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -548,28 +356,7 @@ sgmv_status sgmv_bgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_m
                           1, add_inputs, stream, true);
 }
 
-sgmv_status sgmv_shrink(sgmv_matrix inputs, sgmv_stack lora_a, sgmv_matrix out,
-                        const int64_t* b_seq_start_loc, const int64_t* seq_lens,
-                        const int64_t* lora_indices, int64_t batches, int64_t max_seq_len,
-                        float scale, hipStream_t stream) {
-  sgmv_shrink_slice s;
-  s.lora_a = lora_a;
-  s.out = out;
-  return shrink_check_and_launch(inputs, &s, 1, b_seq_start_loc, seq_lens, lora_indices, batches,
-                                 max_seq_len, scale, stream);
-}
-
-sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice* slices,
-                                    int num_slices, const int64_t* b_seq_start_loc,
-                                    const int64_t* seq_lens, const int64_t* lora_indices,
-                                    int64_t batches, int64_t max_seq_len, float scale,
-                                    hipStream_t stream) {
-  if (!slices) return fail(SGMV_ERR_INVALID_ARGUMENT, "slices pointer is null");
-  return shrink_check_and_launch(inputs, slices, num_slices, b_seq_start_loc, seq_lens,
-                                 lora_indices, batches, max_seq_len, scale, stream);
-}
-
-const char* sgmv_last_error(void) { return g_error.c_str(); }
+const char* sgmv_last_error(void) { return sgmv::host::g_error.c_str(); }
 
 int sgmv_abi_version(void) { return SGMV_ABI_VERSION; }
 

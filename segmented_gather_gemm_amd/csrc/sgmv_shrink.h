@@ -38,6 +38,7 @@
 #pragma once
 
 #include "sgmv_device.h"
+#include "sgmv_shrink_launch.h"
 
 namespace sgmv {
 namespace dev {

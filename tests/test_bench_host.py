@@ -38,6 +38,8 @@ def test_named_workload_byte_counts():
 def test_kernel_source_hash_is_stable():
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+    # the shrink's hash also covers its own sources
+    assert bench.kernel_source_hash("shrink") != bench.kernel_source_hash("expand")
 
 
 def test_refuses_more_than_one_gpu():
