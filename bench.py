@@ -492,7 +492,8 @@ def run_shrink(args):
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "traffic_bytes_per_launch": traffic_bytes,
-            "kernel": "shrink_fast",
+            # the library runs split-T from 64 units of 64 tokens up, split-H below
+            "kernel": "shrink_split_t" if -(-wl.T // 64) >= 64 else "shrink_split_h",
             "kernel_source_sha256_16": ksha,
         },
         "copy_ceiling_gbs": ceiling,
