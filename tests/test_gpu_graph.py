@@ -34,3 +34,35 @@ def test_graph_replays_match_eager(multi):
         other = to_host_bits(run(dw.fresh_out()))  # eager work in between
         torch.cuda.synchronize()
         assert np.array_equal(other, eager)
+
+
+@pytest.mark.parametrize("multi,T", [(False, 300), (True, 300), (True, 5000)])
+def test_shrink_graph_replays_match_eager(multi, T):
+    """sgmv_shrink / sgmv_shrink_multi_slice captured once and replayed; T =
+    5000 takes the split-T kernels, T = 300 the split-H ones."""
+    import torch
+    from gpu_util import DeviceShrink, assert_shrink_parity
+    rng = np.random.default_rng(T)
+    lens = rng.integers(1, 2 * T // 10, size=10)
+    lens = (lens * T // lens.sum()).tolist()
+    wl = W.shrink_custom(lens, [0, 1, -1, 2, 1, 0, 2, -1, 1, 0], H=512, K=32, L=3,
+                         slices=3 if multi else 1, seed=T)
+    dw = DeviceShrink(wl)
+    eager = [to_host_bits(o) for o in dw.run(multi=multi)]
+    assert assert_shrink_parity(wl, eager) > 0
+    outs = dw.fresh_outs()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        dw.run(outs, multi=multi)
+    for replay in range(4):
+        for o, o0 in zip(outs, dw.outs0):
+            o.copy_(o0)                           # eager reset between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert np.array_equal(to_host_bits(o), eager[i]), f"replay {replay} slice {i}"
+        other = [to_host_bits(o) for o in dw.run(multi=multi)]  # eager work in between
+        torch.cuda.synchronize()
+        for a, b in zip(other, eager):
+            assert np.array_equal(a, b)
