@@ -120,6 +120,16 @@ __device__ __forceinline__ void shrink_store(const ShrinkParams& p, int i, int32
   store4<OD>(orc, off, v * p.scale);
 }
 
+// LDS layout of an operand fragment staged from coalesced loads (16 rows x
+// 32 hidden, 1 KiB in MFMA operand order, lora_A or input): lane (j, g)'s 16
+// bytes sit in slot 16 g + (j ^ 4 g) of the fragment.  A coalesced load
+// reads R rows x 64 / R lanes of contiguous 16-byte blocks; the 16 lanes the
+// LDS serves together then cover one or two rows and 4 or 2 steps, whose
+// slots fall in 16 different bank groups when fragments are 65 slots apart
+// (one row, 4 steps) or 66 (two rows, 2 steps).  The MFMA operand reads
+// (16 lanes of one g, j = 0..15) are conflict-free for any stride.
+__device__ __forceinline__ int frag_slot(int j, int g) { return 16 * g + (j ^ (4 * g)); }
+
 // ---------------------------------------------------------------------------
 // Split-H: 16 tokens per unit; the four waves of the workgroup split the
 // hidden steps and add their partial sums through LDS.
@@ -142,10 +152,26 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
   // fragments added per LDS round: kW x kRound fragments of 1 KiB <= 32 KiB
   constexpr int kRound = kT < 32 / kW ? kT : 32 / kW;
   constexpr int xb = XD == F32 ? 4 : 2;
+  // Coalesced loads (up to 8 k tiles): load i of a block reads rows
+  // i kRPI .. + kRPI - 1 of a 16-row tile, kLPR lanes per row covering the
+  // block's kB steps contiguously (lane l: row l / kLPR, hidden block
+  // l % kLPR, i.e. block (l % kLPR) % 4 of step (l % kLPR) / 4); the wave
+  // scatters them into MFMA operand order in its own LDS region (see
+  // frag_slot; fragments 65 slots apart, 66 when a load spans 8 rows) and
+  // reads the operands back.  More k tiles load operands directly (16 rows x
+  // 64 bytes per load), which needs no LDS.
+  constexpr bool kCoal = kT <= 8;
+  constexpr int kLPR = 4 * kB;
+  constexpr int kRPI = 64 / kLPR;
+  constexpr int kStride = kLPR == 8 ? 66 : 65;
+  static_assert(!kCoal || (kB % 2 == 0 && kRPI * kB == 16), "coalesced block shape");
   prefetch_params(p);
   extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kW];
   __shared__ f32x4 red[kW][kRound][64];
+  // per wave: the block's input fragments (steps 0 .. kB - 1), then each k
+  // tile's ([tile + 1] kB + step)
+  __shared__ u32x4 stage[kCoal ? kW : 1][kCoal ? (kT + 1) * kB : 1][kCoal ? kStride : 1];
   const SegTable tab = seg_table(lds, p.batches);
   const int32_t U = build_tile_table(p, tab, wave_total, kTileRows);
   if (U == 0) return;
@@ -163,11 +189,18 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
   // run over p.steps >= q loop positions (the rest read nothing).
   const int32_t q_steps = (((H + 31) >> 5) + kW - 1) / kW;
   const int32_t s_beg = wave * q_steps;
+  // direct operand loads: row j, hidden block 8 g
   const uint32_t x_lane = (uint32_t)j * xrb + (uint32_t)(8 * g * xb);
   uint32_t a_lane[K16];  // row 16 kt + j of a slice's lora_A[a], hidden block 8 g
 #pragma unroll
   for (int kt = 0; kt < K16; ++kt)
     a_lane[kt] = (uint32_t)(16 * kt + j) * (uint32_t)H * 2u + (uint32_t)(16 * g);
+  // coalesced loads: row cr of the load, hidden block cb of the block's span
+  const int cr = lane / kLPR, cb = lane % kLPR;
+  const int cst = cb >> 2, cg = cb & 3;  // its step within the block and block in the step
+  const uint32_t xc_lane = (uint32_t)cr * xrb + (uint32_t)(8 * cb * xb);
+  const uint32_t ac_lane = (uint32_t)cr * (uint32_t)H * 2u + (uint32_t)(16 * cb);
+  const int r_slot = frag_slot(j, g);
 
   int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
   for (; u < u_end; ++u) {
@@ -175,29 +208,69 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
     const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kTileRows);
 
     auto load_block = [&](Block& blk, int32_t v0) __attribute__((always_inline)) {
-#pragma unroll
-      for (int st = 0; st < kB; ++st) {
-        const int32_t v = v0 + st;
+      if constexpr (kCoal) {
+        const int32_t v = v0 + cst;  // this lane's step
         const int32_t step = s_beg + v;
-        const bool ok = v < q_steps && 32 * step + 8 * g < H;
-        buf_load8<XD>(su.x, ok ? x_lane + (uint32_t)(32 * step * xb) : kOut, blk.x[st]);
+        const bool ok = v < q_steps && 32 * step + 8 * cg < H;
+        const uint32_t span = (uint32_t)(s_beg + v0);  // the block's first step
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int i = 0; i < kB; ++i) {
+          const uint32_t rows = (uint32_t)(i * kRPI);
+          buf_load8<XD>(su.x, ok ? xc_lane + rows * xrb + span * (uint32_t)(32 * xb) : kOut,
+                        blk.x[i]);
 #pragma unroll
-          for (int kt = 0; kt < K16; ++kt)
-            buf_load8<WD>(su.a[s], ok ? a_lane[kt] + (uint32_t)(64 * step) : kOut,
-                          &blk.a[st][s * K16 + kt]);
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < K16; ++kt)
+              buf_load8<WD>(su.a[s],
+                            ok ? ac_lane + (16u * kt + rows) * (uint32_t)H * 2u + span * 64u : kOut,
+                            &blk.a[i][s * K16 + kt]);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kB; ++st) {
+          const int32_t v = v0 + st;
+          const int32_t step = s_beg + v;
+          const bool ok = v < q_steps && 32 * step + 8 * g < H;
+          buf_load8<XD>(su.x, ok ? x_lane + (uint32_t)(32 * step * xb) : kOut, blk.x[st]);
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < K16; ++kt)
+              buf_load8<WD>(su.a[s], ok ? a_lane[kt] + (uint32_t)(64 * step) : kOut,
+                            &blk.a[st][s * K16 + kt]);
+        }
       }
     };
     f32x4 acc[kT];
 #pragma unroll
     for (int i = 0; i < kT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute_block = [&](const Block& blk) __attribute__((always_inline)) {
+      if constexpr (kCoal) {
+        // scatter into operand order (float32 inputs rounded to the weight
+        // dtype here), then read the operands back; one wave's region, so
+        // the LDS keeps the writes and reads in order without a barrier
 #pragma unroll
-      for (int st = 0; st < kB; ++st) {
-        const u32x4 xo = x_operand<XD, WD>(blk.x[st]);
+        for (int i = 0; i < kB; ++i) {
+          const int sl = frag_slot(i * kRPI + cr, cg);
+          stage[wave][cst][sl] = x_operand<XD, WD>(blk.x[i]);
 #pragma unroll
-        for (int i = 0; i < kT; ++i) acc[i] = mfma<WD>(blk.a[st][i], xo, acc[i]);
+          for (int t = 0; t < kT; ++t) stage[wave][(t + 1) * kB + cst][sl] = blk.a[i][t];
+        }
+#pragma unroll
+        for (int st = 0; st < kB; ++st) {
+          const u32x4 xo = stage[wave][st][r_slot];
+#pragma unroll
+          for (int t = 0; t < kT; ++t)
+            acc[t] = mfma<WD>(stage[wave][(t + 1) * kB + st][r_slot], xo, acc[t]);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kB; ++st) {
+          const u32x4 xo = x_operand<XD, WD>(blk.x[st]);
+#pragma unroll
+          for (int i = 0; i < kT; ++i) acc[i] = mfma<WD>(blk.a[st][i], xo, acc[i]);
+        }
       }
     };
 
@@ -257,15 +330,9 @@ struct SplitTBlock {
   u32x4 a[NS][Sh::kPairs];           // this wave's share of the block's lora_A tiles
 };
 
-// LDS layout of a split-T operand fragment (16 rows x 32 hidden, 1 KiB in
-// MFMA operand order, lora_A or input): lane (j, g)'s 16 bytes sit in slot
-// 16 g + (j ^ 4 g) of the fragment, and fragments are kFragSlots = 66 slots
-// apart.  The loads that fill it read 8 rows x 64 contiguous elements each
-// (lane l: row l / 8, elements 8 (l % 8) .. of the row's two-step span), so
-// the 16 lanes the LDS serves together write 16 different bank groups, and
-// the MFMA reads (16 lanes of one g) do as well.
+// Split-T fragments are kFragSlots = 66 slots apart (see frag_slot; its
+// loads span 8 rows).
 constexpr int kFragSlots = 66;
-__device__ __forceinline__ int frag_slot(int j, int g) { return 16 * g + (j ^ (4 * g)); }
 
 template <int XD, int WD, int OD, int K16, int NS>
 __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p) {

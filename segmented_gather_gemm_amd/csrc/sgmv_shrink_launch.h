@@ -61,7 +61,8 @@ constexpr int kShrinkTokensSplitT = 64;
 // is 4 or 2 (even: each load covers two steps).
 constexpr int shrink_block_steps_h(int xd, int tiles) {
   const int regs = 4 * ((xd == 2 ? 2 : 1) + tiles);
-  return regs <= 8 ? 8 : regs <= 16 ? 4 : regs <= 32 ? 2 : 1;
+  const int steps = regs <= 8 ? 8 : regs <= 16 ? 4 : regs <= 32 ? 2 : 1;
+  return tiles <= 8 && steps < 2 ? 2 : steps;  // coalesced loads (tiles <= 8) cover >= 2 steps
 }
 constexpr int shrink_block_steps_t(int tiles) {
   return tiles <= 4 ? 4 : 2;  // even: the loads cover two steps
