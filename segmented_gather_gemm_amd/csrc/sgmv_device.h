@@ -838,6 +838,34 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 #pragma unroll
   for (int q = 0; q < 2; ++q)
     o_off[q] = (uint32_t)(GATHER ? 0 : j * os_bytes) + (32 * q + 8 * g) * ob;
+  // Output tile of the wave (16 rows x 64 columns) in HBM, for contiguous
+  // rows (not GATHER): accessed row-wise, kLPR lanes per row (a row's 128
+  // bytes, 256 for float32, in one instruction, against 64 bytes with the
+  // accumulator layout), and moved between that layout and the MFMA
+  // accumulator layout through a per-wave LDS tile -- 16-byte block b of
+  // row r in slot kNB r + (b ^ swizzle(r)), which keeps both the row-wise
+  // and the accumulator-layout accesses free of bank conflicts.  Access m
+  // covers rows m kRPI .. + kRPI - 1; this lane reads or writes block oblk
+  // of row m kRPI + orow.
+  constexpr int kNB = 64 * ob / 16;           // 16-byte blocks per tile row
+  constexpr int kLPR = kNB;
+  constexpr int kRPI = 64 / kLPR;
+  constexpr int kOAcc = 2 * raw_vecs<OD>();   // row-wise accesses per tile
+  static_assert(kOAcc * kRPI == kTileRows, "row-wise accesses cover the tile");
+  __shared__ u32x4 o_lds[GATHER ? 1 : kWaves][GATHER ? 1 : kTileRows * kNB];
+  auto o_slot = [](int r, int b) __attribute__((always_inline)) -> int {
+    return kNB * r + (b ^ (kNB == 8 ? (r >> 1) : r));
+  };
+  // accumulator-layout block of lane (j, g): column group q, vector v
+  auto acc_blk = [&](int q, int v) __attribute__((always_inline)) -> int {
+    return raw_vecs<OD>() == 1 ? 4 * q + g : 2 * (4 * q + g) + v;
+  };
+  const int orow = lane / kLPR, oblk = lane % kLPR;
+  const int ocol = oblk * (16 / ob);          // first column of this lane's block
+  uint32_t oc_off[kOAcc];
+#pragma unroll
+  for (int m = 0; m < kOAcc; ++m)
+    oc_off[m] = (uint32_t)((m * kRPI + orow) * os_bytes + oblk * 16);
   auto w_off = [&](int s, int ks) __attribute__((always_inline)) -> uint32_t {
     const int kb = 32 * ks + 8 * g;
     return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
@@ -910,9 +938,16 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
       if (x_chunk(i) < kSteps) buf_load8<XD>(u.x, u.lx + x_off[i], &st.x[i * raw_vecs<XD>()]);
-    if constexpr (ADD) {
+    if constexpr (ADD && GATHER) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, u.lo + o_off[q], &st.o[q * raw_vecs<OD>()]);
+    } else if constexpr (ADD) {
+      // prior output, row-wise (st.o[m] = access m)
+#pragma unroll
+      for (int m = 0; m < kOAcc; ++m)
+        st.o[m] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.o, ocol < u.n_rem ? oc_off[m] : kOut,
+                                                         0, 0));
     }
   };
   // Publish this wave's chunks of a unit's input tile to LDS buffer `buf`
@@ -930,10 +965,22 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][kSteps],
                            const FastUnit& u, int buf) __attribute__((always_inline)) {
     f32x4 acc[4];
+    if constexpr (ADD && !GATHER) {
+      // row-wise prior output -> the wave's LDS tile -> accumulator layout
+#pragma unroll
+      for (int m = 0; m < kOAcc; ++m) o_lds[wave][o_slot(m * kRPI + orow, oblk)] = st.o[m];
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if constexpr (ADD) out_values<OD>(&st.o[q * raw_vecs<OD>()], v);
+      if constexpr (ADD && GATHER) {
+        out_values<OD>(&st.o[q * raw_vecs<OD>()], v);
+      } else if constexpr (ADD) {
+        u32x4 raw[raw_vecs<OD>()];
+#pragma unroll
+        for (int rv = 0; rv < raw_vecs<OD>(); ++rv) raw[rv] = o_lds[wave][o_slot(j, acc_blk(q, rv))];
+        out_values<OD>(raw, v);
+      }
       acc[2 * q] = f32x4{v[0], v[1], v[2], v[3]};
       acc[2 * q + 1] = f32x4{v[4], v[5], v[6], v[7]};
     }
@@ -952,13 +999,26 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
                           acc[2 * q + 1][3]};
       u32x4 raw[raw_vecs<OD>()];
       out_pack<OD>(v, raw);
-      // Column groups past the slice (only in a slice's last column tile)
-      // take an out-of-range offset; rows past the segment already lie
-      // outside the resource.
-      const uint32_t off = 32 * q + 8 * g < u.n_rem ? u.lo + o_off[q] : kOut;
-      // An overwrite writes each output line once and never reads it: stream
-      // it.  An accumulation has just read the line into L2; keep the default.
-      buf_store8<OD, ADD ? 0 : kStream>(u.o, off, raw);
+      if constexpr (GATHER) {
+        // Column groups past the slice (only in a slice's last column tile)
+        // take an out-of-range offset; rows past the segment already lie
+        // outside the resource.  An overwrite writes each output line once
+        // and never reads it: stream it.  An accumulation has just read the
+        // line into L2; keep the default.
+        const uint32_t off = 32 * q + 8 * g < u.n_rem ? u.lo + o_off[q] : kOut;
+        buf_store8<OD, ADD ? 0 : kStream>(u.o, off, raw);
+      } else {
+#pragma unroll
+        for (int rv = 0; rv < raw_vecs<OD>(); ++rv) o_lds[wave][o_slot(j, acc_blk(q, rv))] = raw[rv];
+      }
+    }
+    if constexpr (!GATHER) {
+      // the wave's LDS tile -> row-wise stores (same column and row clamps)
+#pragma unroll
+      for (int m = 0; m < kOAcc; ++m)
+        __builtin_amdgcn_raw_buffer_store_b128(o_lds[wave][o_slot(m * kRPI + orow, oblk)], u.o,
+                                               ocol < u.n_rem ? oc_off[m] : kOut, 0,
+                                               ADD ? 0 : kStream);
     }
   };
 
