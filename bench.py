@@ -40,15 +40,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+SHARED_SOURCES = ("sgmv_common.h", "sgmv_launch.h", "sgmv_host.h", "sgmv_host.cpp")
+
+
 def kernel_source_hash(family: str = "expand") -> str:
     """Hash of the library sources a kernel family is built from (kernels,
     launch and entry points): the expand's files are every source not named
-    sgmv_shrink*; the shrink (LoRA-A projection) uses all of them."""
+    sgmv_shrink*; the shrink's (LoRA-A projection) are the sgmv_shrink* files
+    and the shared ones."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if not name.endswith((".hip", ".h", ".cpp")):
             continue
         if family == "expand" and name.startswith("sgmv_shrink"):
+            continue
+        if family == "shrink" and not (name.startswith("sgmv_shrink") or name in SHARED_SOURCES):
             continue
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:

@@ -1,9 +1,11 @@
 """Build libsgmv.so in-tree with hipcc for gfx950 (MI355X).
 
 The library holds the C entry points (csrc/sgmv_api.cpp,
-csrc/sgmv_shrink_api.cpp) and the gfx950
+csrc/sgmv_shrink_api.cpp, with shared helpers in csrc/sgmv_host.cpp) and the
+gfx950
 kernels (csrc/sgmv_fast_ks*.hip, csrc/sgmv_generic.hip, built from
-csrc/sgmv_device.h; csrc/sgmv_shrink_*.hip, built from csrc/sgmv_shrink.h)
+csrc/sgmv_device.h; csrc/sgmv_shrink_*.hip, built from csrc/sgmv_shrink.h;
+both on csrc/sgmv_common.h)
 with the code object embedded; nothing is
 compiled at run time.  Packed-fp32 VALU instructions are disabled for every
 HIP translation unit.
@@ -19,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libsgmv.so")
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("sgmv_api.cpp", "sgmv_shrink_api.cpp", "sgmv_generic.hip", "sgmv_fast_ks0.hip", "sgmv_fast_ks1.hip",
+           ("sgmv_api.cpp", "sgmv_host.cpp", "sgmv_shrink_api.cpp", "sgmv_generic.hip", "sgmv_fast_ks0.hip", "sgmv_fast_ks1.hip",
             "sgmv_fast_ks2.hip", "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip",
             "sgmv_shrink_generic.hip", "sgmv_shrink_k1.hip", "sgmv_shrink_k2.hip",
             "sgmv_shrink_k4.hip", "sgmv_shrink_k8.hip", "sgmv_shrink_k16.hip")]

@@ -7,65 +7,11 @@
 // Predibase Lorax SGMV Expand Slice Kernel": inputs (total_tokens, rank);
 // lora_b (lora_num, slice_size, rank) float16/bfloat16; output
 // (total_tokens, full_hidden_size); slice_size equal to lora_b's row count.
-#include <cstdarg>
-#include <cstdio>
-#include <map>
-#include <mutex>
-#include <string>
-#include <tuple>
+#include <stdint.h>
 
 #include "sgmv.h"
 #include "sgmv_host.h"
 #include "sgmv_launch.h"
-
-namespace sgmv {
-namespace host {
-
-thread_local std::string g_error;
-
-sgmv_status fail(sgmv_status status, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_error = buf;
-  return status;
-}
-
-// Per-device compute-unit counts and per-(device, kernel, LDS bucket)
-// occupancy, computed once.
-std::mutex g_mu;
-std::map<int, int> g_cus;
-std::map<std::tuple<int, const void*, size_t>, int> g_occupancy;
-
-hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const size_t bucket = (lds_bytes + 4095) / 4096 * 4096;
-  std::lock_guard<std::mutex> lock(g_mu);
-  auto cu = g_cus.find(dev);
-  if (cu == g_cus.end()) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    cu = g_cus.emplace(dev, n > 0 ? n : 1).first;
-  }
-  const auto key = std::make_tuple(dev, kernel, bucket);
-  auto occ = g_occupancy.find(key);
-  if (occ == g_occupancy.end()) {
-    int blocks = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, sgmv::kThreads, bucket);
-    if (e != hipSuccess) return e;
-    occ = g_occupancy.emplace(key, blocks > 0 ? blocks : 1).first;
-  }
-  *workgroups = cu->second * occ->second;
-  return hipSuccess;
-}
-
-}  // namespace host
-}  // namespace sgmv
 
 namespace {
 

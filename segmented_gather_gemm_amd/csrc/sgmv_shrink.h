@@ -37,7 +37,7 @@
 // vmcnt.
 #pragma once
 
-#include "sgmv_device.h"
+#include "sgmv_common.h"
 #include "sgmv_shrink_launch.h"
 
 namespace sgmv {
