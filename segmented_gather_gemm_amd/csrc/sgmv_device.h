@@ -14,25 +14,27 @@
 //    device-side scheduler.  Index -1 segments and segments outside [0, T)
 //    get no tiles.
 //  * Work unit = (column tile of 256 output columns, 16-row tile of one
-//    segment).  Units are ordered column-tile-major, so consecutive units of
-//    a workgroup walk down the rows of a segment under one column tile and
-//    the adapter's weight tile stays in registers across all of them.
-//    Workgroups take equal contiguous unit ranges; workgroup ids are
-//    remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
-//    owns one contiguous eighth of the range, i.e. its own column tiles and
-//    hence its own slice of every adapter's weights in its L2.
+//    segment).  The column tiles are split into 8 groups, one per XCD
+//    (workgroup ids are dealt round-robin to the XCDs); a group's units are
+//    walked band of row tiles by band, column tile by column tile, so
+//    consecutive units of a workgroup run down the rows of a segment under
+//    one column tile and the adapter's weight tile stays in registers.  The
+//    workgroups of an XCD take interleaved chunks of that walk and so share
+//    input rows and weight tiles through the XCD's L2.
 //  * Each of the 4 wavefronts owns 64 of the 256 columns.  The contraction
 //    runs on the matrix cores as C^T = W . X^T with v_mfma_f32_16x16x32_
 //    {bf16,f16}: the weight rows are the MFMA rows (A operand, stationary in
 //    VGPRs), the 16 tokens of the tile are the MFMA columns (B operand).
 //    Weight rows are assigned to MFMA rows so that every lane ends up holding
-//    8 consecutive output columns of one token: the epilogue then reads the
-//    prior output and writes the result with 16-byte accesses, 64 contiguous
-//    bytes per token per instruction.
+//    8 consecutive output columns of one token.
 //  * Rank step ks of the MFMA covers rank [32 ks, 32 ks + 32); lane group g
 //    loads the 16-byte block 32 ks + 8 g of its token's input row and of its
-//    weight row, so one load instruction reads 64 contiguous bytes of each
-//    of 16 rows.
+//    weight row.
+//  * The prior output is read and the result written row-wise (a row's 128
+//    bytes, 256 for float32, per instruction) and moved to and from the
+//    accumulator layout through a small per-wave LDS tile.  The stores are
+//    non-temporal at device scope: every output line is written once and not
+//    read again by the call.
 //  * fp32 accumulation; with add_inputs the prior output seeds the
 //    accumulator, so the result is rounded once (v_cvt_pk_{bf16,f16}_f32,
 //    nearest even).  float32 inputs are rounded to the weight dtype first.
@@ -577,11 +579,9 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       if constexpr (GATHER) {
         // Column groups past the slice (only in a slice's last column tile)
         // take an out-of-range offset; rows past the segment already lie
-        // outside the resource.  An overwrite writes each output line once
-        // and never reads it: stream it.  An accumulation has just read the
-        // line into L2; keep the default.
+        // outside the resource.
         const uint32_t off = 32 * q + 8 * g < u.n_rem ? u.lo + o_off[q] : kOut;
-        buf_store8<OD, ADD ? 0 : kStream>(u.o, off, raw);
+        buf_store8<OD, kStream>(u.o, off, raw);
       } else {
 #pragma unroll
         for (int rv = 0; rv < raw_vecs<OD>(); ++rv) o_lds[wave][o_slot(j, acc_blk(q, rv))] = raw[rv];
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       for (int m = 0; m < kOAcc; ++m)
         __builtin_amdgcn_raw_buffer_store_b128(o_lds[wave][o_slot(m * kRPI + orow, oblk)], u.o,
                                                ocol < u.n_rem ? oc_off[m] : kOut, 0,
-                                               ADD ? 0 : kStream);
+                                               kStream);
     }
   };
 
