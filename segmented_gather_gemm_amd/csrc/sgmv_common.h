@@ -180,6 +180,22 @@ __device__ __forceinline__ void store_any8(void* base, int64_t e, int cnt, bool 
 // Scheduler.
 // ---------------------------------------------------------------------------
 
+// Inclusive prefix sum over the 64 lanes of a wave through DPP (VALU
+// operands routed across lanes, no LDS round trip): shifts by 1, 2, 4 and 8
+// within each 16-lane row, then lane 15 of each row added into the next row
+// (rows 1 and 3) and lane 31 into rows 2 and 3.  Lanes a shift or broadcast
+// does not reach add the `old` operand, 0.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 4, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 8, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowBcast15, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowBcast31, 0xc, 0xf, false);
+  return v;
+}
+
 // Segment table in LDS, filled by build_tile_table, one slot per segment
 // (slot order: see build_tile_table):
 //   tile_start[0..batches]  exclusive prefix sum of row tiles per slot
@@ -338,6 +354,23 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
         }
       }
     }
+  } else if (B <= 64) {
+    // Index order, every segment in one lane of wave 0: the tile counts are
+    // scanned in registers and the table is complete after one barrier.
+    if (wave == 0) {
+      int32_t row = 0, end = 0, a32 = -1, tiles = 0;
+      if (lane < B) read_segment(lane, &row, &end, &a32, &tiles);
+      const int32_t incl = wave_inclusive_sum(tiles);
+      if (lane < B) {
+        tab.tile_start[lane] = incl - tiles;
+        tab.seg_row[lane] = row;
+        tab.seg_end[lane] = end;
+        tab.seg_lora[lane] = a32 < 0 ? 0 : a32;
+      }
+      if (lane == 63) tab.tile_start[B] = incl;  // lanes >= B hold no tiles
+    }
+    __syncthreads();
+    return uniform(tab.tile_start[B]);
   } else {
     for (int b = tid; b < B; b += kThreads) {
       int32_t row, end, a32, tiles;
@@ -354,12 +387,7 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
   for (int base = 0; base < B; base += kThreads) {
     const int i = base + tid;
     const int32_t tiles = i < B ? tab.tile_start[i] : 0;
-    int32_t incl = tiles;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
+    const int32_t incl = wave_inclusive_sum(tiles);
     if (lane == 63) wave_total[wave] = incl;
     __syncthreads();
     int32_t before = carry, all = 0;

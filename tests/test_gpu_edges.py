@@ -107,6 +107,19 @@ def test_many_segments_multi_chunk_scan():
     run_and_check(wl)
 
 
+
+@pytest.mark.parametrize("B", [1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 100])
+def test_segment_counts_around_the_wave_scan(B):
+    # Up to 64 segments the row-tile prefix sums are taken in one wave's
+    # registers (a scan inside 16-lane rows, then across the rows); more
+    # segments take the workgroup-wide path.  Inactive segments in between.
+    rng = np.random.default_rng(500 + B)
+    lens = rng.integers(1, 40, size=B)
+    idx = rng.integers(-1, 5, size=B)
+    wl = W.custom(lens.tolist(), idx.tolist(), K=16, N=256, H=256, off=0, L=5, add=True,
+                  seed=B)
+    run_and_check(wl)
+
 def shuffled_placement(rng, lens):
     """Start rows for segments placed in a random order with small gaps."""
     start = np.zeros(len(lens), dtype=np.int64)

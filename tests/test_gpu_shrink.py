@@ -117,6 +117,16 @@ def test_shrink_adapter_ordered_table():
     assert run_and_check(wl) > 0
 
 
+
+@pytest.mark.parametrize("B,max_len", [(16, 30), (17, 30), (33, 30), (64, 30), (65, 30),
+                                       (49, 200), (64, 200), (65, 200)])
+def test_shrink_segment_counts_around_the_wave_scan(B, max_len):
+    """Segment counts at the edges of the in-register table scan (16-lane
+    rows, one wave of 64); the longer segments reach the 64-token units."""
+    lens, idx = ragged(700 + B + max_len, B, max_len, 6)
+    wl = W.shrink_custom(lens, idx, H=256, K=16, L=6, seed=B)
+    assert run_and_check(wl) > 0
+
 def test_shrink_long_segment_several_units_per_workgroup():
     """More 16-row tiles than the grid holds workgroups."""
     wl = W.shrink_custom([9000, 37, 1], [1, 0, 1], H=256, K=16, L=2, seed=10)
