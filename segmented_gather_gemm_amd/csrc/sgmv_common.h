@@ -453,12 +453,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // only picks the fast kernel when 16 rows of inputs or output span < 2 GiB).
 constexpr uint32_t kOut = 0x80000000u;
 
-template <int D>
+// Cache policy of a load: 0 is the default; kStreamLoad (non-temporal) for
+// data that is read once.
+constexpr int kStreamLoad = 0x2;  // nt
+
+template <int D, int POLICY = 0>
 __device__ __forceinline__ void buf_load8(rsrc_t r, uint32_t off, u32x4* dst) {
-  dst[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  dst[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY));
   if constexpr (D == F32)
-    dst[1] = __builtin_bit_cast(u32x4,
-                                __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0));
+    dst[1] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, POLICY));
 }
 
 // Cache policy of a store: 0 is the default; kStream (non-temporal at device

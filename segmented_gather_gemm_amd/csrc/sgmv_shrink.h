@@ -14,27 +14,32 @@
 //
 // Design.  The projection reads every input row once and writes a row of K
 // values, so it is bound by reading x (and, with many adapters and short
-// segments, by reading the lora_A stacks).  Per work unit -- a 16-row tile of
-// one segment -- the four wavefronts of a workgroup split the hidden
-// dimension into four contiguous quarters, each wave streams its quarter of
-// the 16 input rows and of every lora_A row the slices need, and the partial
-// sums are added through LDS at the end of the unit.  The slices share the
-// input tile: their lora_A rows are just more K rows (k tiles) of one
-// contraction, so a fused QKV projection reads x once.
+// segments, by reading the lora_A stacks).  The slices share the input tile:
+// their lora_A rows are just more K rows (k tiles) of one contraction, so a
+// fused QKV projection reads x once.  Two kernel forms:
+//  * split-H: a work unit is a 16-row tile of one segment; the four
+//    wavefronts split the hidden dimension, each streams its part of the 16
+//    input rows and of every lora_A row the slices need, and the partial
+//    sums are added through LDS at the end of the unit;
+//  * split-T (enough tokens): a unit is a 64-row tile; wave t owns tokens
+//    16 t .. 16 t + 15 over the whole hidden dimension and the lora_A blocks
+//    are loaded once per workgroup and shared through LDS.
 //
 // The contraction is y^T = A . x^T on the matrix cores
 // (v_mfma_f32_16x16x32_{bf16,f16}): 16 lora_A rows are the A operand, the 16
-// tokens of the tile the B operand, 32 hidden elements per instruction; lane
-// group g holds the 8-element block 8 g of each 32-wide step, so one load
-// instruction reads 64 contiguous bytes of each of 16 rows.  Each lane ends
-// with 4 consecutive k of one token per k tile.  Loads go through buffer
-// resources bounded by the tile's valid rows and the slice's K rows, so rows
-// past the segment and k past K read zero and store nothing; hidden blocks
-// past H take an offset outside every resource.  The step loop runs over a
-// ring of blocks in registers, issuing each block several blocks ahead of
-// its use; every block issues the same load instructions (blocks past the
-// end read nothing), so the compiler waits for one block with a nonzero
-// vmcnt.
+// tokens of the tile the B operand, 32 hidden elements per instruction; each
+// lane ends with 4 consecutive k of one token per k tile.  Loads are
+// coalesced -- 128 or more contiguous bytes of each row per instruction --
+// and staged through LDS into the MFMA operand order.  Input rows are read
+// once, so their loads are non-temporal (measured on MI355X, streaming reads
+// are markedly faster that way); lora_A rows are re-read by the units of an
+// adapter and keep the default policy.  Loads go through buffer resources
+// bounded by the tile's valid rows and the slice's K rows, so rows past the
+// segment and k past K read zero and store nothing; hidden blocks past H
+// take an offset outside every resource.  The step loop runs over a ring of
+// blocks in registers, issuing each block several blocks ahead of its use;
+// every block issues the same load instructions (blocks past the end read
+// nothing), so the compiler waits for one block with a nonzero vmcnt.
 #pragma once
 
 #include "sgmv_common.h"
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
           const uint32_t rows = (uint32_t)(i * kRPI);
-          buf_load8<XD>(su.x, ok ? xc_lane + rows * xrb + span * (uint32_t)(32 * xb) : kOut,
+          buf_load8<XD, kStreamLoad>(su.x, ok ? xc_lane + rows * xrb + span * (uint32_t)(32 * xb) : kOut,
                         blk.x[i]);
 #pragma unroll
           for (int s = 0; s < NS; ++s)
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
           const int32_t v = v0 + st;
           const int32_t step = s_beg + v;
           const bool ok = v < q_steps && 32 * step + 8 * g < H;
-          buf_load8<XD>(su.x, ok ? x_lane + (uint32_t)(32 * step * xb) : kOut, blk.x[st]);
+          buf_load8<XD, kStreamLoad>(su.x, ok ? x_lane + (uint32_t)(32 * step * xb) : kOut, blk.x[st]);
 #pragma unroll
           for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
         const int32_t step = v0 + 2 * (xq >> 1) + (lb >> 2);
         const bool ok = step < h_steps && 32 * step + 8 * (lb & 3) < H;
         const uint32_t span = (uint32_t)(32 * (step - (lb >> 2)) * xb);
-        buf_load8<XD>(su.x, ok ? x_lane[xq & 1] + span : kOut, blk.x[xq]);
+        buf_load8<XD, kStreamLoad>(su.x, ok ? x_lane[xq & 1] + span : kOut, blk.x[xq]);
       }
 #pragma unroll
       for (int q = 0; q < kP; ++q) {
