@@ -21,9 +21,11 @@
 //    wavefronts split the hidden dimension, each streams its part of the 16
 //    input rows and of every lora_A row the slices need, and the partial
 //    sums are added through LDS at the end of the unit;
-//  * split-T (enough tokens): a unit is a 64-row tile; wave t owns tokens
-//    16 t .. 16 t + 15 over the whole hidden dimension and the lora_A blocks
-//    are loaded once per workgroup and shared through LDS.
+//  * split-T (enough tokens): a unit is a 64-row tile, every wave runs the
+//    whole hidden dimension, and the lora_A blocks are loaded once per
+//    workgroup and shared through LDS; wave t owns tokens 16 t .. 16 t + 15,
+//    or, with an even number of k tiles (at least 4), 32 tokens and half of
+//    the k tiles, so that each fragment read from LDS feeds two MFMAs.
 //
 // The contraction is y^T = A . x^T on the matrix cores
 // (v_mfma_f32_16x16x32_{bf16,f16}): 16 lora_A rows are the A operand, the 16
@@ -324,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Split-T: 64 tokens per unit; wave t owns tokens 16 t .. 16 t + 15 and runs
-// all hidden steps, with the lora_A blocks shared through LDS.
+// Split-T: 64 tokens per unit, every wave runs all hidden steps, the lora_A
+// blocks shared through LDS (the wave-to-tile assignment is at the kernel).
 // ---------------------------------------------------------------------------
 
 template <int XD, int K16, int NS>
@@ -348,15 +350,26 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
   constexpr int kP = Sh::kPairs;
   constexpr int xb = XD == F32 ? 4 : 2;
   constexpr int kBuf = kT * kB;  // fragments of one block
+  // With an even number of k tiles, at least 4, the waves form a 2 x 2 grid:
+  // wave w takes token tiles 2 (w % 2) and 2 (w % 2) + 1 and the k tiles of
+  // half w / 2.  Each lora_A fragment read from LDS then feeds two MFMAs and
+  // each input fragment kT / 2, so a step takes 2 + kT / 2 fragment reads
+  // per wave instead of 1 + kT (LDS throughput bounds this kernel).
+  // Otherwise wave t takes token tile t and every k tile.  Either way each
+  // accumulator sees the same MFMAs in the same order.
+  constexpr bool kGrid = kT >= 4 && kT % 2 == 0;
+  constexpr int kTok = kGrid ? 2 : 1;       // token tiles per wave
+  constexpr int kKt = kGrid ? kT / 2 : kT;  // k tiles per wave
   prefetch_params(p);
   extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
   __shared__ int32_t wave_total[kWaves];
   // lora_A fragments of a block per buffer: [buffer][tile i * kB + step]
   // [slot] (see frag_slot)
   __shared__ u32x4 a_lds[2][kBuf][kFragSlots];
-  // each wave's input fragments of the block being computed (private to
-  // the wave, so one buffer)
-  __shared__ u32x4 x_lds[kWaves][kB][kFragSlots];
+  // input fragments of a block by token tile (the tile wave t loads); in
+  // the 2 x 2 grid two waves read each tile, so two buffers as for lora_A,
+  // otherwise a tile is private to its wave and one buffer does
+  __shared__ u32x4 x_lds[kGrid ? 2 : 1][kWaves][kB][kFragSlots];
   const SegTable tab = seg_table(lds, p.batches);
   const int32_t U = build_tile_table(p, tab, wave_total, kShrinkTokensSplitT);
   if (U == 0) return;
@@ -366,7 +379,8 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int tw = wave;  // token tile
+  const int tw = wave;  // token tile this wave loads
+  const int th = wave & 1, kh = wave >> 1;  // 2 x 2 grid: token pair, k half
   const int g = lane >> 4;
   const int j = lane & 15;
   const int32_t H = p.H;
@@ -438,19 +452,28 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
       // float32 inputs are rounded to the weight dtype here
 #pragma unroll
       for (int xq = 0; xq < kB; ++xq)
-        x_lds[wave][2 * (xq >> 1) + (lb >> 2)][x_slot[xq & 1]] = x_operand<XD, WD>(blk.x[xq]);
+        x_lds[kGrid ? buf : 0][wave][2 * (xq >> 1) + (lb >> 2)][x_slot[xq & 1]] =
+            x_operand<XD, WD>(blk.x[xq]);
       __syncthreads();
     };
-    f32x4 acc[kT];
+    f32x4 acc[kTok][kKt];
 #pragma unroll
-    for (int i = 0; i < kT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < kTok; ++h)
+#pragma unroll
+      for (int i = 0; i < kKt; ++i) acc[h][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute_block = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int st = 0; st < kB; ++st) {
-        const u32x4 xo = x_lds[wave][st][r_slot];
+        u32x4 xo[kTok];
 #pragma unroll
-        for (int i = 0; i < kT; ++i)
-          acc[i] = mfma<WD>(a_lds[buf][i * kB + st][r_slot], xo, acc[i]);
+        for (int h = 0; h < kTok; ++h)
+          xo[h] = x_lds[kGrid ? buf : 0][kGrid ? 2 * th + h : wave][st][r_slot];
+#pragma unroll
+        for (int i = 0; i < kKt; ++i) {
+          const u32x4 af = a_lds[buf][((kGrid ? kh * kKt : 0) + i) * kB + st][r_slot];
+#pragma unroll
+          for (int h = 0; h < kTok; ++h) acc[h][i] = mfma<WD>(af, xo[h], acc[h][i]);
+        }
       }
     };
 
@@ -479,8 +502,11 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
     }
 
 #pragma unroll
-    for (int i = 0; i < kT; ++i)
-      shrink_store<OD, K16>(p, i, su.row0, su.rows, 16 * tw, j, g, acc[i]);
+    for (int h = 0; h < kTok; ++h)
+#pragma unroll
+      for (int i = 0; i < kKt; ++i)
+        shrink_store<OD, K16>(p, (kGrid ? kh * kKt : 0) + i, su.row0, su.rows,
+                              16 * (kGrid ? 2 * th + h : tw), j, g, acc[h][i]);
   }
 }
 
