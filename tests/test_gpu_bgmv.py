@@ -56,3 +56,15 @@ def test_bgmv_all_tokens_without_adapter_touch_nothing():
     dw = DeviceWorkload(wl)
     out = to_host_bits(dw.run_bgmv(dw.fresh_out()))
     assert np.array_equal(out, wl.out0)
+
+
+@pytest.mark.parametrize("T,L", [(256, 1023), (400, 1200), (512, 2)])
+def test_bgmv_adapter_order_few_and_many_adapters(T, L):
+    # Tokens are ordered by adapter before they are gathered into row tiles;
+    # from two adapters (long runs) to more adapters than tokens.
+    rng = np.random.default_rng(T + L)
+    idx = rng.integers(-1, L, size=T)
+    wl = W.per_token(idx.tolist(), K=16, N=256, H=256, off=0, L=L, add=True, seed=T)
+    dw = DeviceWorkload(wl)
+    out = dw.run_bgmv(dw.fresh_out())
+    assert_parity(wl, to_host_bits(out))

@@ -144,6 +144,20 @@ def test_adapter_ordered_segment_table(B):
     run_and_check(wl)
 
 
+
+@pytest.mark.parametrize("B,L", [(128, 1023), (300, 1500), (512, 1100)])
+def test_adapter_ordered_segment_table_many_adapters(B, L):
+    # Adapter-ordered tables with up to 1500 adapters (the order is taken by
+    # ranking (adapter, index) keys) and one crowded adapter.
+    rng = np.random.default_rng(200 + B)
+    lens = rng.integers(0, 12, size=B)
+    idx = rng.integers(-1, L, size=B)
+    idx[: B // 8] = L - 1  # a crowded last adapter
+    start, T = shuffled_placement(rng, lens)
+    wl = W.custom(lens.tolist(), idx.tolist(), K=16, N=64, H=64, off=0, L=L, add=True,
+                  seed=B, start=start.tolist(), T=T)
+    run_and_check(wl)
+
 def test_strided_chunks_several_per_workgroup():
     # Enough 16x256 units that every workgroup takes several strided chunks
     # of its column group's walk; with 4 column tiles, half of the 8 column

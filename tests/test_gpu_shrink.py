@@ -127,6 +127,17 @@ def test_shrink_segment_counts_around_the_wave_scan(B, max_len):
     wl = W.shrink_custom(lens, idx, H=256, K=16, L=6, seed=B)
     assert run_and_check(wl) > 0
 
+
+@pytest.mark.parametrize("L", [40, 1100])
+def test_shrink_adapter_ordered_table_few_and_many_adapters(L):
+    """300 segments ordered by adapter, over few or over many adapters."""
+    rng = np.random.default_rng(300 + L)
+    B = 300
+    lens = rng.integers(1, 30, size=B)
+    idx = rng.integers(-1, L, size=B)
+    wl = W.shrink_custom(lens, idx, H=256, K=16, L=L, seed=12)
+    assert run_and_check(wl) > 0
+
 def test_shrink_long_segment_several_units_per_workgroup():
     """More 16-row tiles than the grid holds workgroups."""
     wl = W.shrink_custom([9000, 37, 1], [1, 0, 1], H=256, K=16, L=2, seed=10)
