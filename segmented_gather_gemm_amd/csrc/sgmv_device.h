@@ -600,10 +600,15 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // Software pipeline (see the file comment).  wA holds the weight tile of
   // the unit being computed; with double buffering a changed tile for the
   // next unit is loaded into wB one unit ahead and copied into wA before
-  // that unit computes.
+  // that unit computes.  The input and prior-output loads run kAhead units
+  // ahead: two for the rank <= 16 kernels on contiguous rows (a stage is 12
+  // registers there, and with few units per workgroup the second unit in
+  // flight hides more of the memory latency: llama7b-like q_proj 8.57 ->
+  // 8.04 us), one otherwise (measured slower with two).
   constexpr bool kDoubleW = kSteps <= SGMV_DOUBLE_W_MAX_KSTEPS;
+  constexpr int kAhead = KS == 0 && !GATHER ? 2 : 1;
   u32x4 wA[4][kSteps], wB[4][kDoubleW ? kSteps : 1];
-  Stage<XD, OD, KS> sA, sB;
+  Stage<XD, OD, KS> sA, sB, sC;
 
   FastUnit cur = next_unit();
   load_w(wA, cur);
@@ -611,12 +616,22 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   int32_t w_a = cur.a;
   bool w_pending = false;
   load_stage(sA, cur);
+  // With kAhead = 2, the next unit is decoded and its loads issued here.
+  bool have_nxt = false;
+  FastUnit nxt = cur;
+  if constexpr (kAhead == 2) {
+    have_nxt = pos.next();
+    if (have_nxt) nxt = next_unit();
+    load_stage(sB, nxt);
+  }
 
   // One step: publish the current unit's input tile to LDS buffer `buf`,
-  // issue the next unit's loads, then compute and store the current unit.
-  // The LDS buffers alternate; the barrier in publish_x also orders every
-  // wave's reads of a buffer before the next write to it.
-  auto step = [&](Stage<XD, OD, KS>& s_cur, Stage<XD, OD, KS>& s_nxt, int buf)
+  // issue the loads of the unit kAhead ahead (s_new), then compute and
+  // store the current unit.  Without a next unit the loads repeat the last
+  // one's, so every step issues the same memory instructions.  The LDS
+  // buffers alternate; the barrier in publish_x also orders every wave's
+  // reads of a buffer before the next write to it.
+  auto step = [&](Stage<XD, OD, KS>& s_cur, Stage<XD, OD, KS>& s_new, int buf)
                   __attribute__((always_inline)) -> bool {
     publish_x(s_cur, buf);
     if constexpr (kDoubleW) {
@@ -628,12 +643,12 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
         w_pending = false;
       }
     }
-    // Next unit, if any (without one the loads below repeat cur's, so every
-    // step issues the same memory instructions).
-    const bool more = pos.next();
-    FastUnit nxt = cur;
-    if (more) nxt = next_unit();
-
+    if constexpr (kAhead == 1) {
+      have_nxt = pos.next();
+      nxt = cur;
+      if (have_nxt) nxt = next_unit();
+    }
+    // the weight tile of the next unit
     const bool wswitch = nxt.tile != w_tile || nxt.a != w_a;
     if constexpr (kDoubleW) {
       if (wswitch) {
@@ -643,8 +658,14 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
         w_a = nxt.a;
       }
     }
-    load_stage(s_nxt, nxt);
-    // Keep the next unit's loads ahead of this unit's waits and arithmetic.
+    bool more2 = false;
+    FastUnit nxt2 = nxt;
+    if constexpr (kAhead == 2) {
+      more2 = have_nxt && pos.next();
+      if (more2) nxt2 = next_unit();
+    }
+    load_stage(s_new, nxt2);
+    // Keep the ahead loads in front of this unit's waits and arithmetic.
     __builtin_amdgcn_sched_barrier(0);
     compute_store(s_cur, wA, cur, buf);
     if constexpr (!kDoubleW) {
@@ -654,11 +675,21 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
         w_a = nxt.a;
       }
     }
-    if (!more) return false;
+    if (!have_nxt) return false;
     cur = nxt;
+    if constexpr (kAhead == 2) {
+      nxt = nxt2;
+      have_nxt = more2;
+    }
     return true;
   };
-  while (step(sA, sB, 0) && step(sB, sA, 1)) {
+  if constexpr (kAhead == 2) {
+    // stages rotate A -> B -> C (KS = 0: no LDS input buffers)
+    while (step(sA, sC, 0) && step(sB, sA, 0) && step(sC, sB, 0)) {
+    }
+  } else {
+    while (step(sA, sB, 0) && step(sB, sA, 1)) {
+    }
   }
 }
 
