@@ -164,8 +164,9 @@ typedef struct {
 /*
  * sgmv_shrink -- the LoRA-A projection that produces sgmv_expand_slice's
  * `inputs`.  The page (I/O Contract, Inputs; Usage Examples) describes those
- * inputs as the low-rank activations of the LoRA A projection, packed across
- * sequences, (total_tokens, rank); it prints no formula for the projection,
+ * inputs as the rank-sized activations the A-side LoRA projection produces
+ * for every token of every sequence, (total_tokens, rank); it prints no
+ * formula for the projection,
  * so this takes the plainest reading consistent with the expand:
  *
  *     out[t][k] = scale * sum_h inputs[t][h] * lora_a[a][k][h],   k < rank,

@@ -13,7 +13,8 @@
  *   - I/O Contract, Inputs: lora_B is (lora_num, slice_size, rank), so the
  *     contraction runs over rank: y[n] = sum_k x[k] * B[a][n][k];
  *     b_seq_start_loc gives each segment's first row, seq_len_tensor its
- *     length; lora index -1 means no LoRA is applied (rows untouched);
+ *     length; lora index -1 marks a segment without an adapter (rows
+ *     untouched);
  *     add_inputs=false (default) overwrites, true accumulates.
  *   - Description / Signature (CAST_TYPE, the mixed-precision cast):
  *     float32 inputs are rounded to the 16-bit weight type before the

@@ -111,9 +111,9 @@ int orc_check(const orc_slice* slices, int num_slices, int64_t K, int64_t L,
  * LoRA-A projection (shrink): the step that produces the expand's `inputs`.
  *
  * The wiki page "Implementation: Predibase Lorax SGMV Expand Slice Kernel"
- * (I/O Contract, Inputs; Usage Examples) describes `inputs` as the low-rank
- * activations of the LoRA A projection, packed across sequences, shape
- * (total_tokens, rank).  The page does not print the projection itself;
+ * (I/O Contract, Inputs; Usage Examples) describes `inputs` as the
+ * rank-sized activations the A-side LoRA projection produces for every token
+ * of every sequence, shape (total_tokens, rank).  The page does not print the projection itself;
  * this oracle takes the plainest reading consistent with it and with the
  * expand's conventions:
  *   - lora_A is stacked (lora_num, rank, hidden), out-by-in like lora_B;

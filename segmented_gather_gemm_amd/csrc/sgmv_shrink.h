@@ -4,9 +4,9 @@
 //
 // Operation: the wiki page "Implementation: Predibase Lorax SGMV Expand
 // Slice Kernel" (I/O Contract, Inputs; Usage Examples) describes the
-// expand's inputs as the low-rank activations of the LoRA A projection,
-// (total_tokens, rank), packed across sequences.  For segment b with adapter
-// a = idx[b] in [0, lora_num) and each row t of the segment,
+// expand's inputs as the rank-sized activations the A-side LoRA projection
+// produces for every token of every sequence, (total_tokens, rank).  For
+// segment b with adapter a = idx[b] in [0, lora_num) and each row t of it,
 //     y_s[t][k] = scale * sum_h x[t][h] * A_s[a][k][h],   k in [0, K),
 // for every slice s (lora_A stack A_s (L, K, H), output y_s (T, K)).  Rows of
 // other segments are not written.  float32 inputs are rounded to the weight

@@ -92,7 +92,7 @@ def test_tiny_ref_index_minus_one_rows_untouched():
 
 
 def test_usage_example_q_slice():
-    """Q slice of a fused QKV output, offset 0, accumulate (Usage Examples)."""
+    """Query window of a fused QKV output, offset 0, accumulate (Usage Examples)."""
     g = json.load(open(os.path.join(GOLDEN, "usage_qkv_q_slice.json")))
     wl = W.custom([3, 5, 2], [0, 1, 0], K=16, N=128, H=3 * 128, off=g["slice_offset"], L=2,
                   add=g["add_inputs"], seed=6)

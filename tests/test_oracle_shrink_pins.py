@@ -3,7 +3,8 @@ outside the oracle itself.
 
 The expand page ("Implementation: Predibase Lorax SGMV Expand Slice Kernel",
 I/O Contract, Inputs; Usage Examples) describes its ``inputs`` as the
-low-rank activations of the LoRA A projection, packed across sequences.  The
+rank-sized activations the A-side LoRA projection produces for every token of
+every sequence.  The
 readings (lora_A stacked (lora_num, rank, hidden); y = scale * x A[a]^T per
 active segment row; float32 inputs rounded to the weight dtype; inactive rows
 untouched) are pinned here by
