@@ -171,6 +171,22 @@ def test_strided_chunks_several_per_workgroup():
     run_and_check(wl)
 
 
+
+@pytest.mark.parametrize("dts", DTYPES)
+def test_rank16_pipeline_several_units_and_adapter_changes(dts):
+    # Rank <= 16 on contiguous rows keeps two units of loads in flight; here
+    # workgroups hold several units each and the adapter (so the weight tile)
+    # changes inside their chunks.
+    rng = np.random.default_rng(77)
+    B = 180
+    lens = rng.integers(100, 300, size=B)
+    idx = rng.integers(-1, 6, size=B)
+    x, w, o = dts
+    wl = W.custom(lens.tolist(), idx.tolist(), K=16, N=512, H=544, off=16, L=6,
+                  x_dtype=x, w_dtype=w, out_dtype=o, add=True, seed=77)
+    assert wl.T > 30000
+    run_and_check(wl)
+
 @pytest.mark.parametrize("add", [False, True])
 @pytest.mark.parametrize("dts", DTYPES)
 def test_integer_cases_bit_exact(add, dts):
