@@ -425,8 +425,16 @@ __device__ __forceinline__ void unit_range(const P& p, uint32_t U, uint32_t* beg
   *end = *begin + q + (lw < r ? 1 : 0);
 }
 
-// Largest b in [0, n) with table[b] <= key (table non-decreasing, table[0] = 0).
+// Largest b in [0, n) with table[b] <= key (table non-decreasing, table[0] =
+// 0).  Wave-uniform; called with every lane of the wave active.  Up to 64
+// entries: one LDS read per lane and a ballot (the entries <= key are a
+// prefix of the table), else a binary search.
 __device__ __forceinline__ int last_at_most(const int32_t* table, int n, int32_t key) {
+  if (n <= 64) {
+    const int l = threadIdx.x & 63;
+    const bool le = l < n && table[l] <= key;
+    return __builtin_popcountll(__ballot(le)) - 1;
+  }
   int lo = 0, hi = n;  // answer in [lo, hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
