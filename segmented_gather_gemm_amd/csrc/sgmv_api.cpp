@@ -223,23 +223,28 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
       fast_shapes = false;
   }
   const bool fast = fast_shapes && fast_rank(K);
-  // Per-token calls always order tokens by adapter (when it is cheap enough):
-  // neighbours that share an adapter then share its weight tiles; the fast
-  // kernels then also gather each adapter's tokens into common row tiles,
-  // when T rows of the inputs and of the output span less than 2 GiB (32-bit
-  // row offsets).
-  const bool sort = (per_token || batches >= kSortMinBatches) && batches <= kSortMaxBatches &&
-                    L <= (1 << 22);
-  bool gather = fast && per_token && sort && out.rows * p.out_row_bytes < (int64_t(1) << 31);
+  // Per-token calls on the fast kernels gather each adapter's tokens into
+  // common row tiles (one weight tile and one MFMA pass for up to 16 tokens)
+  // when they are few enough for the gathered table in LDS and T rows of the
+  // inputs and of the output span less than 2 GiB (32-bit row offsets).
+  // Otherwise per-token calls, and calls of many segments, order the
+  // segment table by adapter (when it is cheap enough), so that neighbours
+  // that share an adapter share its weight tiles.
+  bool gather = fast && per_token && batches <= kGatherMaxTokens && L <= kGatherMaxAdapters &&
+                out.rows * p.out_row_bytes < (int64_t(1) << 31);
   for (int i = 0; i < num_slices && gather; ++i)
     if (out.rows * p.s[i].x_row_bytes >= (int64_t(1) << 31)) gather = false;
+  const bool sort = !gather && (per_token || batches >= kSortMinBatches) &&
+                    batches <= kSortMaxBatches && L <= (1 << 22);
   p.sort_slots = sort;
   p.gather = gather;
   const void* kernel =
       pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast, gather);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no kernel for this dtype combination");
 
-  const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);  // segment table
+  // segment table, or the gathered table
+  const size_t lds =
+      (size_t)(gather ? batches + 2 * L + 1 : 4 * batches + 1) * sizeof(int32_t);
   int capacity = 0;
   hipError_t e = device_capacity(kernel, lds, &capacity);
   if (e != hipSuccess)

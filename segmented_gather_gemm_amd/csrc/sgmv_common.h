@@ -236,6 +236,76 @@ __device__ __forceinline__ SegTable seg_table(int32_t* lds, int batches) {
   return t;
 }
 
+// Exclusive prefix sum of v[0 .. n) in place (all NT threads take part, v
+// written before the call is visible to them; wave_total holds NT / 64
+// words); returns the total (wave-uniform).
+template <int NT>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t* v, int n, int32_t* wave_total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t carry = 0;
+  for (int base = 0; base < n; base += NT) {
+    const int i = base + tid;
+    const int32_t x = i < n ? v[i] : 0;
+    const int32_t incl = wave_inclusive_sum(x);
+    if (lane == 63) wave_total[wave] = incl;
+    __syncthreads();
+    int32_t before = carry, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      const int32_t s = wave_total[w];
+      before += w < wave ? s : 0;
+      all += s;
+    }
+    if (i < n) v[i] = before + incl - x;
+    carry += all;
+    __syncthreads();
+  }
+  return uniform(carry);
+}
+
+// Table of a per-token call whose row tiles gather the tokens of one adapter
+// (up to 16 per tile, in token order): the adapter of every token (-1: none
+// or out of range), each adapter's token count and the exclusive prefix of
+// its tile counts.  B + 2 L + 1 words of LDS.
+struct GatherTable {
+  int32_t* tok_a;    // [B]
+  int32_t* a_tiles;  // [L + 1] first row tile of adapter a; a_tiles[L] = row tiles
+  int32_t* a_count;  // [L] tokens of adapter a
+};
+
+__device__ __forceinline__ GatherTable gather_table(int32_t* lds, int batches, int adapters) {
+  GatherTable t;
+  t.tok_a = lds;
+  t.a_tiles = lds + batches;
+  t.a_count = t.a_tiles + adapters + 1;
+  return t;
+}
+
+// Fill the gathered table (all kThreads threads take part): count each
+// adapter's tokens (LDS atomics: the counts do not depend on their order),
+// then the tile prefix.  Returns the number of row tiles (wave-uniform).
+template <typename P>
+__device__ __forceinline__ int32_t build_gather_table(const P& p, const GatherTable& gt,
+                                                      int32_t* wave_total) {
+  const int tid = threadIdx.x;
+  const int B = p.batches, L = p.L;
+  for (int a = tid; a < L; a += kThreads) gt.a_count[a] = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += kThreads) {
+    const int64_t a = p.idx[b];
+    const bool active = a >= 0 && a < L && b < p.T;
+    gt.tok_a[b] = active ? (int32_t)a : -1;
+    if (active) atomicAdd(&gt.a_count[a], 1);
+  }
+  __syncthreads();
+  for (int a = tid; a < L; a += kThreads) gt.a_tiles[a] = (gt.a_count[a] + kTileRows - 1) / kTileRows;
+  __syncthreads();
+  const int32_t total = block_exclusive_scan<kThreads>(gt.a_tiles, L, wave_total);
+  if (tid == 0) gt.a_tiles[L] = total;
+  __syncthreads();
+  return total;
+}
+
 
 // Fill the table (all NT threads of the workgroup take part; wave_total
 // holds NT / 64 words) with row tiles of `tile_rows` rows; returns the total
@@ -246,7 +316,6 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
                                                     int32_t* wave_total,
                                                     int32_t tile_rows = kTileRows) {
   constexpr int kThreads = NT;         // shadows the default block size below
-  constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -320,40 +389,6 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
         tab.seg_lora[slot[i]] = a32[i] < 0 ? 0 : a32[i];
       }
     }
-    if (p.gather) {
-      // Per-token table ordered by adapter: cut the active slots (first in
-      // the order) into row tiles of up to 16 slots that share an adapter,
-      // starting a new tile at every adapter change and every 16th slot.  A
-      // tile's first slot gets one row tile and seg_end = its one-past-last
-      // slot; the other slots get none; seg_row keeps every slot's token row.
-      // A wave holds 64 consecutive slots, so a tile never leaves its wave.
-      __syncthreads();
-      int32_t tiles_g[kPer], end_g[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int sl = tid + i * kThreads;
-        const bool act = sl < B && tab.tile_start[sl] > 0;
-        const bool first = act && ((sl & 15) == 0 || tab.seg_lora[sl] != tab.seg_lora[sl - 1]);
-        const uint64_t starts = __ballot(first);
-        const uint64_t actives = __ballot(act);
-        // next tile start or inactive slot after this lane, else the end of
-        // its 16-slot block
-        const uint64_t stop = (starts | ~actives) & ~((2ull << lane) - 1);
-        const int block_end = (lane & ~15) + 16;
-        const int next = stop ? __builtin_ctzll(stop) : 64;
-        end_g[i] = (sl - lane) + (next < block_end ? next : block_end);
-        tiles_g[i] = first ? 1 : 0;
-      }
-      __syncthreads();  // every neighbour read before the counts change
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int sl = tid + i * kThreads;
-        if (sl < B) {
-          tab.tile_start[sl] = tiles_g[i];
-          tab.seg_end[sl] = tiles_g[i] ? end_g[i] : 0;
-        }
-      }
-    }
   } else if (B <= 64) {
     // Index order, every segment in one lane of wave 0: the tile counts are
     // scanned in registers and the table is complete after one barrier.
@@ -383,27 +418,10 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
   }
   __syncthreads();
   // Second pass: exclusive prefix sum of the tile counts over table slots.
-  int32_t carry = 0;
-  for (int base = 0; base < B; base += kThreads) {
-    const int i = base + tid;
-    const int32_t tiles = i < B ? tab.tile_start[i] : 0;
-    const int32_t incl = wave_inclusive_sum(tiles);
-    if (lane == 63) wave_total[wave] = incl;
-    __syncthreads();
-    int32_t before = carry, all = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int32_t s = wave_total[w];
-      before += w < wave ? s : 0;
-      all += s;
-    }
-    if (i < B) tab.tile_start[i] = before + incl - tiles;
-    carry += all;
-    __syncthreads();
-  }
-  if (tid == 0) tab.tile_start[B] = carry;
+  const int32_t total = block_exclusive_scan<kThreads>(tab.tile_start, B, wave_total);
+  if (tid == 0) tab.tile_start[B] = total;
   __syncthreads();
-  return uniform(carry);
+  return total;
 }
 
 // The scheduler's arithmetic is 32-bit: unit counts, unit indices and

@@ -173,7 +173,9 @@ struct FastUnit {
 template <bool GATHER>
 struct Walk {
   const Params& p;
-  const SegTable& tab;
+  const SegTable& tab;      // segment tiles (not GATHER)
+  const GatherTable& gt;    // gathered tiles (GATHER)
+  int32_t* rows;            // GATHER: this wave's 16 token rows of the current tile
   int32_t RT;       // row tiles
   int wave;
   int ob;           // bytes per output element
@@ -181,7 +183,7 @@ struct Walk {
   int gi, tile_lo, tile_hi;   // column group and its tiles [lo, hi)
   int32_t band_lo, band_hi;   // band's row tiles [lo, hi)
   int band_b;                 // segment holding band_lo
-  int tile, si, b;
+  int tile, si, b;           // b: table slot, or (GATHER) the tile's adapter
   int32_t rt;
   int32_t seg_tile_end;       // first row tile after segment b
   // run state for (tile, b) at row tile rt
@@ -198,21 +200,41 @@ struct Walk {
 
   // Table slot holding row tile r, searching forward from slot `from` (a slot
   // at or before it).  Slots without tiles come before the slot that holds
-  // the tile, so the last slot whose prefix is <= r is the one.  Gathered
-  // tables have many tile-less slots: a binary search there.
+  // the tile, so the last slot whose prefix is <= r is the one.
   __device__ __forceinline__ int slot_of(int32_t r, int from) const {
-    if constexpr (GATHER) {
-      return last_at_most(tab.tile_start, p.batches + 1, r);
-    } else {
-      int s = from;
-      while (uniform(tab.tile_start[s + 1]) <= r) ++s;
-      return s;
+    int s = from;
+    while (uniform(tab.tile_start[s + 1]) <= r) ++s;
+    return s;
+  }
+
+  // GATHER: the adapter whose tiles hold row tile r (adapters without tokens
+  // share the prefix of the next one, so the last prefix <= r is the owner).
+  __device__ __forceinline__ int adapter_of(int32_t r) const {
+    return last_at_most(gt.a_tiles, p.L + 1, r);
+  }
+
+  // GATHER: rows of tokens 16 k .. 16 k + 15 of adapter a, in token order,
+  // into rows[0 ..): one ballot per 64 tokens of the table.
+  __device__ __forceinline__ void fetch_rows(int a, int32_t k) const {
+    const int lane = threadIdx.x & 63;
+    const int32_t lo = kTileRows * k, hi = lo + kTileRows;
+    int32_t seen = 0;
+    for (int c = 0; c < p.batches && seen < hi; c += 64) {
+      const int t = c + lane;
+      const bool m = t < p.batches && gt.tok_a[t] == a;
+      const uint64_t mask = __ballot(m);
+      const int32_t r = seen + (int32_t)__builtin_amdgcn_mbcnt_hi(
+                                   (uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+      if (m && r >= lo && r < hi) rows[r - lo] = t;
+      seen += (int32_t)__builtin_popcountll(mask);
     }
   }
 
-  __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, int32_t rt_total,
-                                  int wave_, int ob_, uint32_t u)
-      : p(p_), tab(t), RT(rt_total), wave(wave_), ob(ob_) {
+  __device__ __forceinline__ Walk(const Params& p_, const SegTable& t, const GatherTable& g,
+                                  int32_t* rows_, int32_t rt_total, int wave_, int ob_,
+                                  uint32_t u)
+      : p(p_), tab(t), gt(g), rows(rows_), RT(rt_total), wave(wave_), ob(ob_) {
     seek(u);
   }
 
@@ -254,8 +276,12 @@ struct Walk {
     const uint32_t wq = w / rb;
     tile = tile_lo + (int)wq;
     rt = band_lo + (int32_t)(w - wq * rb);
-    band_b = last_at_most(tab.tile_start, p.batches + 1, band_lo);
-    b = slot_of(rt, band_b);
+    if constexpr (GATHER) {
+      b = adapter_of(rt);
+    } else {
+      band_b = last_at_most(tab.tile_start, p.batches + 1, band_lo);
+      b = slot_of(rt, band_b);
+    }
     si = slice_of(p, tile);
     new_run();
   }
@@ -266,13 +292,16 @@ struct Walk {
     const int64_t n_left = S.n - col0;
     n_rem = n_left <= 0 ? 0 : (n_left > kWaveCols ? kWaveCols : (int32_t)n_left);
     if constexpr (GATHER) {
-      // slot b opens a gathered tile of slots [b, seg_end[b]); each lane
-      // finds its token row in seg_row (see the fast kernel)
-      rows_left = uniform(tab.seg_end[b]) - b;
-      a = uniform(tab.seg_lora[b]);
+      // row tile rt is tile k of adapter b; each lane takes its token's row
+      // from rows (see the fast kernel)
+      const int32_t k = rt - uniform(gt.a_tiles[b]);
+      const int32_t left = uniform(gt.a_count[b]) - kTileRows * k;
+      rows_left = left < kTileRows ? left : kTileRows;
+      a = b;
       seg_tile_end = rt + 1;
       x_row = static_cast<const char*>(S.x);
       o_row = static_cast<const char*>(p.out) + (S.offset + col0) * ob;
+      fetch_rows(b, k);
       return;
     }
     const int64_t seg_row = uniform(tab.seg_row[b]);
@@ -302,15 +331,15 @@ struct Walk {
         }
         band_hi = band_lo + p.band_tiles < RT ? band_lo + p.band_tiles : RT;
         tile = tile_lo;
-        band_b = slot_of(band_lo, b);
+        if constexpr (!GATHER) band_b = slot_of(band_lo, b);
       }
       rt = band_lo;
-      b = band_b;
+      b = GATHER ? adapter_of(rt) : band_b;
       si = slice_of(p, tile);
       new_run();
     } else if (rt == seg_tile_end) {
       if constexpr (GATHER) {
-        b = uniform(tab.seg_end[b]);  // the next tile opens where this one ends
+        while (uniform(gt.a_tiles[b + 1]) <= rt) ++b;  // the next tile's adapter
       } else {
         ++b;
         while (uniform(tab.tile_start[b + 1]) <= rt) ++b;
@@ -352,10 +381,15 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   constexpr int kSteps = FastShape<KS>::kSteps;
   constexpr bool kShareX = FastShape<KS>::kShareX;
   prefetch_params(p);
-  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
+  // segment table, 4 * batches + 1 words, or (GATHER) the gathered table,
+  // batches + 2 L + 1 words
+  extern __shared__ __align__(16) int32_t lds[];
   __shared__ int32_t wave_total[kWaves];
   const SegTable tab = seg_table(lds, p.batches);
-  const int32_t RT = build_tile_table(p, tab, wave_total);
+  const GatherTable gt = gather_table(lds, p.batches, p.L);
+  int32_t RT;
+  if constexpr (GATHER) RT = build_gather_table(p, gt, wave_total);
+  else RT = build_tile_table(p, tab, wave_total);
   const uint32_t U = (uint32_t)RT * (uint32_t)p.total_tiles;
   if (U == 0) return;
 
@@ -468,7 +502,8 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     x_si = si;
   };
 
-  Walk<GATHER> pos(p, tab, RT, wave, ob, c_start);
+  __shared__ int32_t tile_rows[GATHER ? kWaves : 1][kTileRows];  // GATHER: token rows per wave
+  Walk<GATHER> pos(p, tab, gt, tile_rows[GATHER ? wave : 0], RT, wave, ob, c_start);
   pos.c_left = c_len - 1;
   pos.next_off = next_off;
   pos.g_base = g_base;
@@ -486,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
     if constexpr (GATHER) {
       // Token j of the tile: this lane's row (the host keeps T rows of x and
       // of the output within 2 GiB, so row offsets fit 32 bits).
-      const int64_t row = j < pos.rows_left ? tab.seg_row[pos.b + j] : -1;
+      const int64_t row = j < pos.rows_left ? pos.rows[j] : -1;
       u.lx = row >= 0 ? (uint32_t)(row * p.s[pos.si].x_row_bytes) : kOut;
       u.lo = row >= 0 ? (uint32_t)(row * p.out_row_bytes) : kOut;
       u.x = make_rsrc(pos.x_row, p.T * p.s[pos.si].x_row_bytes);

@@ -19,6 +19,11 @@ constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk or
 // ordering costs O(batches^2 / threads) per workgroup.
 constexpr int kSortMinBatches = 128;
 constexpr int kSortMaxBatches = 512;
+// Per-token calls gather each adapter's tokens into row tiles for up to this
+// many tokens and adapters (the gathered table: tokens + 2 adapters + 1 LDS
+// words; each unit's decode scans the tokens once).
+constexpr int kGatherMaxTokens = 512;
+constexpr int kGatherMaxAdapters = 1024;
 static_assert(kSortMaxBatches % kThreads == 0 && kSortMaxBatches <= 512,
               "segments per thread when ordering; 9-bit segment index in the sort key");
 
@@ -58,7 +63,7 @@ struct Params {
   int32_t chunk_units;  // fast kernels: units per chunk of the strided assignment
   int32_t sort_slots;   // order the segment table by adapter (batches <= kSortMaxBatches)
   int32_t per_token;    // segment b is row b alone (start and lens unused)
-  int32_t gather;       // per-token table cut into gathered row tiles (fast kernels <..., true>)
+  int32_t gather;       // gathered per-token row tiles (fast kernels <..., true>)
   SliceDesc s[kMaxSlices];
 };
 
