@@ -39,6 +39,7 @@ constexpr int32_t kChunkUnits = SGMV_CHUNK_UNITS;
 #define SGMV_UNITS_PER_WORKGROUP 3
 #endif
 constexpr int64_t kUnitsPerWorkgroup = SGMV_UNITS_PER_WORKGROUP;
+static_assert(sgmv::kGatherMaxTokens == SGMV_MAX_BATCHES, "every per-token call can gather");
 static_assert(kChunkUnits >= 1 && kBandTiles % kChunkUnits == 0,
               "chunks must not straddle a column tile's run of a band");
 

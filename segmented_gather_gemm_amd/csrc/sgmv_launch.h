@@ -20,9 +20,11 @@ constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk or
 constexpr int kSortMinBatches = 128;
 constexpr int kSortMaxBatches = 512;
 // Per-token calls gather each adapter's tokens into row tiles for up to this
-// many tokens and adapters (the gathered table: tokens + 2 adapters + 1 LDS
-// words; each unit's decode scans the tokens once).
-constexpr int kGatherMaxTokens = 512;
+// many tokens (every per-token call the ABI accepts, SGMV_MAX_BATCHES) and
+// adapters (the gathered table: tokens + 2 adapters + 1 LDS words; each
+// unit's decode scans the tokens once).  Measured on q_proj shapes with 32
+// adapters, gathering beats one-token tiles 3-3.6x from 1024 to 4000 tokens.
+constexpr int kGatherMaxTokens = 4000;
 constexpr int kGatherMaxAdapters = 1024;
 static_assert(kSortMaxBatches % kThreads == 0 && kSortMaxBatches <= 512,
               "segments per thread when ordering; 9-bit segment index in the sort key");
