@@ -58,10 +58,12 @@ def test_bgmv_all_tokens_without_adapter_touch_nothing():
     assert np.array_equal(out, wl.out0)
 
 
-@pytest.mark.parametrize("T,L", [(256, 1023), (400, 1200), (512, 2)])
+@pytest.mark.parametrize("T,L", [(256, 1023), (300, 1024), (300, 1025), (400, 1200), (512, 2),
+                                 (3000, 7)])
 def test_bgmv_adapter_order_few_and_many_adapters(T, L):
-    # Tokens are ordered by adapter before they are gathered into row tiles;
-    # from two adapters (long runs) to more adapters than tokens.
+    # Up to 1024 adapters the tokens of each adapter are gathered into row
+    # tiles (a table of adapter buckets), past that each token is its own
+    # tile; from two adapters (long runs) to more adapters than tokens.
     rng = np.random.default_rng(T + L)
     idx = rng.integers(-1, L, size=T)
     wl = W.per_token(idx.tolist(), K=16, N=256, H=256, off=0, L=L, add=True, seed=T)
