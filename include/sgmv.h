@@ -148,8 +148,9 @@ sgmv_status sgmv_expand_multi_slice(const sgmv_slice* slices, int num_slices, sg
  * lora_indices  device int64[total_tokens]; read only.  total_tokens =
  *               out.rows <= SGMV_MAX_BATCHES (else SGMV_ERR_UNSUPPORTED).
  *
- * Tokens are processed grouped by adapter (up to 512 tokens), so tokens that
- * share an adapter share its weight tiles.  Returns as sgmv_expand_slice.
+ * Tokens are processed grouped by adapter (up to 16 per group, for up to
+ * 1024 adapters), so tokens that share an adapter share its weight tiles.
+ * Returns as sgmv_expand_slice.
  */
 sgmv_status sgmv_bgmv_expand_slice(sgmv_matrix inputs, sgmv_stack lora_b, sgmv_matrix out,
                                    const int64_t* lora_indices, int64_t slice_offset,
