@@ -195,6 +195,8 @@ SPLIT_T_IDX = [1, 0, 2, -1, 1, 0, 2, 1, -1]
     (96, 256, 1, ("f16", "f16", "f16"), 1.0),      # 16 k tiles
     (40, 8, 3, ("f32", "f16", "f32"), 1.0),
     (128, 64, 5, ("bf16", "bf16", "f32"), 1.0),    # 5 slices: launches of 2 and 3
+    (256, 32, 1, ("bf16", "bf16", "bf16"), 1.0),   # 2 k tiles: one token tile per wave
+    (128, 16, 2, ("f16", "f16", "f16"), 1.0),      # 2 k tiles over two slices
 ])
 def test_shrink_split_t_parity(H, K, slices, dts, scale):
     x_dt, a_dt, o_dt = dts
