@@ -167,8 +167,8 @@ typedef struct {
  * `inputs`.  The page (I/O Contract, Inputs; Usage Examples) describes those
  * inputs as the rank-sized activations the A-side LoRA projection produces
  * for every token of every sequence, (total_tokens, rank); it prints no
- * formula for the projection,
- * so this takes the plainest reading consistent with the expand:
+ * formula for the projection, so this takes the plainest reading consistent
+ * with the expand:
  *
  *     out[t][k] = scale * sum_h inputs[t][h] * lora_a[a][k][h],   k < rank,
  *
