@@ -157,7 +157,8 @@ __device__ __forceinline__ int64_t weight_row(int64_t col0, int s, int j) {
 struct FastUnit {
   rsrc_t x;       // inputs: the tile's valid rows (rows past the segment read zero)
   rsrc_t o;       // output: from (row0, off + col0) to the end of the last valid row's block
-  uint32_t lx, lo;  // gathered tiles: this lane's row offset in x and o (kOut: none)
+  uint32_t lx;     // gathered tiles: this lane's input row offset (kOut: none)
+  uint32_t lro[4]; // gathered tiles: this lane's output offset per row-wise access (kOut: none)
   int32_t a;      // adapter
   int32_t col0;   // first of the wave's 64 columns, within the slice
   int32_t n_rem;  // slice columns left from col0 (<= 0: the wave has none)
@@ -443,27 +444,24 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // Rank step ks covers rank [32 ks, 32 ks + 32); lane group g holds the
   // 8-element block 32 ks + 8 g (the same grouping as the generic kernel, so
   // both give bit-identical results).  Blocks past K read zero.
-  // Loop-invariant lane offsets: output (row j, column group 32 q + 8 g of
-  // the wave's block) and weights (row weight_row(0, s, j) of the tile).
-  uint32_t o_off[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    o_off[q] = (uint32_t)(GATHER ? 0 : j * os_bytes) + (32 * q + 8 * g) * ob;
-  // Output tile of the wave (16 rows x 64 columns) in HBM, for contiguous
-  // rows (not GATHER): accessed row-wise, kLPR lanes per row (a row's 128
+  // Loop-invariant lane offsets of the weights: row weight_row(0, s, j) of
+  // the tile.
+  // Output tile of the wave (16 rows x 64 columns) in HBM: accessed
+  // row-wise, kLPR lanes per row (a row's 128
   // bytes, 256 for float32, in one instruction, against 64 bytes with the
   // accumulator layout), and moved between that layout and the MFMA
   // accumulator layout through a per-wave LDS tile -- 16-byte block b of
   // row r in slot kNB r + (b ^ swizzle(r)), which keeps both the row-wise
   // and the accumulator-layout accesses free of bank conflicts.  Access m
   // covers rows m kRPI .. + kRPI - 1; this lane reads or writes block oblk
-  // of row m kRPI + orow.
+  // of row m kRPI + orow -- at offset oc_off[m] for contiguous rows, or
+  // (GATHER) at the unit's lro[m], from that row's token.
   constexpr int kNB = 64 * ob / 16;           // 16-byte blocks per tile row
   constexpr int kLPR = kNB;
   constexpr int kRPI = 64 / kLPR;
   constexpr int kOAcc = 2 * raw_vecs<OD>();   // row-wise accesses per tile
   static_assert(kOAcc * kRPI == kTileRows, "row-wise accesses cover the tile");
-  __shared__ u32x4 o_lds[GATHER ? 1 : kWaves][GATHER ? 1 : kTileRows * kNB];
+  __shared__ u32x4 o_lds[kWaves][kTileRows * kNB];
   auto o_slot = [](int r, int b) __attribute__((always_inline)) -> int {
     return kNB * r + (b ^ (kNB == 8 ? (r >> 1) : r));
   };
@@ -473,10 +471,17 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   };
   const int orow = lane / kLPR, oblk = lane % kLPR;
   const int ocol = oblk * (16 / ob);          // first column of this lane's block
+  static_assert(kOAcc <= 4, "FastUnit::lro holds the row-wise offsets");
   uint32_t oc_off[kOAcc];
 #pragma unroll
   for (int m = 0; m < kOAcc; ++m)
     oc_off[m] = (uint32_t)((m * kRPI + orow) * os_bytes + oblk * 16);
+  // offset of row-wise access m of unit u; blocks past the slice (only in a
+  // slice's last column tile) take an out-of-range offset, as do rows past
+  // the segment (outside the resource) or past a gathered tile's tokens
+  auto o_at = [&](const FastUnit& u, int m) __attribute__((always_inline)) -> uint32_t {
+    return ocol < u.n_rem ? (GATHER ? u.lro[m] : oc_off[m]) : kOut;
+  };
   auto w_off = [&](int s, int ks) __attribute__((always_inline)) -> uint32_t {
     const int kb = 32 * ks + 8 * g;
     return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
@@ -523,12 +528,18 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
       // of the output within 2 GiB, so row offsets fit 32 bits).
       const int64_t row = j < pos.rows_left ? pos.rows[j] : -1;
       u.lx = row >= 0 ? (uint32_t)(row * p.s[pos.si].x_row_bytes) : kOut;
-      u.lo = row >= 0 ? (uint32_t)(row * p.out_row_bytes) : kOut;
+      // row-wise output accesses: row m kRPI + orow of the tile, block oblk
+#pragma unroll
+      for (int m = 0; m < kOAcc; ++m) {
+        const int r = m * kRPI + orow;
+        u.lro[m] = r < pos.rows_left ? (uint32_t)(pos.rows[r] * p.out_row_bytes) + oblk * 16
+                                     : kOut;
+      }
       u.x = make_rsrc(pos.x_row, p.T * p.s[pos.si].x_row_bytes);
       u.o = make_rsrc(pos.o_row,
                       u.n_rem > 0 ? (p.T - 1) * p.out_row_bytes + (int64_t)u.n_rem * ob : 0);
     } else {
-      u.lx = u.lo = 0;
+      u.lx = 0;
       u.x = make_rsrc(pos.x_row, rows * p.s[pos.si].x_row_bytes);
       u.o = make_rsrc(pos.o_row,
                       u.n_rem > 0 ? (rows - 1) * p.out_row_bytes + (int64_t)u.n_rem * ob : 0);
@@ -550,16 +561,12 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
       if (x_chunk(i) < kSteps) buf_load8<XD>(u.x, u.lx + x_off[i], &st.x[i * raw_vecs<XD>()]);
-    if constexpr (ADD && GATHER) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) buf_load8<OD>(u.o, u.lo + o_off[q], &st.o[q * raw_vecs<OD>()]);
-    } else if constexpr (ADD) {
+    if constexpr (ADD) {
       // prior output, row-wise (st.o[m] = access m)
 #pragma unroll
       for (int m = 0; m < kOAcc; ++m)
         st.o[m] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.o, ocol < u.n_rem ? oc_off[m] : kOut,
-                                                         0, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(u.o, o_at(u, m), 0, 0));
     }
   };
   // Publish this wave's chunks of a unit's input tile to LDS buffer `buf`
@@ -577,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   auto compute_store = [&](const Stage<XD, OD, KS>& st, const u32x4 (&w)[4][kSteps],
                            const FastUnit& u, int buf) __attribute__((always_inline)) {
     f32x4 acc[4];
-    if constexpr (ADD && !GATHER) {
+    if constexpr (ADD) {
       // row-wise prior output -> the wave's LDS tile -> accumulator layout
 #pragma unroll
       for (int m = 0; m < kOAcc; ++m) o_lds[wave][o_slot(m * kRPI + orow, oblk)] = st.o[m];
@@ -585,9 +592,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if constexpr (ADD && GATHER) {
-        out_values<OD>(&st.o[q * raw_vecs<OD>()], v);
-      } else if constexpr (ADD) {
+      if constexpr (ADD) {
         u32x4 raw[raw_vecs<OD>()];
 #pragma unroll
         for (int rv = 0; rv < raw_vecs<OD>(); ++rv) raw[rv] = o_lds[wave][o_slot(j, acc_blk(q, rv))];
@@ -611,25 +616,14 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
                           acc[2 * q + 1][3]};
       u32x4 raw[raw_vecs<OD>()];
       out_pack<OD>(v, raw);
-      if constexpr (GATHER) {
-        // Column groups past the slice (only in a slice's last column tile)
-        // take an out-of-range offset; rows past the segment already lie
-        // outside the resource.
-        const uint32_t off = 32 * q + 8 * g < u.n_rem ? u.lo + o_off[q] : kOut;
-        buf_store8<OD, kStream>(u.o, off, raw);
-      } else {
 #pragma unroll
-        for (int rv = 0; rv < raw_vecs<OD>(); ++rv) o_lds[wave][o_slot(j, acc_blk(q, rv))] = raw[rv];
-      }
+      for (int rv = 0; rv < raw_vecs<OD>(); ++rv) o_lds[wave][o_slot(j, acc_blk(q, rv))] = raw[rv];
     }
-    if constexpr (!GATHER) {
-      // the wave's LDS tile -> row-wise stores (same column and row clamps)
+    // the wave's LDS tile -> row-wise stores (same column and row clamps)
 #pragma unroll
-      for (int m = 0; m < kOAcc; ++m)
-        __builtin_amdgcn_raw_buffer_store_b128(o_lds[wave][o_slot(m * kRPI + orow, oblk)], u.o,
-                                               ocol < u.n_rem ? oc_off[m] : kOut, 0,
-                                               kStream);
-    }
+    for (int m = 0; m < kOAcc; ++m)
+      __builtin_amdgcn_raw_buffer_store_b128(o_lds[wave][o_slot(m * kRPI + orow, oblk)], u.o,
+                                             o_at(u, m), 0, kStream);
   };
 
   // Software pipeline (see the file comment).  wA holds the weight tile of
