@@ -103,6 +103,27 @@ def _load_library() -> ctypes.CDLL:
 
 lib = _load_library()
 
+import torch as _torch  # noqa: E402  (loaded by _load_library before the library)
+
+_DTYPE_CODES = {_torch.float16: 0, _torch.bfloat16: 1, _torch.float32: 2}
+# The current stream's raw handle without building a Stream object (a
+# measurable part of a call's host time); the public route where absent.
+_RAW_STREAM = getattr(_torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(device.index)
+    return _torch.cuda.current_stream(device).cuda_stream
+
+
+def _call_on(device, fn, *args):
+    """fn(*args) with `device` current (made current only when it is not)."""
+    if _torch.cuda.current_device() == device.index:
+        return fn(*args)
+    with _torch.cuda.device(device):
+        return fn(*args)
+
 
 class SgmvError(RuntimeError):
     """A HIP runtime failure reported by libsgmv."""
@@ -118,20 +139,21 @@ def _raise(status: int):
 
 
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
-    if t.dtype not in codes:
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return code
 
 
 def _matrix(t, what: str) -> Matrix:
-    if t.dim() != 2:
-        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    shape = t.shape
+    if len(shape) != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(shape)}")
+    rows, cols = shape
+    s0, s1 = t.stride()
+    if cols > 1 and s1 != 1:
         raise ValueError(f"{what} must have unit column stride")
-    return Matrix(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1],
-                  t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0)))
+    return Matrix(t.data_ptr(), _dtype_code(t), rows, cols, s0 if rows > 1 else max(cols, s0))
 
 
 def _stack(w, what: str) -> Stack:
@@ -139,32 +161,22 @@ def _stack(w, what: str) -> Stack:
         if w.shape[1] != 1:
             raise ValueError(f"{what}: a 4-D lora_b must be (lora_num, 1, slice_size, rank)")
         w = w.squeeze(1)
-    if w.dim() != 3:
-        raise ValueError(f"{what} must be (lora_num, slice_size, rank), got {tuple(w.shape)}")
+    shape = w.shape
+    if len(shape) != 3:
+        raise ValueError(f"{what} must be (lora_num, slice_size, rank), got {tuple(shape)}")
     if not w.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
-    return Stack(w.data_ptr(), _dtype_code(w), w.shape[0], w.shape[1], w.shape[2])
+    return Stack(w.data_ptr(), _dtype_code(w), shape[0], shape[1], shape[2])
 
 
 def _meta(t, what: str, device):
-    import torch
     if t.dim() != 1:
         raise ValueError(f"{what} must be 1-D")
     if t.device != device:
         raise ValueError(f"{what} must be on {device}")
-    if t.dtype != torch.int64 or not t.is_contiguous():
-        t = t.to(torch.int64).contiguous()   # documented marshalling copy
+    if t.dtype is not _torch.int64 or not t.is_contiguous():
+        t = t.to(_torch.int64).contiguous()   # documented marshalling copy
     return t
-
-
-def _on_device(device):
-    """Context that makes `device` current for the launch (a no-op when it
-    already is)."""
-    import contextlib
-    import torch
-    if torch.cuda.current_device() == device.index:
-        return contextlib.nullcontext()
-    return torch.cuda.device(device)
 
 
 def _common(output_tensor, metas):
@@ -181,23 +193,21 @@ def sgmv_expand_slice(inputs, lora_b_weights, output_tensor, b_seq_start_loc, se
     """In place: output_tensor[start_b + m, slice_offset:slice_offset + slice_size]
     (+)= inputs[start_b + m] @ lora_b_weights[lora_indices[b]].T for every
     segment b with index != -1.  Enqueued on the current stream."""
-    import torch
     device, (start, lens, idx) = _common(output_tensor, [
         (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
         (lora_indices_tensor, "lora_indices_tensor")])
     for t, n in ((inputs, "inputs"), (lora_b_weights, "lora_b_weights")):
         if t.device != device:
             raise ValueError(f"{n} must be on {device}")
-    if len(start) < batches or len(lens) < batches or len(idx) < batches:
+    if start.shape[0] < batches or lens.shape[0] < batches or idx.shape[0] < batches:
         raise ValueError("segment metadata shorter than batches")
     x = _matrix(inputs, "inputs")
     w = _stack(lora_b_weights, "lora_b_weights")
     out = _matrix(output_tensor, "output_tensor")
-    stream = torch.cuda.current_stream(device).cuda_stream
-    with _on_device(device):
-        st = lib.sgmv_expand_slice(x, w, out, start.data_ptr(), lens.data_ptr(), idx.data_ptr(),
-                                   int(batches), int(max_seq_length), int(slice_offset),
-                                   int(slice_size), int(bool(add_inputs)), stream)
+    stream = _stream(device)
+    st = _call_on(device, lib.sgmv_expand_slice, x, w, out, start.data_ptr(), lens.data_ptr(),
+                  idx.data_ptr(), int(batches), int(max_seq_length), int(slice_offset),
+                  int(slice_size), int(bool(add_inputs)), stream)
     if st != SGMV_OK:
         _raise(st)
     return output_tensor
@@ -211,13 +221,12 @@ def sgmv_expand_multi_slice(slices: Sequence[Tuple[object, object, int]], output
     ``slices``: sequence of (inputs, lora_b_weights, slice_offset); each
     slice's size is its lora_b_weights.size(-2).  Bit-identical to one
     sgmv_expand_slice call per slice."""
-    import torch
     if not 1 <= len(slices) <= MAX_SLICES:
         raise ValueError(f"1..{MAX_SLICES} slices, got {len(slices)}")
     device, (start, lens, idx) = _common(output_tensor, [
         (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
         (lora_indices_tensor, "lora_indices_tensor")])
-    if len(start) < batches or len(lens) < batches or len(idx) < batches:
+    if start.shape[0] < batches or lens.shape[0] < batches or idx.shape[0] < batches:
         raise ValueError("segment metadata shorter than batches")
     arr = (SliceDesc * len(slices))()
     for i, (x, w, off) in enumerate(slices):
@@ -226,11 +235,10 @@ def sgmv_expand_multi_slice(slices: Sequence[Tuple[object, object, int]], output
         st = _stack(w, f"slice {i} lora_b")
         arr[i] = SliceDesc(_matrix(x, f"slice {i} inputs"), st, int(off), st.rows)
     out = _matrix(output_tensor, "output_tensor")
-    stream = torch.cuda.current_stream(device).cuda_stream
-    with _on_device(device):
-        rc = lib.sgmv_expand_multi_slice(arr, len(slices), out, start.data_ptr(), lens.data_ptr(),
-                                         idx.data_ptr(), int(batches), int(max_seq_length),
-                                         int(bool(add_inputs)), stream)
+    stream = _stream(device)
+    rc = _call_on(device, lib.sgmv_expand_multi_slice, arr, len(slices), out, start.data_ptr(),
+                  lens.data_ptr(), idx.data_ptr(), int(batches), int(max_seq_length),
+                  int(bool(add_inputs)), stream)
     if rc != SGMV_OK:
         _raise(rc)
     return output_tensor
@@ -241,20 +249,18 @@ def bgmv_expand_slice(inputs, lora_b_weights, output_tensor, lora_indices_tensor
     """Per-token form: output_tensor[t, slice_offset:slice_offset + slice_size]
     (+)= inputs[t] @ lora_b_weights[lora_indices[t]].T for every token t with
     index != -1.  Enqueued on the current stream."""
-    import torch
     device, (idx,) = _common(output_tensor, [(lora_indices_tensor, "lora_indices_tensor")])
     for t, n in ((inputs, "inputs"), (lora_b_weights, "lora_b_weights")):
         if t.device != device:
             raise ValueError(f"{n} must be on {device}")
-    if len(idx) < output_tensor.shape[0]:
+    if idx.shape[0] < output_tensor.shape[0]:
         raise ValueError("lora_indices_tensor shorter than the number of tokens")
     x = _matrix(inputs, "inputs")
     w = _stack(lora_b_weights, "lora_b_weights")
     out = _matrix(output_tensor, "output_tensor")
-    stream = torch.cuda.current_stream(device).cuda_stream
-    with _on_device(device):
-        st = lib.sgmv_bgmv_expand_slice(x, w, out, idx.data_ptr(), int(slice_offset),
-                                        int(slice_size), int(bool(add_inputs)), stream)
+    stream = _stream(device)
+    st = _call_on(device, lib.sgmv_bgmv_expand_slice, x, w, out, idx.data_ptr(),
+                  int(slice_offset), int(slice_size), int(bool(add_inputs)), stream)
     if st != SGMV_OK:
         _raise(st)
     return output_tensor
@@ -285,13 +291,12 @@ def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_s
     """Several LoRA-A projections of the same inputs (e.g. Q, K, V) reading
     the inputs once.  ``slices``: sequence of (lora_a_weights, output_tensor).
     Bit-identical to one sgmv_shrink call per slice."""
-    import torch
     if not 1 <= len(slices) <= MAX_SLICES:
         raise ValueError(f"1..{MAX_SLICES} slices, got {len(slices)}")
     device, (start, lens, idx) = _common(inputs, [
         (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
         (lora_indices_tensor, "lora_indices_tensor")])
-    if len(start) < batches or len(lens) < batches or len(idx) < batches:
+    if start.shape[0] < batches or lens.shape[0] < batches or idx.shape[0] < batches:
         raise ValueError("segment metadata shorter than batches")
     arr = (ShrinkSliceDesc * len(slices))()
     for i, (w, o) in enumerate(slices):
@@ -299,11 +304,10 @@ def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_s
             raise ValueError(f"slice {i} must be on {device}")
         arr[i] = ShrinkSliceDesc(_stack_a(w, f"slice {i} lora_a"), _matrix(o, f"slice {i} output"))
     x = _matrix(inputs, "inputs")
-    stream = torch.cuda.current_stream(device).cuda_stream
-    with _on_device(device):
-        rc = lib.sgmv_shrink_multi_slice(x, arr, len(slices), start.data_ptr(), lens.data_ptr(),
-                                         idx.data_ptr(), int(batches), int(max_seq_length),
-                                         float(scaling), stream)
+    stream = _stream(device)
+    rc = _call_on(device, lib.sgmv_shrink_multi_slice, x, arr, len(slices), start.data_ptr(),
+                  lens.data_ptr(), idx.data_ptr(), int(batches), int(max_seq_length),
+                  float(scaling), stream)
     if rc != SGMV_OK:
         _raise(rc)
     return [o for _, o in slices]
