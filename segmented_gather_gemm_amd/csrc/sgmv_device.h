@@ -447,12 +447,14 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   // Loop-invariant lane offsets of the weights: row weight_row(0, s, j) of
   // the tile.
   // Output tile of the wave (16 rows x 64 columns) in HBM: accessed
-  // row-wise, kLPR lanes per row (a row's 128
-  // bytes, 256 for float32, in one instruction, against 64 bytes with the
-  // accumulator layout), and moved between that layout and the MFMA
-  // accumulator layout through a per-wave LDS tile -- 16-byte block b of
-  // row r in slot kNB r + (b ^ swizzle(r)), which keeps both the row-wise
-  // and the accumulator-layout accesses free of bank conflicts.  Access m
+  // row-wise, kLPR lanes per row (a row's 128 bytes, 256 for float32, in one
+  // instruction, against 64 bytes with the accumulator layout), and moved
+  // between that layout and the MFMA accumulator layout through a per-wave
+  // LDS tile: 16-byte block b of row r in slot kNB r + (b ^ (r mod kNB)).
+  // The LDS serves a 16-byte access 8 lanes at a time, free of bank
+  // conflicts when they hit 8 slot classes mod 8: the 8 lanes of a row-wise
+  // access share a row (blocks b ^ const), those of the accumulator layout
+  // share a block over 8 consecutive rows (r mod 8 differs).  Access m
   // covers rows m kRPI .. + kRPI - 1; this lane reads or writes block oblk
   // of row m kRPI + orow -- at offset oc_off[m] for contiguous rows, or
   // (GATHER) at the unit's lro[m], from that row's token.
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void expand_fast(const Params p) {
   static_assert(kOAcc * kRPI == kTileRows, "row-wise accesses cover the tile");
   __shared__ u32x4 o_lds[kWaves][kTileRows * kNB];
   auto o_slot = [](int r, int b) __attribute__((always_inline)) -> int {
-    return kNB * r + (b ^ (kNB == 8 ? (r >> 1) : r));
+    return kNB * r + (b ^ (r % kNB));
   };
   // accumulator-layout block of lane (j, g): column group q, vector v
   auto acc_blk = [&](int q, int v) __attribute__((always_inline)) -> int {

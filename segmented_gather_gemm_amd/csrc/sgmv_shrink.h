@@ -128,14 +128,18 @@ __device__ __forceinline__ void shrink_store(const ShrinkParams& p, int i, int32
 }
 
 // LDS layout of an operand fragment staged from coalesced loads (16 rows x
-// 32 hidden, 1 KiB in MFMA operand order, lora_A or input): lane (j, g)'s 16
-// bytes sit in slot 16 g + (j ^ 4 g) of the fragment.  A coalesced load
-// reads R rows x 64 / R lanes of contiguous 16-byte blocks; the 16 lanes the
-// LDS serves together then cover one or two rows and 4 or 2 steps, whose
-// slots fall in 16 different bank groups when fragments are 65 slots apart
-// (one row, 4 steps) or 66 (two rows, 2 steps).  The MFMA operand reads
-// (16 lanes of one g, j = 0..15) are conflict-free for any stride.
-__device__ __forceinline__ int frag_slot(int j, int g) { return 16 * g + (j ^ (4 * g)); }
+// 32 hidden, 1 KiB in MFMA operand order, lora_A or input), both kernels:
+// lane (j, g)'s 16 bytes sit in slot 16 g + (j ^ 2 g) of the fragment, and
+// fragments are kFragSlots = 65 slots apart.  The LDS serves a 16-byte
+// access 8 lanes (128 bytes, 8 slot classes mod 8) at a time (measured on
+// gfx950 with the SQ_LDS_BANK_CONFLICT counter).  The MFMA operand reads
+// (8 lanes of one g, consecutive j) hit 8 classes for any g.  The staging
+// writes of a coalesced load put 8 lanes on one row: g = 0..3 of two
+// consecutive steps, i.e. of fragments f and f + 1; they hit the 4 classes
+// of one parity in fragment f and, 65 being odd, the other 4 in f + 1.
+// (Slot 16 g + (j ^ 4 g) hits 4 classes there: 2-way conflicts.)
+constexpr int kFragSlots = 65;
+__device__ __forceinline__ int frag_slot(int j, int g) { return 16 * g + (j ^ (2 * g)); }
 
 // ---------------------------------------------------------------------------
 // Split-H: 16 tokens per unit; the four waves of the workgroup split the
@@ -164,13 +168,11 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
   // block's kB steps contiguously (lane l: row l / kLPR, hidden block
   // l % kLPR, i.e. block (l % kLPR) % 4 of step (l % kLPR) / 4); the wave
   // scatters them into MFMA operand order in its own LDS region (see
-  // frag_slot; fragments 65 slots apart, 66 when a load spans 8 rows) and
-  // reads the operands back.  More k tiles load operands directly (16 rows x
-  // 64 bytes per load), which needs no LDS.
+  // frag_slot) and reads the operands back.  More k tiles load operands
+  // directly (16 rows x 64 bytes per load), which needs no LDS.
   constexpr bool kCoal = kT <= 8;
   constexpr int kLPR = 4 * kB;
   constexpr int kRPI = 64 / kLPR;
-  constexpr int kStride = kLPR == 8 ? 66 : 65;
   static_assert(!kCoal || (kB % 2 == 0 && kRPI * kB == 16), "coalesced block shape");
   prefetch_params(p);
   extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
   __shared__ f32x4 red[kW][kRound][64];
   // per wave: the block's input fragments (steps 0 .. kB - 1), then each k
   // tile's ([tile + 1] kB + step)
-  __shared__ u32x4 stage[kCoal ? kW : 1][kCoal ? (kT + 1) * kB : 1][kCoal ? kStride : 1];
+  __shared__ u32x4 stage[kCoal ? kW : 1][kCoal ? (kT + 1) * kB : 1][kCoal ? kFragSlots : 1];
   const SegTable tab = seg_table(lds, p.batches);
   const int32_t U = build_tile_table(p, tab, wave_total, kTileRows);
   if (U == 0) return;
@@ -336,10 +338,6 @@ struct SplitTBlock {
   u32x4 x[Sh::kBlockT][Sh::kNV];     // this wave's input rows
   u32x4 a[NS][Sh::kPairs];           // this wave's share of the block's lora_A tiles
 };
-
-// Split-T fragments are kFragSlots = 66 slots apart (see frag_slot; its
-// loads span 8 rows).
-constexpr int kFragSlots = 66;
 
 template <int XD, int WD, int OD, int K16, int NS>
 __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p) {
