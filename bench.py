@@ -3,11 +3,15 @@
 
 One step = one call of the hot path (sgmv_expand_slice, or one
 sgmv_expand_multi_slice call for the fused QKV workload) over one batch of
-seeded synthetic input already resident in HBM.  W untimed warm-up steps,
-then exactly K timed steps between HIP events on the launch stream, bracketed
-by device synchronisation.  Each step uses the next of S identical buffer
-sets (inputs, weights, output), S >= 2 and S * footprint >= 1 GiB, so no
-step finds its data in the 256 MB Infinity Cache or the L2s.
+seeded synthetic input already resident in HBM.  The default workload is the
+largest configuration, the 14336-wide MLP gate/up slice (mlp_gate_up);
+--workload selects another.  W untimed warm-up steps, then exactly K timed
+steps, captured in one HIP graph and replayed once between HIP events on the
+launch stream, bracketed by device synchronisation (a cache-evicting fill
+runs on the stream just before the first event, so the host's submission of
+the graph is not timed).  Each step uses the next of S identical buffer sets
+(inputs, weights, output), S >= 2 and S * footprint >= 1 GiB, so no step
+finds its data in the 256 MB Infinity Cache or the L2s.
 
 Effective bandwidth uses the algorithmic byte count
     T_act * rank * in_bytes + sum_distinct_adapters slice * rank * w_bytes
@@ -32,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak, GB/s
-DEFAULT_WORKLOAD = "llama7b_q_proj"
+DEFAULT_WORKLOAD = "mlp_gate_up"
 CSRC = os.path.join(ROOT, "segmented_gather_gemm_amd", "csrc")
 
 
@@ -148,49 +152,76 @@ def time_steps(step, steps, warmup):
     return t0.elapsed_time(t1) / steps, wall
 
 
-def time_steps_graph(step, steps, warmup, batches=5):
-    """Capture `warmup` steps and the `steps` timed steps (as up to `batches`
-    consecutive batches) into HIP graphs and replay them back to back: the
-    same launches with the host's launch overhead taken out of the loop.
-    Returns (ms per step over all timed steps, wall seconds, median over the
-    batches of ms per step)."""
+def _graph_upload(graph, stream):
+    """Upload an instantiated graph to the device ahead of its first launch
+    (hipGraphUpload through the HIP runtime torch uses), so the first replay
+    does not carry it.  Best effort: False if the runtime call is not there."""
+    import ctypes
+    try:
+        path = next(l.split()[-1] for l in open("/proc/self/maps")
+                    if "libamdhip64" in l and l.split()[-1].startswith("/"))
+        hip = ctypes.CDLL(path)
+        return hip.hipGraphUpload(ctypes.c_void_p(graph.raw_cuda_graph_exec()),
+                                  ctypes.c_void_p(stream.cuda_stream)) == 0
+    except Exception:
+        return False
+
+
+class _Flush:
+    """A 1 GiB device buffer; fill() enqueues two writes of it (about half a
+    millisecond of GPU work that also evicts the caches)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty((1 << 30) // 4, dtype=torch.int32, device="cuda")
+        self.n = 0
+
+    def fill(self):
+        self.n += 1
+        self.buf.fill_(self.n)
+        self.buf.fill_(-self.n)
+
+
+def time_steps_graph(step, steps, warmup, repeats=5):
+    """Exactly `steps` timed steps in one HIP graph, after `warmup` eager
+    untimed steps (which also fill the library's device caches): the graph is
+    captured, uploaded, and replayed once between HIP events on the launch
+    stream, right behind a cache-evicting fill so the GPU never waits for the
+    host.  Then `repeats` more replays, each behind its own fill, give a
+    median.  Returns (ms per step of the timed replay, wall seconds of it,
+    median ms per step over the repeats)."""
     import statistics
     import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(3):            # first calls fill the library's device caches
-            step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    nb = max(1, min(batches, steps))
-    sizes = [steps // nb + (1 if b < steps % nb else 0) for b in range(nb)]
-    g_warm = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_warm):
-        for i in range(warmup):
-            step(i)
-    graphs, first = [], warmup
-    for n in sizes:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                step(first + i)
-        graphs.append(g)
-        first += n
-    torch.cuda.synchronize()
-    g_warm.replay()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(steps):
+            step(warmup + i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
-    wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for b, g in enumerate(graphs):
-        g.replay()
-        ev[b + 1].record(stream)
+    _graph_upload(g, stream)
+    flush = _Flush()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per_batch = [ev[b].elapsed_time(ev[b + 1]) / sizes[b] for b in range(nb)]
-    return ev[0].elapsed_time(ev[nb]) / steps, wall, statistics.median(per_batch)
+
+    def one():
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        flush.fill()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        w0 = time.perf_counter()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - w0
+
+    ms, wall = one()
+    rep = [one()[0] for _ in range(repeats)]
+    del flush
+    return ms, wall, statistics.median(rep)
 
 
 def time_single_launches(step, reps=50, flush_bytes=1 << 30):
@@ -214,26 +245,78 @@ def time_single_launches(step, reps=50, flush_bytes=1 << 30):
     return statistics.median(times)
 
 
-def copy_ceiling(nbytes, device, reps=20):
-    """GB/s of a plain device copy moving `nbytes` read + `nbytes` written
-    (context only)."""
+def byte_split(wl):
+    """(read, written) algorithmic bytes of one expand call: inputs, each
+    distinct adapter's weights and (add_inputs) the prior output are read,
+    the slice windows of active rows written."""
+    from sgmv_workloads import DTYPE_BYTES
+    total, t_act, distinct = byte_model(wl)
+    ob = DTYPE_BYTES[wl.out_dtype]
+    written = sum(t_act * s.N * ob for s in wl.slices)
+    return total - written, written
+
+
+def _stream_library():
+    import ctypes
+    path = os.path.join(ROOT, "segmented_gather_gemm_amd", "libsgmv_stream.so")
+    lib = ctypes.CDLL(path)
+    lib.sgmv_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lib.sgmv_stream_probe.restype = ctypes.c_int
+    return lib
+
+
+def stream_ceilings(read_bytes, write_bytes, reps=20, grids=(1024, 2048, 4096, 8192)):
+    """Streaming ceilings for a traffic of `read_bytes` read and
+    `write_bytes` written per launch, from the hand-written probe kernel in
+    libsgmv_stream.so (16-byte buffer accesses, non-temporal loads,
+    non-temporal device-scope stores -- the SGMV kernels' forms): GB/s of
+    the reads alone, of the writes alone, and of both in one launch with the
+    reads spread evenly among the writes.  Each figure is the best over a
+    few grid sizes of `reps` back-to-back launches, each on the next of
+    enough buffer copies that no launch finds its data in the caches (1 GiB
+    and more).  Context for the HBM roofline, not the metric."""
     import torch
-    n = max(1, nbytes // 2)
-    sets = max(2, math.ceil((1 << 30) / (2 * n)))
-    src = [torch.empty(n, dtype=torch.int16, device=device).fill_(1) for _ in range(sets)]
-    dst = [torch.empty_like(s) for s in src]
-    for i in range(5):
-        dst[i % sets].copy_(src[i % sets])
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(reps):
-        dst[i % sets].copy_(src[i % sets])
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / reps
-    return 2 * n * 2 / (ms * 1e-3) / 1e9
+    lib = _stream_library()
+    R = (int(read_bytes) // 16) * 16
+    Wb = (int(write_bytes) // 16) * 16
+    limit = (1 << 31) - 16
+    R, Wb = min(R, limit), min(Wb, limit)
+    sets = max(2, math.ceil((1 << 30) / max(1, R + Wb)))
+    src = [torch.ones(max(R, 16) // 4, dtype=torch.int32, device="cuda") for _ in range(sets)]
+    dst = [torch.empty(max(Wb, 16) // 4, dtype=torch.int32, device="cuda") for _ in range(sets)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def rate(rb, wb):
+        if rb + wb == 0:
+            return None
+        best = 0.0
+        for blocks in grids:
+            def launch(i):
+                rc = lib.sgmv_stream_probe(src[i % sets].data_ptr(), rb, dst[i % sets].data_ptr(),
+                                           wb, sink.data_ptr(), blocks, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream probe failed with HIP error {rc}")
+            for i in range(3):
+                launch(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            best = max(best, (rb + wb) / (ms * 1e-3) / 1e9)
+        return round(best, 1)
+
+    out = {"read_bytes": R, "write_bytes": Wb, "read_gbs": rate(R, 0),
+           "write_gbs": rate(0, Wb), "mix_gbs": rate(R, Wb)}
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def traffic_from_profiles(workload, ksha):
@@ -321,6 +404,14 @@ def shrink_byte_model(wl, rows=None):
     total += ns * distinct * wl.K * wl.H * DTYPE_BYTES[wl.a_dtype]
     total += ns * t_act * wl.K * DTYPE_BYTES[wl.out_dtype]
     return total, t_act, distinct
+
+
+def shrink_byte_split(wl):
+    """(read, written) algorithmic bytes of one shrink call."""
+    from sgmv_workloads import DTYPE_BYTES
+    total, t_act, _ = shrink_byte_model(wl)
+    written = len(wl.lora_a) * t_act * wl.K * DTYPE_BYTES[wl.out_dtype]
+    return total - written, written
 
 
 class ShrinkBufferSet:
@@ -446,9 +537,14 @@ def run_shrink(args):
     traffic = None if traffic_bytes is None else round(traffic_bytes / sec / 1e9, 2)
     log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
         f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
-    ceiling = None if args.no_copy_ceiling else round(copy_ceiling(model_bytes // 2, device), 1)
     del sets, first
     torch.cuda.empty_cache()
+    ceilings = None
+    if not args.no_ceiling:
+        log("bench: streaming ceilings for the same read / write traffic")
+        rb, wb = shrink_byte_split(wl)
+        ceilings = stream_ceilings(rb, wb)
+        ceilings["pct_of_mix"] = round(100 * gbs / ceilings["mix_gbs"], 1)
     cpu = None
     if args.cpu_budget > 0:
         log("bench: timing the CPU oracle baseline")
@@ -502,7 +598,7 @@ def run_shrink(args):
             "kernel": "shrink_split_t" if -(-wl.T // 64) >= 64 else "shrink_split_h",
             "kernel_source_sha256_16": ksha,
         },
-        "copy_ceiling_gbs": ceiling,
+        "streaming_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -517,7 +613,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU-oracle time for the baseline (0 = skip)")
-    ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-ceiling probes")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: HIP-graph replay, eager also reported)")
     ap.add_argument("--split-slices", action="store_true",
@@ -578,9 +675,14 @@ def main():
     log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
         f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
 
-    ceiling = None if args.no_copy_ceiling else round(copy_ceiling(model_bytes // 2, device), 1)
     del sets, first
     torch.cuda.empty_cache()
+    ceilings = None
+    if not args.no_ceiling:
+        log("bench: streaming ceilings for the same read / write traffic")
+        rb, wb = byte_split(wl)
+        ceilings = stream_ceilings(rb, wb)
+        ceilings["pct_of_mix"] = round(100 * gbs / ceilings["mix_gbs"], 1)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -636,7 +738,7 @@ def main():
             "kernel": "expand_fast",
             "kernel_source_sha256_16": ksha,
         },
-        "copy_ceiling_gbs": ceiling,
+        "streaming_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

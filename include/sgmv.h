@@ -192,6 +192,14 @@ typedef struct {
  *               preconditions.
  * scale         fp32 factor applied to every sum (1 for the plain product).
  *
+ * Kernel choice (results are the same within tolerance, and bit for bit on
+ * integer-valued data): the register-tiled kernels take rank % 8 == 0,
+ * hidden % 8 == 0, 16-byte aligned rows, 64 rows of inputs and of each
+ * output spanning < 2 GiB, and 16 * p rows of one adapter's lora_a block
+ * spanning < 2 GiB, i.e. 32 * p * hidden < 2^31, where p is the next power
+ * of two of ceil(rank / 16) (rank 256: hidden < 4 Mi); every other shape
+ * runs on the generic kernel.
+ *
  * Returns SGMV_OK, or a status with nothing launched; batches == 0 or
  * total_tokens == 0 return SGMV_OK without a launch.
  */

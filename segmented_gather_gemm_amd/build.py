@@ -9,6 +9,9 @@ both on csrc/sgmv_common.h)
 with the code object embedded; nothing is
 compiled at run time.  Packed-fp32 VALU instructions are disabled for every
 HIP translation unit.
+
+It also builds libsgmv_stream.so (csrc/sgmv_stream.hip), the benchmark's
+streaming-bandwidth probe, which is not part of the operation.
 """
 import os
 import subprocess
@@ -25,6 +28,9 @@ SOURCES = [os.path.join(CSRC, f) for f in
             "sgmv_fast_ks2.hip", "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip",
             "sgmv_shrink_generic.hip", "sgmv_shrink_k1.hip", "sgmv_shrink_k2.hip",
             "sgmv_shrink_k4.hip", "sgmv_shrink_k8.hip", "sgmv_shrink_k16.hip")]
+
+STREAM_SOURCE = os.path.join(CSRC, "sgmv_stream.hip")
+STREAM_LIBRARY = os.path.join(HERE, "libsgmv_stream.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -46,9 +52,14 @@ def _diagnostics(text: str) -> str:
 
 
 def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY) -> str:
-    """Compile every translation unit in parallel and link libsgmv.so (always
-    rebuilds); return its path."""
+    """Compile every translation unit in parallel and link libsgmv.so, and
+    build the streaming probe library (always rebuilds); return libsgmv's
+    path."""
     t0 = time.time()
+    stream_tmp = STREAM_LIBRARY + ".tmp%d" % os.getpid()
+    stream_cmd = [HIPCC, *FLAGS, "-shared", STREAM_SOURCE, "-o", stream_tmp]
+    stream_proc = subprocess.Popen(stream_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                   text=True)
     tmpdir = output + ".objs%d" % os.getpid()
     os.makedirs(tmpdir, exist_ok=True)
     try:
@@ -73,7 +84,13 @@ def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY) -> str:
         if res.returncode != 0:
             raise RuntimeError(f"link failed:\n{_diagnostics(res.stdout + res.stderr)}")
         os.replace(tmp, output)
+        out, _ = stream_proc.communicate()
+        if stream_proc.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {STREAM_SOURCE}:\n{_diagnostics(out)}")
+        os.replace(stream_tmp, STREAM_LIBRARY)
     finally:
+        if stream_proc.poll() is None:
+            stream_proc.wait()
         for f in os.listdir(tmpdir):
             os.remove(os.path.join(tmpdir, f))
         os.rmdir(tmpdir)

@@ -228,14 +228,15 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   // common row tiles (one weight tile and one MFMA pass for up to 16 tokens)
   // when they are few enough for the gathered table in LDS and T rows of the
   // inputs and of the output span less than 2 GiB (32-bit row offsets).
-  // Otherwise per-token calls, and calls of many segments, order the
-  // segment table by adapter (when it is cheap enough), so that neighbours
-  // that share an adapter share its weight tiles.
+  // Otherwise per-token calls, calls of many segments and large calls order
+  // the segment table by adapter (when it is cheap enough), so that
+  // neighbours that share an adapter share its weight tiles.
   bool gather = fast && per_token && batches <= kGatherMaxTokens && L <= kGatherMaxAdapters &&
                 out.rows * p.out_row_bytes < (int64_t(1) << 31);
   for (int i = 0; i < num_slices && gather; ++i)
     if (out.rows * p.s[i].x_row_bytes >= (int64_t(1) << 31)) gather = false;
-  const bool sort = !gather && (per_token || batches >= kSortMinBatches) &&
+  const bool sort = !gather &&
+                    (per_token || batches >= kSortMinBatches || units >= kSortMinUnits) &&
                     batches <= kSortMaxBatches && L <= (1 << 22);
   p.sort_slots = sort;
   p.gather = gather;

@@ -1,5 +1,6 @@
 // sgmv_launch.h -- interface between the host entry points (sgmv_api.cpp)
-// and the gfx950 kernels (sgmv_kernels.hip).  Internal to libsgmv.
+// and the gfx950 expand kernels (sgmv_device.h, instantiated in
+// sgmv_fast_ks*.hip and sgmv_generic.hip).  Internal to libsgmv.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,11 +15,15 @@ constexpr int kWaveCols = 64;          // output columns one wavefront owns per 
 constexpr int kTileCols = kWaves * kWaveCols;  // columns per work unit (256)
 constexpr int kTileRows = 16;          // rows per work unit (one MFMA column block)
 constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk order
-// Segment tables are ordered by adapter for batches in [min, max]: with many
-// (short) segments, neighbours that share an adapter share weight tiles; the
-// ordering costs O(batches^2 / threads) per workgroup.
+// Segment tables are ordered by adapter for batches in [min, max], and for
+// any batch count up to max when the call holds at least kSortMinUnits work
+// units: segments that share an adapter are then neighbours in the walk and
+// share its weight tiles (from registers or L2) instead of fetching them
+// again from memory.  The ordering costs O(batches^2 / threads) per
+// workgroup (a few tenths of a microsecond), which only small calls notice.
 constexpr int kSortMinBatches = 128;
 constexpr int kSortMaxBatches = 512;
+constexpr int64_t kSortMinUnits = 8192;
 // Per-token calls gather each adapter's tokens into row tiles for up to this
 // many tokens (every per-token call the ABI accepts, SGMV_MAX_BATCHES) and
 // adapters (the gathered table: tokens + 2 adapters + 1 LDS words; each

@@ -11,11 +11,13 @@
 
 #include "sgmv.h"
 #include "sgmv_host.h"
+#include "sgmv_limits.h"
 #include "sgmv_shrink_launch.h"
 
 namespace {
 
 using namespace sgmv::host;
+using sgmv::limits::shrink_fast_lora_a_fits;
 
 // Fast shrink kernel for k16 tiles of 16 rows per slice and ns slices.
 const void* pick_shrink_kernel(int xd, int wd, int od, int k16, int ns, bool split_t) {
@@ -175,14 +177,19 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
     if (!slices[i].out.data || (!slices[i].lora_a.data && L > 0))
       return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: null data pointer", i);
 
-  // Fast kernels: 16-byte blocks everywhere, hidden < 2^26 and a unit's rows
-  // (64) of inputs or outputs spanning less than 2 GiB (32-bit buffer
-  // offsets).  Decided for the inputs, then per slice; slices are launched
+  // Fast kernels: 16-byte blocks everywhere, hidden < 2^26, a unit's rows
+  // (64) of inputs or outputs spanning less than 2 GiB, and the lora_A rows
+  // the k tiles address (16 k16 rows of one adapter's (K, H) block, the
+  // rows past K masked) spanning less than 2 GiB as well: their buffer
+  // offsets are 32-bit and the masked-lane offset 2^31 must lie past every
+  // resource.  Decided for the inputs, then per slice; slices are launched
   // in runs that take the same kernel family (so a slice's result does not
   // depend on the others in the call).
   const int64_t xb = elem_bytes(x.dtype), ob = elem_bytes(s0.out.dtype);
   const int64_t span = kShrinkTokensSplitT;
+  const int k16 = next_pow2((int)((K + 15) / 16));
   const bool fast_x = K % 8 == 0 && x.cols % 8 == 0 && x.cols < (int64_t(1) << 26) &&
+                      shrink_fast_lora_a_fits(K, x.cols) &&
                       aligned16(x.data) && (x.row_stride * xb) % 16 == 0 &&
                       span * x.row_stride * xb < (int64_t(1) << 31);
   auto fast_slice = [&](int i) {
@@ -193,7 +200,6 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
   // The fast kernels take up to kShrinkMaxSlicesPerLaunch slices and 16 k
   // tiles of 16 rows per launch: more slices go in several launches (each
   // reads the inputs again).
-  const int k16 = next_pow2((int)((K + 15) / 16));
   int fast_per_launch = 16 / k16;
   if (fast_per_launch > kShrinkMaxSlicesPerLaunch) fast_per_launch = kShrinkMaxSlicesPerLaunch;
   const bool split_t =

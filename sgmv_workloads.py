@@ -246,6 +246,47 @@ def per_token(idx: Sequence[int], **kw) -> Workload:
     return wl
 
 
+def nonfinite(x_dtype: str = "f16", w_dtype: str = "f16", out_dtype: str = "f16",
+              add: bool = True, off: int = 8, seed: int = 0) -> Workload:
+    """Integer-valued data (x, W in [-3, 3], prior in [-8, 8]) with NaN, +-Inf
+    and overflowing values planted in rows of active segments, in weights
+    those rows use and in their prior output; also NaN in a row and a prior
+    element of the index -1 segment.  Segments: rows 0-5 adapter 0, 6-10
+    adapter 1, 11-14 index -1, 15-21 adapter 0; rank 16, slice of 64 columns
+    at ``off`` in rows of 80.
+
+    Planted (slice-relative columns):
+      x[1][3] = NaN; x[2][0] = +Inf; x[3][0] = +Inf and x[3][1] = -Inf;
+      x[16][:] = 6144 (sums of up to 16 * 3 * 6144 = 294912 overflow f16);
+      x[17][0] = 3.4e38 when x is float32 (its cast to f16 or bf16 is +Inf);
+      W[1][5][2] = NaN; W[1][9][4] = +Inf;
+      prior[4][5] = -Inf; prior[5][7] = NaN (overwritten unless add);
+      x[12][0] = NaN and prior[13][1] = NaN in the index -1 segment."""
+    lens, idx = [6, 5, 4, 7], [0, 1, -1, 0]
+    wl = custom(lens, idx, K=16, N=64, H=80, off=off, L=2, x_dtype=x_dtype, w_dtype=w_dtype,
+                out_dtype=out_dtype, add=add, seed=seed, values="int", name="nonfinite")
+    s = wl.slices[0]
+    x, w, o = s.x.copy(), s.w.copy(), wl.out0.copy()
+
+    def put(a, index, value, dtype):
+        a[index] = _to_storage(np.array([value], dtype=np.float32), dtype)[0]
+
+    for (r, k), v in {(1, 3): np.nan, (2, 0): np.inf, (3, 0): np.inf, (3, 1): -np.inf,
+                      (12, 0): np.nan}.items():
+        put(x, (r, k), v, x_dtype)
+    for k in range(16):
+        put(x, (16, k), 6144.0, x_dtype)
+    if x_dtype == "f32":
+        x[17, 0] = np.float32(3.4e38)
+    put(w, (1, 5, 2), np.nan, w_dtype)
+    put(w, (1, 9, 4), np.inf, w_dtype)
+    put(o, (4, off + 5), -np.inf, out_dtype)
+    put(o, (5, off + 7), np.nan, out_dtype)
+    put(o, (13, off + 1), np.nan, out_dtype)
+    return Workload("nonfinite", [SliceInput(x, x_dtype, w, w_dtype, off)], o, out_dtype,
+                    wl.start, wl.lens, wl.idx, add, wl.K, wl.L, seed)
+
+
 WORKLOADS: Dict[str, Callable[..., Workload]] = {
     "tiny_ref": tiny_ref,
     "llama7b_q_proj": llama7b_q_proj,

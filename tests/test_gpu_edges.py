@@ -274,6 +274,31 @@ def test_nan_in_skipped_rows_and_unused_adapters_does_not_leak():
     assert np.array_equal(bits[6:11], wl.out0[6:11])
 
 
+@pytest.mark.parametrize("off", [8, 3])                # fast kernel; generic (misaligned)
+@pytest.mark.parametrize("add", [False, True])
+@pytest.mark.parametrize("dts", [("f16", "f16", "f16"), ("f32", "f16", "f32"),
+                                 ("bf16", "bf16", "bf16"), ("f32", "bf16", "bf16")])
+def test_nan_and_inf_in_active_rows_propagate(dts, add, off):
+    """NaN and +-Inf in inputs, weights and prior output of active rows, an
+    input cast that overflows, and sums that overflow f16 (see
+    sgmv_workloads.nonfinite): every written element must be NaN exactly
+    where the oracle's exact value is NaN, the same infinity where it rounds
+    to one, within tolerance elsewhere; the index -1 segment's rows (with
+    their own NaNs) keep their bits.  The data are integers, so every finite
+    fp32 partial sum is exact."""
+    wl = W.nonfinite(*dts, add=add, off=off)
+    dw, bits = run_and_check(wl)
+    from oracle_pins_util import np_values
+    got = np_values(np.ascontiguousarray(bits[:, off:off + 64]), wl.out_dtype)
+    assert np.isnan(got[1]).all() and np.isnan(got[6:11, 5]).all()
+    assert np.isposinf(got[2]).any() and np.isneginf(got[2]).any()
+    if add:
+        assert np.isneginf(got[4, 5]) and np.isnan(got[5, 7])
+    bview = bits.view(np.uint32) if wl.out_dtype == "f32" else bits
+    oview = wl.out0.view(np.uint32) if wl.out_dtype == "f32" else wl.out0
+    assert np.array_equal(bview[11:15], oview[11:15])
+
+
 @pytest.mark.parametrize("add", [False, True])
 def test_multi_slice_bit_identical_to_single_calls(add):
     # QKV-like three slices and gate/up-like two slices, ragged widths
