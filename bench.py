@@ -7,9 +7,10 @@ seeded synthetic input already resident in HBM.  The default workload is the
 largest configuration, the 14336-wide MLP gate/up slice (mlp_gate_up);
 --workload selects another.  W untimed warm-up steps, then exactly K timed
 steps, captured in one HIP graph and replayed once between HIP events on the
-launch stream, bracketed by device synchronisation (a cache-evicting fill
-runs on the stream just before the first event, so the host's submission of
-the graph is not timed).  Each step uses the next of S identical buffer sets
+launch stream right behind the W warm-up steps (themselves one graph,
+preceded by a cache-evicting fill), bracketed by device synchronisation, so
+the timed steps start on a busy GPU and the host's submission is not
+timed.  Each step uses the next of S identical buffer sets
 (inputs, weights, output), S >= 2 and S * footprint >= 1 GiB, so no step
 finds its data in the 256 MB Infinity Cache or the L2s.
 
@@ -183,27 +184,31 @@ class _Flush:
 
 
 def time_steps_graph(step, steps, warmup, repeats=5):
-    """Exactly `steps` timed steps in one HIP graph, after `warmup` eager
-    untimed steps (which also fill the library's device caches): the graph is
-    captured, uploaded, and replayed once between HIP events on the launch
-    stream, right behind a cache-evicting fill so the GPU never waits for the
-    host.  Then `repeats` more replays, each behind its own fill, give a
-    median.  Returns (ms per step of the timed replay, wall seconds of it,
-    median ms per step over the repeats)."""
+    """The `warmup` untimed steps and exactly `steps` timed steps as two HIP
+    graphs, captured and uploaded ahead; then, on the launch stream, a
+    cache-evicting fill, the warm-up graph, an event, the timed graph and an
+    event, so the timed steps follow real work (the GPU is neither idle nor
+    waiting for the host when they start).  Then `repeats` more rounds of
+    the same give a median.  Returns (ms per step of the first timed replay,
+    wall seconds of it, median ms per step over the repeats)."""
     import statistics
     import torch
-    for i in range(warmup):
-        step(i)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    g_warm = None
+    if warmup > 0:
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm):
+            for i in range(warmup):
+                step(i)
     g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.graph(g, stream=side):
+    with torch.cuda.graph(g):
         for i in range(steps):
             step(warmup + i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    _graph_upload(g, stream)
+    for gr in (g_warm, g):
+        if gr is not None:
+            _graph_upload(gr, stream)
     flush = _Flush()
     torch.cuda.synchronize()
 
@@ -211,6 +216,8 @@ def time_steps_graph(step, steps, warmup, repeats=5):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         flush.fill()
+        if g_warm is not None:
+            g_warm.replay()
         e0.record(stream)
         g.replay()
         e1.record(stream)

@@ -235,8 +235,11 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
                 out.rows * p.out_row_bytes < (int64_t(1) << 31);
   for (int i = 0; i < num_slices && gather; ++i)
     if (out.rows * p.s[i].x_row_bytes >= (int64_t(1) << 31)) gather = false;
-  const bool sort = !gather &&
-                    (per_token || batches >= kSortMinBatches || units >= kSortMinUnits) &&
+  int64_t adapter_bytes = 0;  // one adapter's weights over all slices
+  for (int i = 0; i < num_slices; ++i)
+    adapter_bytes += slices[i].slice_size * K * elem_bytes(slices[i].lora_b.dtype);
+  const bool large = units >= kSortMinUnits && adapter_bytes >= kSortMinAdapterBytes;
+  const bool sort = !gather && (per_token || batches >= kSortMinBatches || large) &&
                     batches <= kSortMaxBatches && L <= (1 << 22);
   p.sort_slots = sort;
   p.gather = gather;

@@ -17,13 +17,21 @@ constexpr int kTileRows = 16;          // rows per work unit (one MFMA column bl
 constexpr int kColumnGroups = 8;       // one per XCD: the fast kernels' walk order
 // Segment tables are ordered by adapter for batches in [min, max], and for
 // any batch count up to max when the call holds at least kSortMinUnits work
-// units: segments that share an adapter are then neighbours in the walk and
-// share its weight tiles (from registers or L2) instead of fetching them
-// again from memory.  The ordering costs O(batches^2 / threads) per
-// workgroup (a few tenths of a microsecond), which only small calls notice.
+// units and one adapter's weights (all slices) are at least
+// kSortMinAdapterBytes: segments that share an adapter are then neighbours
+// in the walk and share its weight tiles (from registers or L2) instead of
+// fetching them again from memory.  The ordering costs O(batches^2 /
+// threads) per workgroup (a few tenths of a microsecond) and changes the
+// walk's balance; measured on MI355X it pays where weights are a large part
+// of the traffic (14336-wide slice at rank 64: 108.9 -> 105.8 us) and not
+// where they are small (fused QKV at rank 32: 55.1 -> 56.1 us).
 constexpr int kSortMinBatches = 128;
 constexpr int kSortMaxBatches = 512;
-constexpr int64_t kSortMinUnits = 8192;
+#ifndef SGMV_SORT_MIN_UNITS
+#define SGMV_SORT_MIN_UNITS 8192
+#endif
+constexpr int64_t kSortMinUnits = SGMV_SORT_MIN_UNITS;
+constexpr int64_t kSortMinAdapterBytes = int64_t(1) << 20;
 // Per-token calls gather each adapter's tokens into row tiles for up to this
 // many tokens (every per-token call the ABI accepts, SGMV_MAX_BATCHES) and
 // adapters (the gathered table: tokens + 2 adapters + 1 LDS words; each
