@@ -45,21 +45,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-SHARED_SOURCES = ("sgmv_common.h", "sgmv_launch.h", "sgmv_host.h", "sgmv_host.cpp")
+# Library sources by kernel family (the profiles under profiles/ name the
+# hash of the family they measured); the shared ones belong to every family.
+SHARED_SOURCES = ("sgmv_common.h", "sgmv_launch.h", "sgmv_host.h", "sgmv_host.cpp",
+                  "sgmv_limits.h")
+FAMILY_SOURCES = {
+    "expand": ("sgmv_api.cpp", "sgmv_device.h", "sgmv_fast_ks", "sgmv_generic.hip"),
+    "shrink": ("sgmv_shrink",),
+    "fused": ("sgmv_fused", "sgmv_shrink.h", "sgmv_shrink_launch.h", "sgmv_device.h"),
+}
 
 
 def kernel_source_hash(family: str = "expand") -> str:
     """Hash of the library sources a kernel family is built from (kernels,
-    launch and entry points): the expand's files are every source not named
-    sgmv_shrink*; the shrink's (LoRA-A projection) are the sgmv_shrink* files
-    and the shared ones."""
+    launch and entry points, and the shared helpers)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if not name.endswith((".hip", ".h", ".cpp")):
             continue
-        if family == "expand" and name.startswith("sgmv_shrink"):
-            continue
-        if family == "shrink" and not (name.startswith("sgmv_shrink") or name in SHARED_SOURCES):
+        if name not in SHARED_SOURCES and not name.startswith(FAMILY_SOURCES[family]):
             continue
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -611,6 +615,232 @@ def run_shrink(args):
     print(json.dumps(result), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Fused LoRA delta (shrink and expand in one launch) workloads.
+# ---------------------------------------------------------------------------
+
+def fused_byte_model(wl):
+    """Algorithmic bytes of one fused call: the input rows of active
+    segments, each distinct adapter's lora_A and lora_B rows once per slice,
+    the windows of active rows written (and read, with add_inputs); the
+    projection never leaves the chip.  Returns (total, read, T_act,
+    distinct)."""
+    from sgmv_workloads import DTYPE_BYTES
+    act = wl.active_mask()
+    t_act = int(wl.lens[act].sum())
+    distinct = len(set(wl.idx[act].tolist()))
+    wb, ob = DTYPE_BYTES[wl.w_dtype], DTYPE_BYTES[wl.out_dtype]
+    n_total = sum(b.shape[1] for b in wl.lora_b)
+    read = t_act * wl.H * DTYPE_BYTES[wl.x_dtype]
+    read += distinct * len(wl.lora_a) * wl.K * wl.H * wb + distinct * n_total * wl.K * wb
+    read += t_act * n_total * ob if wl.add else 0
+    written = t_act * n_total * ob
+    return read + written, read, t_act, distinct
+
+
+class FusedBufferSet:
+    def __init__(self, wl, device):
+        import numpy as np
+        import torch
+        from sgmv_workloads import to_torch
+        self.x = to_torch(wl.x, wl.x_dtype, device)
+        self.a = [to_torch(np.ascontiguousarray(a).reshape(a.shape[0], -1), wl.w_dtype,
+                           device).view(a.shape) for a in wl.lora_a]
+        self.b = [to_torch(np.ascontiguousarray(b).reshape(b.shape[0], -1), wl.w_dtype,
+                           device).view(b.shape) for b in wl.lora_b]
+        self.out = to_torch(wl.out0, wl.out_dtype, device)
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[wl.w_dtype]
+        self.y = [torch.zeros((wl.T, wl.K), dtype=tdt, device=device) for _ in wl.lora_a]
+
+    def clone(self):
+        c = object.__new__(FusedBufferSet)
+        c.x = self.x.clone()
+        c.a = [t.clone() for t in self.a]
+        c.b = [t.clone() for t in self.b]
+        c.out = self.out.clone()
+        c.y = [t.clone() for t in self.y]
+        return c
+
+
+def make_fused_step(wl, meta, sets, unfused=False):
+    """One step: one sgmv_fused_shrink_expand call, or with `unfused` the
+    two-launch pair it replaces (sgmv_shrink_multi_slice into weight-dtype
+    projections, then sgmv_expand_multi_slice of them)."""
+    import segmented_gather_gemm_amd as sg
+    start, lens, idx = meta
+    B, M = wl.batches, wl.max_seq_len
+    if unfused:
+        def step(i):
+            bs = sets[i % len(sets)]
+            sg.sgmv_shrink_multi_slice(bs.x, list(zip(bs.a, bs.y)), start, lens, idx, B, M,
+                                       wl.scale)
+            sg.sgmv_expand_multi_slice(list(zip(bs.y, bs.b, wl.offsets)), bs.out, start, lens,
+                                       idx, B, M, wl.add)
+    else:
+        def step(i):
+            bs = sets[i % len(sets)]
+            sg.sgmv_fused_shrink_expand(bs.x, list(zip(bs.a, bs.b, wl.offsets)), bs.out, start,
+                                        lens, idx, B, M, wl.scale, wl.add)
+    return step
+
+
+def fused_cpu_baseline(wl, budget_s):
+    """Time the oracle's fused reference (shrink, then expand; as it stands)
+    on a bounded sample: the first segments, as many as about `budget_s`
+    seconds of work on all host cores allow; then a smaller sample on one
+    core."""
+    import numpy as np
+    import oracle
+    import sgmv_workloads as W
+    threads = len(os.sched_getaffinity(0))
+    n_total = sum(b.shape[1] for b in wl.lora_b)
+    macs_row = len(wl.lora_a) * wl.K * wl.H + n_total * wl.K
+
+    def sample_for(seconds, nthreads):
+        # estimate: ~1e8 fp64 multiply-adds per second per thread
+        act = wl.active_mask()
+        macs = int(wl.lens[act].sum()) * macs_row
+        if macs / (1e8 * nthreads) <= seconds:
+            return wl, "full workload"
+        keep = max(1, int(len(wl.lens) * seconds * 1e8 * nthreads / macs))
+        idx = wl.idx.copy()
+        idx[keep:] = -1
+        smp = W.FusedWorkload(wl.name, wl.x, wl.x_dtype, wl.lora_a, wl.lora_b, wl.w_dtype,
+                              wl.offsets, wl.out0, wl.out_dtype, wl.start, wl.lens, idx,
+                              wl.scale, wl.add, wl.K, wl.L, wl.seed)
+        return smp, f"first {keep} of {len(wl.lens)} segments"
+
+    def run(sample, nthreads, seconds, max_reps):
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < seconds and reps < max_reps):
+            out = sample.out0.copy()
+            t0 = time.perf_counter()
+            oracle.fused(sample.x, sample.x_dtype, sample.lora_a, sample.lora_b, sample.w_dtype,
+                         sample.offsets, out, sample.out_dtype, sample.start, sample.lens,
+                         sample.idx, sample.scale, sample.add, threads=nthreads)
+            spent += time.perf_counter() - t0
+            reps += 1
+        return spent / reps, reps
+
+    sample, note = sample_for(budget_s, threads)
+    secs, reps = run(sample, threads, budget_s, 1000)
+    sample_bytes = fused_byte_model(sample)[0]
+    one, one_note = sample_for(budget_s / 4, 1)
+    secs1, _ = run(one, 1, 0.0, 1)
+    one_bytes = fused_byte_model(one)[0]
+    return {"value": round(sample_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_call": round(secs, 4), "reps": reps,
+            "sample": f"{note} of {wl.name} seed {wl.seed}, fp64 C oracle, {reps} calls",
+            "single_core_gbs": round(one_bytes / secs1 / 1e9, 4),
+            "single_core_sample": f"{one_note}, one call"}
+
+
+def run_fused(args):
+    import torch
+    import sgmv_workloads as W
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    log(f"bench: generating {args.workload} seed {args.seed}")
+    wl = W.FUSED_WORKLOADS[args.workload](args.seed)
+    model_bytes, read_bytes, t_act, distinct = fused_byte_model(wl)
+    fp = (wl.x.nbytes + sum(a.nbytes for a in wl.lora_a) + sum(b.nbytes for b in wl.lora_b) +
+          wl.out0.nbytes)
+    nsets = max(2, math.ceil((1 << 30) / fp))
+    log(f"bench: {len(wl.lora_a)} slice(s), T={wl.T} (active {t_act}), hidden {wl.H} -> rank "
+        f"{wl.K} -> {[b.shape[1] for b in wl.lora_b]}, {distinct} distinct adapters, "
+        f"{model_bytes / 1e6:.2f} MB per call, {nsets} rotated buffer sets of {fp / 1e6:.1f} MB")
+    meta = tuple(torch.from_numpy(a).to(device) for a in (wl.start, wl.lens, wl.idx))
+    first = FusedBufferSet(wl, device)
+    sets = [first] + [first.clone() for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+    step = make_fused_step(wl, meta, sets, args.unfused)
+
+    log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
+    ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
+    log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
+    ms_median = None
+    if args.eager:
+        ms, wall, mode = ms_eager, wall_eager, "eager"
+    else:
+        log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
+        ms, wall, ms_median = time_steps_graph(step, args.steps, args.warmup)
+        mode = "hip-graph replay"
+    log("bench: single launches after a cache flush")
+    ms_single = time_single_launches(step)
+    sec = ms * 1e-3
+    gbs = model_bytes / sec / 1e9
+    tokens_s = wl.T / sec
+    ksha = kernel_source_hash("fused")
+    traffic_bytes = None if args.unfused else traffic_from_profiles(args.workload, ksha)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / sec / 1e9, 2)
+    log(f"bench: {ms * 1e3:.2f} us per step, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% "
+        f"of peak), {tokens_s / 1e6:.2f} M tokens/s (wall {wall:.2f} s)")
+    del sets, first
+    torch.cuda.empty_cache()
+    ceilings = None
+    if not args.no_ceiling:
+        log("bench: streaming ceilings for the same read / write traffic")
+        ceilings = stream_ceilings(read_bytes, model_bytes - read_bytes)
+        ceilings["pct_of_mix"] = round(100 * gbs / ceilings["mix_gbs"], 1)
+    cpu = None
+    if args.cpu_budget > 0:
+        log("bench: timing the CPU oracle baseline")
+        cpu = fused_cpu_baseline(wl, args.cpu_budget)
+    result = {
+        "metric": "effective HBM GB/s (% of MI355X peak) and tokens/s for sgmv_fused_shrink_expand",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.w_dtype,
+        "data": "synthetic",
+        "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(tokens_s, 1),
+        "config": {
+            "workload": args.workload,
+            "seed": args.seed,
+            "hidden": wl.H,
+            "rank": wl.K,
+            "slices": [[o, b.shape[1]] for o, b in zip(wl.offsets, wl.lora_b)],
+            "batches": wl.batches,
+            "total_tokens": wl.T,
+            "active_tokens": t_act,
+            "distinct_adapters": distinct,
+            "scale": wl.scale,
+            "add_inputs": wl.add,
+            "dtypes": {"inputs": wl.x_dtype, "lora_a_b": wl.w_dtype, "output": wl.out_dtype,
+                       "projection": wl.w_dtype, "accumulate": "f32"},
+            "bytes_per_step": model_bytes,
+            "rotated_buffer_sets": nsets,
+            "call": ("sgmv_shrink_multi_slice + sgmv_expand_multi_slice" if args.unfused else
+                     "sgmv_fused_shrink_expand"),
+            "launch": mode,
+            "batch_median_us_per_step": None if ms_median is None else round(ms_median * 1e3, 3),
+            "eager_us_per_step": round(ms_eager * 1e3, 3),
+            "single_launch_after_flush_us": round(ms_single * 1e3, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "traffic_bytes_per_launch": traffic_bytes,
+            "kernel": "two launches" if args.unfused else "fused_shrink_expand",
+            "kernel_source_sha256_16": ksha,
+        },
+        "streaming_ceilings": ceilings,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +854,9 @@ def main():
                     help="skip the streaming-ceiling probes")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: HIP-graph replay, eager also reported)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="fused workloads: time the two-launch pair (shrink, then expand) "
+                         "instead of the fused call")
     ap.add_argument("--split-slices", action="store_true",
                     help="multi-slice workloads: one single-slice call per slice per step "
                          "instead of one fused multi-slice call")
@@ -641,9 +874,11 @@ def main():
 
     if args.workload in W.SHRINK_WORKLOADS:
         return run_shrink(args)
+    if args.workload in W.FUSED_WORKLOADS:
+        return run_fused(args)
     if args.workload not in W.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from "
-                 f"{sorted(W.WORKLOADS) + sorted(W.SHRINK_WORKLOADS)}")
+                 f"{sorted(W.WORKLOADS) + sorted(W.SHRINK_WORKLOADS) + sorted(W.FUSED_WORKLOADS)}")
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     log(f"bench: generating {args.workload} seed {args.seed}")

@@ -33,10 +33,11 @@
 extern "C" {
 #endif
 
-#define SGMV_ABI_VERSION 3
+#define SGMV_ABI_VERSION 4
 #define SGMV_MAX_SLICES 8      /* slices per multi-slice call                       */
 #define SGMV_MAX_RANK 256      /* largest rank the register-tiled kernels take; larger
                                   ranks (any size) run on the generic kernel */
+#define SGMV_MAX_FUSED_SLICES 3 /* slices per fused shrink-expand call (QKV, gate/up) */
 #define SGMV_MAX_BATCHES 4000  /* segment table lives in on-chip memory (LDS, 64 KiB);
                                   also the most tokens of one per-token call */
 
@@ -221,6 +222,68 @@ sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice*
                                     const int64_t* seq_lens, const int64_t* lora_indices,
                                     int64_t batches, int64_t max_seq_len, float scale,
                                     hipStream_t stream);
+
+/* One slice of a fused LoRA delta for sgmv_fused_shrink_expand. */
+typedef struct {
+  sgmv_stack lora_a;      /* (lora_num, rank, hidden)                     */
+  sgmv_stack lora_b;      /* (lora_num, slice_size, rank)                 */
+  int64_t slice_offset;   /* first output column of the slice's window    */
+} sgmv_fused_slice;
+
+/*
+ * sgmv_fused_shrink_expand -- the LoRA-A projection (sgmv_shrink) and the
+ * expand-slice of its result (sgmv_expand_multi_slice) for the slices of a
+ * fused QKV or gate/up layer, in one launch, without storing the projected
+ * rows.  The page motivates the slice kernel by a later operator that fuses
+ * several slice operations into one launch (Description; Usage: fused QKV
+ * and gate/up layers) and describes the expand's inputs as the A-side
+ * projection's rank-sized activations (I/O Contract, Inputs).  For each
+ * segment b with a = lora_indices[b] != -1, each row t of it and each slice
+ * s:
+ *
+ *     y_s[t][k] = rne_w(scale * sum_h inputs[t][h] * lora_a_s[a][k][h]),
+ *     out[t][off_s + n] = (add_inputs ? out[t][off_s + n] : 0)
+ *                         + sum_k y_s[t][k] * lora_b_s[a][n][k],
+ *
+ * with rne_w the nearest-even rounding to the weights' 16-bit dtype -- the
+ * result of sgmv_shrink_multi_slice into outputs of the weights' dtype
+ * followed by sgmv_expand_multi_slice on those outputs (bit for bit equal
+ * to them when the shrink takes its large-batch form, i.e. from 64 units of
+ * 64 tokens); sums in fp32, each result rounded once (nearest even) to the
+ * output dtype; float32 inputs rounded to the weight dtype first.  Rows of
+ * index -1 segments, rows outside every segment and columns outside the
+ * windows are left untouched.
+ *
+ * inputs        device (total_tokens, hidden) f16/bf16/f32; read only.
+ * slices        host array of 1..SGMV_MAX_FUSED_SLICES descriptors, read
+ *               during the call only: lora_a (lora_num, rank, hidden) and
+ *               lora_b (lora_num, slice_size, rank), contiguous, device,
+ *               read only, all of one 16-bit dtype (inputs: that dtype or
+ *               f32), one rank and one lora_num; windows must not overlap.
+ * out           device (total_tokens, out_cols) f16/bf16/f32; written only
+ *               at rows of active segments x the slices' windows; must not
+ *               overlap the other buffers.
+ * b_seq_start_loc, seq_lens, lora_indices, batches, max_seq_len, stream:
+ *               as for sgmv_expand_slice, with the same device-side
+ *               preconditions.
+ * scale         fp32 factor applied to every projected sum before its
+ *               rounding (1 for the plain product).
+ * add_inputs    nonzero: accumulate onto out; zero: overwrite.
+ *
+ * Shapes: rank % 8 == 0 and rank <= 128 with 16 * p * num_slices <= 256
+ * (p = next power of two of ceil(rank / 16)), hidden % 8 == 0, slice widths
+ * % 8 == 0, 16-byte aligned data, rows and windows, and the shrink's lora_a
+ * bound (32 * p * hidden < 2^31); other shapes return SGMV_ERR_UNSUPPORTED
+ * (run sgmv_shrink_multi_slice and sgmv_expand_multi_slice instead).
+ * Returns SGMV_OK, or a status with nothing launched; batches == 0,
+ * total_tokens == 0 or all slice widths 0 return SGMV_OK without a launch.
+ */
+sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice* slices,
+                                     int num_slices, sgmv_matrix out,
+                                     const int64_t* b_seq_start_loc, const int64_t* seq_lens,
+                                     const int64_t* lora_indices, int64_t batches,
+                                     int64_t max_seq_len, float scale, int add_inputs,
+                                     hipStream_t stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if
  * none).  The pointer stays valid until the thread's next libsgmv call. */

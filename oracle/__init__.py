@@ -22,6 +22,10 @@ page describes them as that projection's low-rank activations):
 segments, lora_A stacked (lora_num, rank, hidden); see ``sgmv_oracle.h``
 for the readings it takes where the page is silent.
 
+``fused`` is the two composed: ``shrink`` into outputs of the weights'
+16-bit dtype, then ``expand`` of those outputs (the fused LoRA delta of a
+QKV or gate/up layer); it adds no arithmetic of its own.
+
 Arrays are numpy: 16-bit storage as ``uint16`` bit patterns, float32 as
 ``float32``.  Dtype names are "f16", "bf16", "f32".
 """
@@ -300,3 +304,32 @@ def shrink(x: np.ndarray, x_dtype: str, lora_a: Sequence[np.ndarray], a_dtype: s
     if not want_ref:
         return None
     return [ref[i * T * K:(i + 1) * T * K].reshape(T, K) for i in range(len(outs))]
+
+
+def fused(x: np.ndarray, x_dtype: str, lora_a: Sequence[np.ndarray],
+          lora_b: Sequence[np.ndarray], w_dtype: str, offsets: Sequence[int], out: np.ndarray,
+          out_dtype: str, start, lens, idx, scale: float, add_inputs: bool,
+          want_ref: bool = False, threads: int = 0):
+    """The fused LoRA delta, in place on ``out``: for each slice s, the
+    projection y_s = shrink(x, lora_a[s]) rounded to ``w_dtype`` (the
+    weights' dtype), then expand(y_s, lora_b[s]) into the window at
+    offsets[s].  Returns (the projections, one (T, K) ``w_dtype`` array per
+    slice -- zero in rows without an adapter -- and, if ``want_ref``, the
+    expand's exact values per slice as ``expand`` returns them)."""
+    T = x.shape[0]
+    L, K = lora_a[0].shape[0], lora_a[0].shape[1]
+    ys = [np.zeros((T, K), dtype=_STORAGE[w_dtype]) for _ in lora_a]
+    shrink(x, x_dtype, lora_a, w_dtype, ys, w_dtype, start, lens, idx, scale, threads=threads)
+    slices = [Slice(y, w_dtype, np.ascontiguousarray(b), w_dtype, int(off))
+              for y, b, off in zip(ys, lora_b, offsets)]
+    ref = expand(slices, out, out_dtype, start, lens, idx, add_inputs, K, L, want_ref=want_ref,
+                 threads=threads)
+    return ys, ref
+
+
+def fused_slices(ys: Sequence[np.ndarray], lora_b: Sequence[np.ndarray], w_dtype: str,
+                 offsets: Sequence[int]):
+    """The expand slices of a fused call, given its projections (for
+    ``check``)."""
+    return [Slice(y, w_dtype, np.ascontiguousarray(b), w_dtype, int(off))
+            for y, b, off in zip(ys, lora_b, offsets)]

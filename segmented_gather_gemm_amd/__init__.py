@@ -12,8 +12,9 @@ Lorax SGMV Expand Slice Kernel" (Signature; I/O Contract):
                       seq_len_tensor, lora_indices_tensor, batches,
                       max_seq_length, slice_offset, slice_size, add_inputs=False)
 
-plus the LoRA-A projection that produces those inputs (sgmv_shrink) and the
-per-token and multi-slice forms.
+plus the LoRA-A projection that produces those inputs (sgmv_shrink), the
+per-token and multi-slice forms, and the two steps fused in one launch
+(sgmv_fused_shrink_expand).
 """
 from __future__ import annotations
 
@@ -26,11 +27,12 @@ LIBRARY_PATH = os.path.join(_HERE, "libsgmv.so")
 
 SGMV_OK, SGMV_ERR_INVALID_ARGUMENT, SGMV_ERR_UNSUPPORTED, SGMV_ERR_HIP = range(4)
 MAX_SLICES = 8
+MAX_FUSED_SLICES = 3
 
 # Every symbol include/sgmv.h declares.
 EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_bgmv_expand_slice",
-                    "sgmv_shrink", "sgmv_shrink_multi_slice", "sgmv_last_error",
-                    "sgmv_abi_version")
+                    "sgmv_shrink", "sgmv_shrink_multi_slice", "sgmv_fused_shrink_expand",
+                    "sgmv_last_error", "sgmv_abi_version")
 
 
 class Matrix(ctypes.Structure):
@@ -50,6 +52,10 @@ class SliceDesc(ctypes.Structure):
 
 class ShrinkSliceDesc(ctypes.Structure):
     _fields_ = [("lora_a", Stack), ("out", Matrix)]
+
+
+class FusedSliceDesc(ctypes.Structure):
+    _fields_ = [("lora_a", Stack), ("lora_b", Stack), ("slice_offset", ctypes.c_int64)]
 
 
 def _hip_runtimes_mapped():
@@ -94,6 +100,10 @@ def _load_library() -> ctypes.CDLL:
     lib.sgmv_shrink_multi_slice.argtypes = [Matrix, ctypes.POINTER(ShrinkSliceDesc), ctypes.c_int,
                                             p, p, p, i64, i64, ctypes.c_float, p]
     lib.sgmv_shrink_multi_slice.restype = ctypes.c_int
+    lib.sgmv_fused_shrink_expand.argtypes = [Matrix, ctypes.POINTER(FusedSliceDesc), ctypes.c_int,
+                                             Matrix, p, p, p, i64, i64, ctypes.c_float,
+                                             ctypes.c_int, p]
+    lib.sgmv_fused_shrink_expand.restype = ctypes.c_int
     lib.sgmv_last_error.argtypes = []
     lib.sgmv_last_error.restype = ctypes.c_char_p
     lib.sgmv_abi_version.argtypes = []
@@ -313,10 +323,49 @@ def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_s
     return [o for _, o in slices]
 
 
+def sgmv_fused_shrink_expand(inputs, slices: Sequence[Tuple[object, object, int]], output_tensor,
+                             b_seq_start_loc, seq_len_tensor, lora_indices_tensor, batches: int,
+                             max_seq_length: int, scaling: float = 1.0,
+                             add_inputs: bool = False):
+    """The LoRA-A projection and the expand of its result in one launch, for
+    the slices of a fused layer: for each (lora_a_weights (lora_num, rank,
+    hidden), lora_b_weights (lora_num, slice_size, rank), slice_offset),
+    output_tensor[start_b + m, off:off + slice_size] (+)= rne_w(scaling *
+    inputs[start_b + m] @ lora_a[idx].T) @ lora_b[idx].T, the projection
+    rounded to the weights' 16-bit dtype and never stored.  Equal to
+    sgmv_shrink_multi_slice into weight-dtype outputs followed by
+    sgmv_expand_multi_slice.  Enqueued on the current stream."""
+    if not 1 <= len(slices) <= MAX_FUSED_SLICES:
+        raise ValueError(f"1..{MAX_FUSED_SLICES} slices, got {len(slices)}")
+    device, (start, lens, idx) = _common(output_tensor, [
+        (b_seq_start_loc, "b_seq_start_loc"), (seq_len_tensor, "seq_len_tensor"),
+        (lora_indices_tensor, "lora_indices_tensor")])
+    if inputs.device != device:
+        raise ValueError(f"inputs must be on {device}")
+    if start.shape[0] < batches or lens.shape[0] < batches or idx.shape[0] < batches:
+        raise ValueError("segment metadata shorter than batches")
+    arr = (FusedSliceDesc * len(slices))()
+    for i, (a, w, off) in enumerate(slices):
+        if a.device != device or w.device != device:
+            raise ValueError(f"slice {i} must be on {device}")
+        arr[i] = FusedSliceDesc(_stack_a(a, f"slice {i} lora_a"), _stack(w, f"slice {i} lora_b"),
+                                int(off))
+    x = _matrix(inputs, "inputs")
+    out = _matrix(output_tensor, "output_tensor")
+    stream = _stream(device)
+    rc = _call_on(device, lib.sgmv_fused_shrink_expand, x, arr, len(slices), out,
+                  start.data_ptr(), lens.data_ptr(), idx.data_ptr(), int(batches),
+                  int(max_seq_length), float(scaling), int(bool(add_inputs)), stream)
+    if rc != SGMV_OK:
+        _raise(rc)
+    return output_tensor
+
+
 def abi_version() -> int:
     return lib.sgmv_abi_version()
 
 
 __all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "bgmv_expand_slice", "sgmv_shrink",
-           "sgmv_shrink_multi_slice", "abi_version", "SgmvError", "lib",
-           "Matrix", "Stack", "SliceDesc", "ShrinkSliceDesc", "EXPORTED_SYMBOLS", "LIBRARY_PATH"]
+           "sgmv_shrink_multi_slice", "sgmv_fused_shrink_expand", "abi_version", "SgmvError",
+           "lib", "Matrix", "Stack", "SliceDesc", "ShrinkSliceDesc", "FusedSliceDesc",
+           "EXPORTED_SYMBOLS", "LIBRARY_PATH"]

@@ -27,7 +27,9 @@ SOURCES = [os.path.join(CSRC, f) for f in
            ("sgmv_api.cpp", "sgmv_host.cpp", "sgmv_shrink_api.cpp", "sgmv_generic.hip", "sgmv_fast_ks0.hip", "sgmv_fast_ks1.hip",
             "sgmv_fast_ks2.hip", "sgmv_fast_ks4.hip", "sgmv_fast_ks8.hip",
             "sgmv_shrink_generic.hip", "sgmv_shrink_k1.hip", "sgmv_shrink_k2.hip",
-            "sgmv_shrink_k4.hip", "sgmv_shrink_k8.hip", "sgmv_shrink_k16.hip")]
+            "sgmv_shrink_k4.hip", "sgmv_shrink_k8.hip", "sgmv_shrink_k16.hip",
+            "sgmv_fused_api.cpp", "sgmv_fused_k1.hip", "sgmv_fused_k2.hip", "sgmv_fused_k4.hip",
+            "sgmv_fused_k8.hip")]
 
 STREAM_SOURCE = os.path.join(CSRC, "sgmv_stream.hip")
 STREAM_LIBRARY = os.path.join(HERE, "libsgmv_stream.so")

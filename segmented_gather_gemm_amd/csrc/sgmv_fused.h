@@ -1,0 +1,331 @@
+// sgmv_fused.h -- gfx950 device code for the fused LoRA delta (included by
+// the fused kernel translation units; internal to libsgmv): the LoRA-A
+// projection (shrink) and the SGMV expand-slice of its result in one launch,
+// with the projected rows kept on chip.
+//
+// Operation.  The wiki page "Implementation: Predibase Lorax SGMV Expand
+// Slice Kernel" describes the expand's inputs as the rank-sized activations
+// of the A-side LoRA projection (I/O Contract, Inputs; Usage Examples) and
+// motivates the slice kernel by a later operator that fuses several slice
+// operations in one launch (Description; Usage: fused QKV and gate/up
+// layers).  For segment b with adapter a = idx[b] in [0, lora_num), each row
+// t of it and each slice s:
+//     y_s[t][k] = rne_w(scale * sum_h x[t][h] * A_s[a][k][h]),    k < K,
+//     out[t][off_s + n] = rne_o((add ? out[t][off_s + n] : 0)
+//                               + sum_k y_s[t][k] * B_s[a][n][k]),  n < N_s,
+// with rne_w the rounding to the 16-bit weight dtype -- exactly what
+// sgmv_shrink_multi_slice into weight-dtype outputs followed by
+// sgmv_expand_multi_slice computes, without storing y.
+//
+// Design (MI355X-first).  A work unit is a 64-row tile of one segment, the
+// split-T shrink's unit.  Phase 1 runs the split-T contraction over the
+// whole hidden dimension (SplitTCore: coalesced input and lora_A loads
+// staged through LDS, MFMAs with lora_A rows as the A operand) and writes
+// the unit's projected rows, scaled and rounded as the shrink stores them,
+// into LDS in the expand's operand layout.  Phase 2 sweeps every 256-column
+// tile of every slice: each wave owns 64 columns, holds their lora_B rows
+// in VGPRs (the A operand, rows permuted as in the expand so that each lane
+// ends with 8 consecutive columns of one token), reads the projected rows
+// from LDS as the B operand for the unit's four 16-token tiles, seeds the
+// accumulators with the prior output (add_inputs) and writes the result
+// row-wise through a per-wave LDS tile with non-temporal device-scope
+// stores -- the expand's epilogue.  The next column tile's lora_B rows and
+// prior output are loaded while the current one computes.  Each accumulator
+// sees the same MFMAs in the same order as in the split-T shrink and the
+// expand kernels, so the result equals, bit for bit, those two calls when
+// the shrink takes its split-T form.
+//
+// The fused form saves the projection's round trip through memory and a
+// second launch, and lets one workgroup's projection (read-heavy) overlap
+// another's expansion (write-heavy); it re-reads each adapter's lora_B once
+// per 64-row unit (from L2), where the expand keeps a weight tile for up to
+// 512 rows.
+#pragma once
+
+#include "sgmv_device.h"
+#include "sgmv_fused_launch.h"
+#include "sgmv_shrink.h"
+
+#ifndef SGMV_FUSED_STAGE_REGS
+#define SGMV_FUSED_STAGE_REGS 192
+#endif
+
+namespace sgmv {
+namespace dev {
+
+template <int XD, int WD, int OD, bool ADD, int K16, int NS>
+__global__ __launch_bounds__(kThreads) void fused_shrink_expand(const FusedParams p) {
+  using Core = SplitTCore<XD, WD, K16, NS>;
+  constexpr int kSteps = K16 >= 2 ? K16 / 2 : 1;  // 32-wide rank steps of the expand
+  constexpr int kKB = 4 * kSteps;                  // 16-byte blocks of a projected row
+  constexpr int kTT = kFusedTokens / kTileRows;    // 16-token tiles per unit
+  constexpr int ob = OD == F32 ? 4 : 2;
+  // Output tile of a wave and token tile (16 rows x 64 columns), accessed
+  // row-wise kLPR lanes per row through the per-wave LDS tile, as in the
+  // expand (block b of row r in slot kNB r + (b ^ (r mod kNB))).
+  constexpr int kNB = 64 * ob / 16;
+  constexpr int kLPR = kNB;
+  constexpr int kRPI = 64 / kLPR;
+  constexpr int kOAcc = 2 * raw_vecs<OD>();
+  static_assert(kOAcc * kRPI == kTileRows, "row-wise accesses cover the tile");
+  static_assert(kKB == 4 || kKB == 8 || kKB == 16, "projected row blocks");
+  // Phase-2 ring depth: as many stages (lora_B rows, and the prior output
+  // with add_inputs) as about SGMV_FUSED_STAGE_REGS registers hold, 2 to 6.
+  constexpr int kStageRegs = 16 * kSteps + (ADD ? 4 * kTT * kOAcc : 0);
+  constexpr int kRingFit = SGMV_FUSED_STAGE_REGS / kStageRegs;
+  constexpr int kFusedRing = kRingFit < 2 ? 2 : (kRingFit > 6 ? 6 : kRingFit);
+  prefetch_params(p);
+  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
+  __shared__ int32_t wave_total[kWaves];
+  __shared__ typename Core::ALds a_lds;
+  __shared__ typename Core::XLds x_lds;
+  // The unit's projected rows per slice: 64 rows x kKB 16-byte blocks of
+  // 16-bit values (rank kept to 32 kSteps, zero past 16 K16).  Block kb of
+  // row t in slot t kKB + (kb ^ sw(t)): the expand's operand reads (8 lanes
+  // of one g: rows t .. t + 7 at one block) then hit 8 slot classes mod 8.
+  __shared__ u32x4 y_lds[NS][kFusedTokens * kKB];
+  __shared__ u32x4 o_lds[kWaves][kTileRows * kNB];
+  auto y_slot = [](int t, int kb) __attribute__((always_inline)) -> int {
+    const int sw = kKB >= 8 ? (t & 7) : ((t >> 1) & 3);
+    return t * kKB + (kb ^ sw);
+  };
+  const SegTable tab = seg_table(lds, p.batches);
+  const int32_t U = build_tile_table(p, tab, wave_total, kFusedTokens);
+  if (U == 0) return;
+  uint32_t u, u_end;
+  unit_range(p, (uint32_t)U, &u, &u_end);
+  if (u >= u_end) return;
+
+  Core core(p, a_lds, x_lds);
+  const int lane = core.lane, wave = core.wave, g = core.g, j = core.j;
+  const int K = p.K;
+  if constexpr (16 * K16 < 32 * kSteps) {
+    // rank 16 and below: the expand's rank step also reads k 16 .. 31, which
+    // the projection never writes; they stay zero (ordered before the first
+    // read by the barriers of the first unit's projection)
+    for (int i = threadIdx.x; i < NS * kFusedTokens; i += kThreads) {
+      const int s = i / kFusedTokens, t = i % kFusedTokens;
+      for (int kb = 2 * K16; kb < kKB; ++kb) y_lds[s][y_slot(t, kb)] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // Phase-2 lane constants (see the expand kernel): this lane's block of a
+  // row-wise access and its byte offsets within the unit's rows.
+  const int orow = lane / kLPR, oblk = lane % kLPR;
+  const int ocol = oblk * (16 / ob);
+  auto o_slot = [](int r, int b) __attribute__((always_inline)) -> int {
+    return kNB * r + (b ^ (r % kNB));
+  };
+  auto acc_blk = [&](int q, int v) __attribute__((always_inline)) -> int {
+    return raw_vecs<OD>() == 1 ? 4 * q + g : 2 * (4 * q + g) + v;
+  };
+  const uint32_t orb = (uint32_t)p.out_row_bytes;  // 64 rows span < 2 GiB (host)
+  uint32_t o_row_off[kTT][kOAcc];
+#pragma unroll
+  for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+    for (int m = 0; m < kOAcc; ++m)
+      o_row_off[tt][m] = (uint32_t)(kTileRows * tt + m * kRPI + orow) * orb + (uint32_t)(oblk * 16);
+  auto w_off = [&](int s, int ks) __attribute__((always_inline)) -> uint32_t {
+    const int kb = 32 * ks + 8 * g;
+    return kb < K ? (uint32_t)((weight_row(0, s, j) * K + kb) * 2) : kOut;
+  };
+
+  // One column tile of phase 2 as this wave sees it.
+  struct Tile {
+    rsrc_t w;            // lora_B rows [col0, col0 + n_rem) of the unit's adapter
+    uint32_t col_bytes;  // byte offset of column off_s + col0 within a row
+    int32_t n_rem;       // columns of the wave (<= 0: none)
+    int si;              // slice
+  };
+  struct Stage {
+    u32x4 w[4][kSteps];
+    u32x4 o[ADD ? kTT : 1][ADD ? kOAcc : 1];
+  };
+
+  int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
+  for (; u < u_end; ++u) {
+    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
+    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kFusedTokens);
+    const int64_t a = uniform(tab.seg_lora[b]);
+
+    // Phase 1: the unit's projection, scaled and rounded to the weight
+    // dtype as the shrink stores it, into y_lds.  The barrier first orders
+    // the previous unit's reads of y_lds before these writes.
+    {
+      f32x4 acc[Core::kTok][Core::kKt];
+      core.run(su, acc);
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < Core::kTok; ++h)
+#pragma unroll
+        for (int i = 0; i < Core::kKt; ++i) {
+          const int kg = core.k_tile(i);
+          const int si = kg / K16, kt = kg % K16;
+          const int t = kTileRows * core.tok_tile(h) + j;
+          const f32x4 v = acc[h][i] * p.scale;
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          u32x2* dst = reinterpret_cast<u32x2*>(&y_lds[si][y_slot(t, 2 * kt + (g >> 1))]) + (g & 1);
+          *dst = u32x2{pack2<WD>(v[0], v[1]), pack2<WD>(v[2], v[3])};
+        }
+      __syncthreads();
+    }
+
+    // Phase 2: every column tile of every slice.
+    const rsrc_t orc = make_rsrc(static_cast<char*>(p.out) + (int64_t)su.row0 * p.out_row_bytes,
+                                 (int64_t)su.rows * p.out_row_bytes);
+    auto tile_at = [&](int ct) __attribute__((always_inline)) -> Tile {
+      int si = 0;
+#pragma unroll
+      for (int s = 1; s < NS; ++s)
+        if (ct >= p.s[s].tile_begin) si = s;
+      const FusedSliceDesc& S = p.s[si];
+      const int32_t col0 = (ct - S.tile_begin) * kTileCols + wave * kWaveCols;
+      const int64_t left = ct < p.total_tiles ? S.n - col0 : 0;
+      Tile tl;
+      tl.si = si;
+      tl.n_rem = left <= 0 ? 0 : (left > kWaveCols ? kWaveCols : (int32_t)left);
+      tl.col_bytes = (uint32_t)((S.offset + col0) * ob);
+      tl.w = make_rsrc(static_cast<const char*>(S.w) + (a * S.n + col0) * K * 2,
+                       (int64_t)tl.n_rem * K * 2);
+      return tl;
+    };
+    auto load_stage = [&](Stage& st, const Tile& tl) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) buf_load8<WD>(tl.w, w_off(s, ks), &st.w[s][ks]);
+      if constexpr (ADD) {
+#pragma unroll
+        for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+          for (int m = 0; m < kOAcc; ++m)
+            st.o[tt][m] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           orc, ocol < tl.n_rem ? o_row_off[tt][m] + tl.col_bytes : kOut, 0, 0));
+      }
+    };
+    auto compute_store = [&](const Stage& st, const Tile& tl) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        f32x4 acc[4];
+        if constexpr (ADD) {
+          // row-wise prior output -> the wave's LDS tile -> accumulator layout
+#pragma unroll
+          for (int m = 0; m < kOAcc; ++m) o_lds[wave][o_slot(m * kRPI + orow, oblk)] = st.o[tt][m];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+          if constexpr (ADD) {
+            u32x4 raw[raw_vecs<OD>()];
+#pragma unroll
+            for (int rv = 0; rv < raw_vecs<OD>(); ++rv)
+              raw[rv] = o_lds[wave][o_slot(j, acc_blk(q, rv))];
+            out_values<OD>(raw, v);
+          }
+          acc[2 * q] = f32x4{v[0], v[1], v[2], v[3]};
+          acc[2 * q + 1] = f32x4{v[4], v[5], v[6], v[7]};
+        }
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+          const u32x4 yo = y_lds[tl.si][y_slot(kTileRows * tt + j, 4 * ks + g)];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[s] = mfma<WD>(st.w[s][ks], yo, acc[s]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float v[8] = {acc[2 * q][0], acc[2 * q][1], acc[2 * q][2], acc[2 * q][3],
+                              acc[2 * q + 1][0], acc[2 * q + 1][1], acc[2 * q + 1][2],
+                              acc[2 * q + 1][3]};
+          u32x4 raw[raw_vecs<OD>()];
+          out_pack<OD>(v, raw);
+#pragma unroll
+          for (int rv = 0; rv < raw_vecs<OD>(); ++rv)
+            o_lds[wave][o_slot(j, acc_blk(q, rv))] = raw[rv];
+        }
+        // rows past the unit's tokens lie outside orc; columns past the
+        // slice take the out-of-range offset
+#pragma unroll
+        for (int m = 0; m < kOAcc; ++m)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              o_lds[wave][o_slot(m * kRPI + orow, oblk)], orc,
+              ocol < tl.n_rem ? o_row_off[tt][m] + tl.col_bytes : kOut, 0, kStream);
+      }
+    };
+
+    // A ring of kRing stages: the loads of column tile c + kRing - 1 are
+    // issued before tile c computes and stores.  On gfx9 the vector-memory
+    // counter covers stores as well as loads and retires in issue order, so
+    // waiting for a tile's loads also waits for every store issued before
+    // them: with the loads kRing - 1 tiles ahead, a tile's stores have
+    // kRing - 1 tiles of work to complete before anything waits on them
+    // (with one tile ahead, every tile paid a store round trip: fused
+    // gate/up 3.7 us per tile).  The loop runs over whole turns of the
+    // ring; positions past the last tile load nothing and store nothing.
+    constexpr int kRing = kFusedRing;
+    Stage ring[kRing];
+    Tile tr[kRing];
+#pragma unroll
+    for (int d = 0; d + 1 < kRing; ++d) {
+      tr[d] = tile_at(d);
+      load_stage(ring[d], tr[d]);
+    }
+    for (int ct = 0; ct < p.total_tiles; ct += kRing) {
+#pragma unroll
+      for (int d = 0; d < kRing; ++d) {
+        const int nxt = (d + kRing - 1) % kRing;
+        tr[nxt] = tile_at(ct + d + kRing - 1);
+        load_stage(ring[nxt], tr[nxt]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_store(ring[d], tr[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel tables.
+// ---------------------------------------------------------------------------
+
+template <int XD, int WD, int OD, int K16>
+const void* fused_by_ns(bool add, int ns) {
+  auto pick = [&](auto nsc) -> const void* {
+    constexpr int NS = decltype(nsc)::value;
+    if constexpr (K16 * NS > 16) {
+      return nullptr;
+    } else {
+      return add ? reinterpret_cast<const void*>(&fused_shrink_expand<XD, WD, OD, true, K16, NS>)
+                 : reinterpret_cast<const void*>(&fused_shrink_expand<XD, WD, OD, false, K16, NS>);
+    }
+  };
+  switch (ns) {
+    case 1: return pick(std::integral_constant<int, 1>{});
+    case 2: return pick(std::integral_constant<int, 2>{});
+    case 3: return pick(std::integral_constant<int, 3>{});
+    default: return nullptr;
+  }
+}
+
+template <int XD, int WD, int K16>
+const void* fused_by_out(int od, bool add, int ns) {
+  switch (od) {
+    case F16: return fused_by_ns<XD, WD, F16, K16>(add, ns);
+    case BF16: return fused_by_ns<XD, WD, BF16, K16>(add, ns);
+    case F32: return fused_by_ns<XD, WD, F32, K16>(add, ns);
+    default: return nullptr;
+  }
+}
+
+template <int K16>
+const void* fused_table(int xd, int wd, int od, bool add, int ns) {
+  if (wd == BF16 && xd == BF16) return fused_by_out<BF16, BF16, K16>(od, add, ns);
+  if (wd == BF16 && xd == F32) return fused_by_out<F32, BF16, K16>(od, add, ns);
+  if (wd == F16 && xd == F16) return fused_by_out<F16, F16, K16>(od, add, ns);
+  if (wd == F16 && xd == F32) return fused_by_out<F32, F16, K16>(od, add, ns);
+  return nullptr;
+}
+
+}  // namespace dev
+}  // namespace sgmv

@@ -1,0 +1,12 @@
+// Fused LoRA delta kernels (shrink and expand in one launch) for ranks of
+// 8 k tile(s) of 16 rows per slice.  Device code and design notes:
+// sgmv_fused.h.
+#include "sgmv_fused.h"
+
+namespace sgmv {
+
+const void* fused_kernel_k8(int xd, int wd, int od, bool add, int ns) {
+  return dev::fused_table<8>(xd, wd, od, add, ns);
+}
+
+}  // namespace sgmv

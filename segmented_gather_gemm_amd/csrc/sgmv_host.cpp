@@ -51,7 +51,7 @@ hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups
     int blocks = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, sgmv::kThreads, bucket);
     if (e != hipSuccess) return e;
-    occ = g_occupancy.emplace(key, blocks > 0 ? blocks : 1).first;
+    occ = g_occupancy.emplace(key, blocks > 0 ? blocks : 0).first;
   }
   *workgroups = cu->second * occ->second;
   return hipSuccess;

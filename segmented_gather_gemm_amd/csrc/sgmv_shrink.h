@@ -93,8 +93,8 @@ struct ShrinkUnit {
   rsrc_t a[NS];
 };
 
-template <int NS>
-__device__ __forceinline__ ShrinkUnit<NS> shrink_unit(const ShrinkParams& p, const SegTable& tab,
+template <int NS, typename P>
+__device__ __forceinline__ ShrinkUnit<NS> shrink_unit(const P& p, const SegTable& tab,
                                                       int b, uint32_t u, int32_t tile_rows) {
   ShrinkUnit<NS> su;
   su.row0 = uniform(tab.seg_row[b]) + ((int32_t)u - uniform(tab.tile_start[b])) * tile_rows;
@@ -339,88 +339,102 @@ struct SplitTBlock {
   u32x4 a[NS][Sh::kPairs];           // this wave's share of the block's lora_A tiles
 };
 
-template <int XD, int WD, int OD, int K16, int NS>
-__global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p) {
+// The split-T contraction of one 64-token unit, shared by the shrink kernel
+// and the fused shrink-expand kernel: `run` leaves in acc[h][i] this wave's
+// fp32 sums (unscaled) of token tile tok_tile(h) and k tile k_tile(i) (k
+// tile i of the launch is tile i % K16 of slice i / K16); lane (j, g) holds
+// k = 16 (i % K16) + 4 g .. + 3 of token 16 tok_tile(h) + j.  The LDS
+// staging buffers are the caller's (declared in the kernel).  P: a
+// parameter block with the ShrinkParams fields x_row_bytes, H, steps and
+// s[].a.
+//
+// With an even number of k tiles, at least 4, the waves form a 2 x 2 grid:
+// wave w takes token tiles 2 (w % 2) and 2 (w % 2) + 1 and the k tiles of
+// half w / 2.  Each lora_A fragment read from LDS then feeds two MFMAs and
+// each input fragment kT / 2, so a step takes 2 + kT / 2 fragment reads
+// per wave instead of 1 + kT.  Otherwise wave t takes token tile t and every
+// k tile.  Either way each accumulator sees the same MFMAs in the same
+// order.
+template <int XD, int WD, int K16, int NS>
+struct SplitTCore {
   using Sh = ShrinkShape<XD, K16, NS>;
   using Block = SplitTBlock<XD, K16, NS>;
-  constexpr int kT = Sh::kTiles;
-  constexpr int kB = Sh::kBlockT;
-  constexpr int kP = Sh::kPairs;
-  constexpr int xb = XD == F32 ? 4 : 2;
-  constexpr int kBuf = kT * kB;  // fragments of one block
-  // With an even number of k tiles, at least 4, the waves form a 2 x 2 grid:
-  // wave w takes token tiles 2 (w % 2) and 2 (w % 2) + 1 and the k tiles of
-  // half w / 2.  Each lora_A fragment read from LDS then feeds two MFMAs and
-  // each input fragment kT / 2, so a step takes 2 + kT / 2 fragment reads
-  // per wave instead of 1 + kT (LDS throughput bounds this kernel).
-  // Otherwise wave t takes token tile t and every k tile.  Either way each
-  // accumulator sees the same MFMAs in the same order.
-  constexpr bool kGrid = kT >= 4 && kT % 2 == 0;
-  constexpr int kTok = kGrid ? 2 : 1;       // token tiles per wave
-  constexpr int kKt = kGrid ? kT / 2 : kT;  // k tiles per wave
-  prefetch_params(p);
-  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
-  __shared__ int32_t wave_total[kWaves];
-  // lora_A fragments of a block per buffer: [buffer][tile i * kB + step]
-  // [slot] (see frag_slot)
-  __shared__ u32x4 a_lds[2][kBuf][kFragSlots];
-  // input fragments of a block by token tile (the tile wave t loads); in
-  // the 2 x 2 grid two waves read each tile, so two buffers as for lora_A,
-  // otherwise a tile is private to its wave and one buffer does
-  __shared__ u32x4 x_lds[kGrid ? 2 : 1][kWaves][kB][kFragSlots];
-  const SegTable tab = seg_table(lds, p.batches);
-  const int32_t U = build_tile_table(p, tab, wave_total, kShrinkTokensSplitT);
-  if (U == 0) return;
-  uint32_t u, u_end;
-  unit_range(p, (uint32_t)U, &u, &u_end);
-  if (u >= u_end) return;
+  static constexpr int kT = Sh::kTiles;
+  static constexpr int kB = Sh::kBlockT;
+  static constexpr int kP = Sh::kPairs;
+  static constexpr int xb = XD == F32 ? 4 : 2;
+  static constexpr int kBuf = kT * kB;  // fragments of one block
+  static constexpr bool kGrid = kT >= 4 && kT % 2 == 0;
+  static constexpr int kTok = kGrid ? 2 : 1;       // token tiles per wave
+  static constexpr int kKt = kGrid ? kT / 2 : kT;  // k tiles per wave
+  static constexpr int kXBuf = kGrid ? 2 : 1;
+  // lora_A fragments of a block per buffer: [buffer][tile i * kB + step][slot]
+  // (see frag_slot); input fragments of a block by token tile (the tile
+  // wave t loads); in the 2 x 2 grid two waves read each tile, so two
+  // buffers as for lora_A, otherwise a tile is private to its wave and one
+  // buffer does.
+  typedef u32x4 ALds[2][kBuf][kFragSlots];
+  typedef u32x4 XLds[kXBuf][kWaves][kB][kFragSlots];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int tw = wave;  // token tile this wave loads
-  const int th = wave & 1, kh = wave >> 1;  // 2 x 2 grid: token pair, k half
-  const int g = lane >> 4;
-  const int j = lane & 15;
-  const int32_t H = p.H;
-  const int32_t n_steps = p.steps;  // loop positions per unit, a multiple of kD kB
-  const int32_t h_steps = (H + 31) >> 5;  // hidden steps
-  const uint32_t xrb = (uint32_t)p.x_row_bytes;  // 64 rows span < 2 GiB (host)
-  // Input loads of a block, xq < kB: rows 16 tw + 8 (xq & 1) .. + 7 over steps
-  // 2 (xq >> 1), + 1; lane l reads row + l / 8, elements 8 (l % 8) .. of the
-  // span (hidden block l % 4 of step 2 (xq >> 1) + (l % 8) / 4).
-  const int lr = lane >> 3, lb = lane & 7;
-  uint32_t x_lane[2];  // by xq & 1: row offset + the lane's element offset in the span
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-    x_lane[h2] = (uint32_t)(16 * tw + 8 * h2 + lr) * xrb + (uint32_t)(8 * lb * xb);
-  const int x_slot[2] = {frag_slot(lr, lb & 3), frag_slot(8 + lr, lb & 3)};
-  // This wave's lora_A loads of every slice's block: load pr = 4 q + tw
-  // covers rows 16 kt + 8 half .. + 7 over steps 2 sp, 2 sp + 1 of the block
-  // (kt = pr / kB, half and sp from pr % kB); lane l reads row + l / 8,
-  // bytes 16 (l % 8) of the 128-byte span, which is hidden block l % 4 of
-  // step 2 sp + (l % 8) / 4.
+  ALds& a_lds;
+  XLds& x_lds;
+  int lane, wave, tw, th, kh, g, j, lr, lb;
+  int32_t H, n_steps, h_steps;
+  uint32_t xrb;
+  uint32_t x_lane[2];
+  int x_slot[2];
   uint32_t a_lane[kP];  // row offset + byte offset within the span
   int a_step[kP];       // step of this lane's 16 bytes within the block
   int a_frag[kP];       // fragment within a slice's part of the block, and slot
   int a_slot[kP];
+  int r_slot;
+
+  __device__ __forceinline__ int tok_tile(int h) const { return kGrid ? 2 * th + h : tw; }
+  __device__ __forceinline__ int k_tile(int i) const { return (kGrid ? kh * kKt : 0) + i; }
+
+  template <typename P>
+  __device__ __forceinline__ SplitTCore(const P& p, ALds& a, XLds& x) : a_lds(a), x_lds(x) {
+    lane = threadIdx.x & 63;
+    wave = uniform(threadIdx.x >> 6);
+    tw = wave;  // token tile this wave loads
+    th = wave & 1;
+    kh = wave >> 1;  // 2 x 2 grid: token pair, k half
+    g = lane >> 4;
+    j = lane & 15;
+    H = p.H;
+    n_steps = p.steps;  // loop positions per unit, a multiple of kD kB
+    h_steps = (H + 31) >> 5;  // hidden steps
+    xrb = (uint32_t)p.x_row_bytes;  // 64 rows span < 2 GiB (host)
+    // Input loads of a block, xq < kB: rows 16 tw + 8 (xq & 1) .. + 7 over
+    // steps 2 (xq >> 1), + 1; lane l reads row + l / 8, elements 8 (l % 8) ..
+    // of the span (hidden block l % 4 of step 2 (xq >> 1) + (l % 8) / 4).
+    lr = lane >> 3;
+    lb = lane & 7;
 #pragma unroll
-  for (int q = 0; q < kP; ++q) {
-    const int pr = kWaves * q + tw;
-    const int kt = pr / kB, r = pr % kB;
-    const int half = r & 1, sp = r >> 1;
-    const int row = 16 * kt + 8 * half + lr;
-    a_lane[q] = (uint32_t)row * (uint32_t)H * 2u + (uint32_t)(16 * lb);
-    a_step[q] = 2 * sp + (lb >> 2);
-    a_frag[q] = kt * kB + a_step[q];
-    a_slot[q] = frag_slot(8 * half + lr, lb & 3);
+    for (int h2 = 0; h2 < 2; ++h2)
+      x_lane[h2] = (uint32_t)(16 * tw + 8 * h2 + lr) * xrb + (uint32_t)(8 * lb * xb);
+    x_slot[0] = frag_slot(lr, lb & 3);
+    x_slot[1] = frag_slot(8 + lr, lb & 3);
+    // This wave's lora_A loads of every slice's block: load pr = 4 q + tw
+    // covers rows 16 kt + 8 half .. + 7 over steps 2 sp, 2 sp + 1 of the
+    // block (kt = pr / kB, half and sp from pr % kB); lane l reads row +
+    // l / 8, bytes 16 (l % 8) of the 128-byte span, which is hidden block
+    // l % 4 of step 2 sp + (l % 8) / 4.
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+      const int pr = kWaves * q + tw;
+      const int kt = pr / kB, r = pr % kB;
+      const int half = r & 1, sp = r >> 1;
+      const int row = 16 * kt + 8 * half + lr;
+      a_lane[q] = (uint32_t)row * (uint32_t)H * 2u + (uint32_t)(16 * lb);
+      a_step[q] = 2 * sp + (lb >> 2);
+      a_frag[q] = kt * kB + a_step[q];
+      a_slot[q] = frag_slot(8 * half + lr, lb & 3);
+    }
+    r_slot = frag_slot(j, g);  // this lane's slot when reading a fragment
   }
-  const int r_slot = frag_slot(j, g);  // this lane's slot when reading a fragment
 
-  int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
-  for (; u < u_end; ++u) {
-    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
-    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kShrinkTokensSplitT);
-
+  __device__ __forceinline__ void run(const ShrinkUnit<NS>& su, f32x4 (&acc)[kTok][kKt]) {
     auto load_block = [&](Block& blk, int32_t v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int xq = 0; xq < kB; ++xq) {
@@ -454,7 +468,6 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
             x_operand<XD, WD>(blk.x[xq]);
       __syncthreads();
     };
-    f32x4 acc[kTok][kKt];
 #pragma unroll
     for (int h = 0; h < kTok; ++h)
 #pragma unroll
@@ -498,13 +511,37 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+};
 
+template <int XD, int WD, int OD, int K16, int NS>
+__global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p) {
+  using Core = SplitTCore<XD, WD, K16, NS>;
+  prefetch_params(p);
+  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
+  __shared__ int32_t wave_total[kWaves];
+  __shared__ typename Core::ALds a_lds;
+  __shared__ typename Core::XLds x_lds;
+  const SegTable tab = seg_table(lds, p.batches);
+  const int32_t U = build_tile_table(p, tab, wave_total, kShrinkTokensSplitT);
+  if (U == 0) return;
+  uint32_t u, u_end;
+  unit_range(p, (uint32_t)U, &u, &u_end);
+  if (u >= u_end) return;
+
+  Core core(p, a_lds, x_lds);
+  int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
+  for (; u < u_end; ++u) {
+    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
+    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kShrinkTokensSplitT);
+    f32x4 acc[Core::kTok][Core::kKt];
+    core.run(su, acc);
 #pragma unroll
-    for (int h = 0; h < kTok; ++h)
+    for (int h = 0; h < Core::kTok; ++h)
 #pragma unroll
-      for (int i = 0; i < kKt; ++i)
-        shrink_store<OD, K16>(p, (kGrid ? kh * kKt : 0) + i, su.row0, su.rows,
-                              16 * (kGrid ? 2 * th + h : tw), j, g, acc[h][i]);
+      for (int i = 0; i < Core::kKt; ++i)
+        shrink_store<OD, K16>(p, core.k_tile(i), su.row0, su.rows, 16 * core.tok_tile(h), core.j,
+                              core.g, acc[h][i]);
   }
 }
 

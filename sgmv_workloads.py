@@ -503,3 +503,121 @@ SHRINK_WORKLOADS: Dict[str, Callable[..., ShrinkWorkload]] = {
     "shrink_gate_up": shrink_gate_up,
     "shrink_skewed": shrink_skewed,
 }
+
+
+# ---------------------------------------------------------------------------
+# Fused LoRA delta workloads: the LoRA-A projection of the hidden states and
+# the expand of its result into the slices of a fused layer, in one call.
+# Same segment draws as the expand workload of the same layer; lora_A ~
+# N(0, 1/H) (the projection ~ N(0, 1)), lora_B ~ N(0, 0.02), inputs and
+# prior output ~ N(0, 1).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class FusedWorkload:
+    name: str
+    x: np.ndarray              # (T, H) hidden states, or wider rows
+    x_dtype: str
+    lora_a: List[np.ndarray]   # per slice (L, K, H) contiguous
+    lora_b: List[np.ndarray]   # per slice (L, N_s, K) contiguous
+    w_dtype: str               # dtype of lora_A and lora_B (and of the projection)
+    offsets: List[int]         # per slice: first output column
+    out0: np.ndarray           # (T, H_out) prior output
+    out_dtype: str
+    start: np.ndarray
+    lens: np.ndarray
+    idx: np.ndarray
+    scale: float
+    add: bool
+    K: int
+    L: int
+    seed: int = 0
+
+    @property
+    def T(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def batches(self) -> int:
+        return int(len(self.lens))
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.lens.max()) if len(self.lens) else 0
+
+    def active_mask(self) -> np.ndarray:
+        return (self.idx != -1) & (self.lens > 0)
+
+
+def _fused_parts(rng, T, H, K, L, slices, H_out, x_dtype, w_dtype, out_dtype, values="normal",
+                 x_pad=0, out_pad=0):
+    def draw(shape, sigma, lo, hi, dtype):
+        if values == "int":
+            return integers_as(rng, shape, lo, hi, dtype)
+        return normal(rng, shape, sigma, dtype)
+
+    sigma_a = 1.0 / math.sqrt(max(H, 1))
+    lora_a = [draw((L, K, H), sigma_a, -2, 2, w_dtype) for _ in slices]
+    lora_b = [draw((L, n, K), 0.02, -2, 2, w_dtype) for _, n in slices]
+    xfull = draw((T, H + x_pad), 1.0, -2, 2, x_dtype)
+    ofull = draw((T, H_out + out_pad), 1.0, -8, 8, out_dtype)
+    return (xfull[:, :H] if x_pad else xfull, lora_a, lora_b,
+            ofull[:, :H_out] if out_pad else ofull)
+
+
+def fused_qkv(seed: int = 0) -> FusedWorkload:
+    """Fused QKV LoRA delta: the 32 segments of gqa_qkv (lengths
+    log-uniform in [1, 2048]); hidden 4096 -> rank 32 -> Q [0, 4096),
+    K [4096, 5120), V [5120, 6144); 16 adapters, indices uniform in 0..15;
+    bf16 throughout; accumulate onto the prior output."""
+    base = gqa_qkv(seed)
+    rng = np.random.default_rng(seed + 2000)
+    H, K, L = 4096, 32, 16
+    x, la, lb, out0 = _fused_parts(rng, base.T, H, K, L, QKV_SLICES, 6144, "bf16", "bf16", "bf16")
+    return FusedWorkload("fused_qkv", x, "bf16", la, lb, "bf16", [o for o, _ in QKV_SLICES], out0,
+                         "bf16", base.start, base.lens, base.idx, 1.0, True, K, L, seed)
+
+
+def fused_gate_up(seed: int = 0) -> FusedWorkload:
+    """Fused gate/up LoRA delta: the 64 segments of mlp_gate_up (about 16k
+    tokens, lengths uniform in [1, 512]); hidden 4096 -> rank 64 -> gate
+    [0, 14336) and up [14336, 28672); 64 adapters; bf16 throughout;
+    overwrite."""
+    base = mlp_gate_up(seed)
+    rng = np.random.default_rng(seed + 2000)
+    H, K, L = 4096, 64, 64
+    sl = ((0, 14336), (14336, 14336))
+    x, la, lb, out0 = _fused_parts(rng, base.T, H, K, L, sl, 28672, "bf16", "bf16", "bf16")
+    return FusedWorkload("fused_gate_up", x, "bf16", la, lb, "bf16", [o for o, _ in sl], out0,
+                         "bf16", base.start, base.lens, base.idx, 1.0, False, K, L, seed)
+
+
+def fused_custom(lens: Sequence[int], idx: Sequence[int], *, H: int, K: int, L: int,
+                 slices: Sequence[tuple], H_out: int, x_dtype: str = "bf16",
+                 w_dtype: str = "bf16", out_dtype: str = "bf16", add: bool = False,
+                 scale: float = 1.0, seed: int = 0, start: Optional[Sequence[int]] = None,
+                 T: Optional[int] = None, values: str = "normal", x_pad: int = 0,
+                 out_pad: int = 0, name: str = "fused_custom") -> FusedWorkload:
+    """A fused workload with explicit segments and (offset, N) slices;
+    ``values`` "int" draws x, lora_A, lora_B in [-2, 2] and the prior in
+    [-8, 8]."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    start = exclusive_cumsum(lens) if start is None else np.asarray(start, dtype=np.int64)
+    if T is None:
+        T = int((start + lens).max()) if len(lens) else 0
+    x, la, lb, out0 = _fused_parts(rng, T, H, K, L, slices, H_out, x_dtype, w_dtype, out_dtype,
+                                   values, x_pad, out_pad)
+    return FusedWorkload(name, x, x_dtype, la, lb, w_dtype, [o for o, _ in slices], out0,
+                         out_dtype, start, lens, idx, float(scale), add, K, L, seed)
+
+
+FUSED_WORKLOADS: Dict[str, Callable[..., FusedWorkload]] = {
+    "fused_qkv": fused_qkv,
+    "fused_gate_up": fused_gate_up,
+}

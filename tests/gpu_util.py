@@ -219,3 +219,125 @@ def assert_shrink_parity(wl, cand_bits, rows=None, idx=None, exact=False):
                                f"err/tol {float(np.max(err / tol)):.3g}")
         n_checked += int(m.sum()) * wl.K
     return n_checked
+
+
+# --------------------------------------------------------------------------
+# Fused LoRA delta (shrink and expand in one call).
+# --------------------------------------------------------------------------
+
+class DeviceFused:
+    """A fused workload's tensors on the GPU."""
+
+    def __init__(self, wl, device="cuda"):
+        import torch
+        self.wl = wl
+        self.start = torch.from_numpy(wl.start).to(device)
+        self.lens = torch.from_numpy(wl.lens).to(device)
+        self.idx = torch.from_numpy(wl.idx).to(device)
+        self.x = to_device(wl.x, wl.x_dtype, device)
+        self.a = [to_device(np.ascontiguousarray(a).reshape(a.shape[0], -1), wl.w_dtype,
+                            device).view(a.shape) for a in wl.lora_a]
+        self.b = [to_device(np.ascontiguousarray(b).reshape(b.shape[0], -1), wl.w_dtype,
+                            device).view(b.shape) for b in wl.lora_b]
+        self.out0 = to_device(wl.out0, wl.out_dtype, device)
+
+    def fresh_out(self):
+        return _device_clone(self.out0)
+
+    def run(self, out=None):
+        import segmented_gather_gemm_amd as sg
+        wl = self.wl
+        out = self.fresh_out() if out is None else out
+        sg.sgmv_fused_shrink_expand(self.x, list(zip(self.a, self.b, wl.offsets)), out,
+                                    self.start, self.lens, self.idx, wl.batches,
+                                    wl.max_seq_len, wl.scale, wl.add)
+        return out
+
+    def run_two(self, out=None):
+        """The two-call path: sgmv_shrink_multi_slice into weight-dtype
+        projections, then sgmv_expand_multi_slice of them."""
+        import torch
+        import segmented_gather_gemm_amd as sg
+        wl = self.wl
+        out = self.fresh_out() if out is None else out
+        ys = [torch.zeros((wl.T, wl.K), dtype=torch_dtype(wl.w_dtype), device=out.device)
+              for _ in wl.lora_a]
+        sg.sgmv_shrink_multi_slice(self.x, list(zip(self.a, ys)), self.start, self.lens,
+                                   self.idx, wl.batches, wl.max_seq_len, wl.scale)
+        sg.sgmv_expand_multi_slice([(y, b, off) for y, b, off in zip(ys, self.b, wl.offsets)],
+                                   out, self.start, self.lens, self.idx, wl.batches,
+                                   wl.max_seq_len, wl.add)
+        return ys, out
+
+
+def fused_written_mask(wl):
+    rows = np.zeros(wl.T, dtype=bool)
+    for s, n, a in zip(wl.start, wl.lens, wl.idx):
+        if 0 <= a < wl.L and n > 0:
+            rows[s:s + n] = True
+    cols = np.zeros(wl.out0.shape[1], dtype=bool)
+    for off, b in zip(wl.offsets, wl.lora_b):
+        cols[off:off + b.shape[1]] = True
+    return rows, cols
+
+
+def assert_fused_parity(wl, cand_bits, exact=False):
+    """GPU output of a fused call vs oracle.fused: elements outside (active
+    rows x windows) keep their bits; with ``exact`` every bit equals the
+    oracle's (integer data); otherwise each written value is within
+
+        atol + rtol |R| + sum_k delta_k |B[a][n][k]|,
+        delta_k = ulp_w(2 (|y_k| + e_k)) + e_k,
+        e_k = |scale| (gamma_H + 2^-23) sum_h |x_h A[a][k][h]|,
+
+    of the exact expand R of the oracle's projection y: the GPU's fp32
+    projection differs from the exact one by at most e_k (summation of H
+    exact products in any order, then the scale's rounding), so its
+    rounding to the weight dtype can land at most delta_k from the oracle's;
+    atol and rtol cover the expand's own fp32 sums and final rounding.
+    Returns the number of values compared."""
+    from oracle_pins_util import np_cast_input, np_values, ulp
+    out = wl.out0.copy()
+    ys, refs = oracle.fused(wl.x, wl.x_dtype, wl.lora_a, wl.lora_b, wl.w_dtype, wl.offsets, out,
+                            wl.out_dtype, wl.start, wl.lens, wl.idx, wl.scale, wl.add,
+                            want_ref=True)
+    rows, cols = fused_written_mask(wl)
+    bits = cand_bits.view(np.uint32) if wl.out_dtype == "f32" else cand_bits
+    prior = wl.out0.view(np.uint32) if wl.out_dtype == "f32" else wl.out0
+    untouched = ~(rows[:, None] & cols[None, :])
+    assert np.array_equal(bits[untouched], prior[untouched]), \
+        f"{wl.name}: elements outside the written region changed"
+    if exact:
+        ob = out.view(np.uint32) if wl.out_dtype == "f32" else out
+        assert np.array_equal(bits, ob), f"{wl.name}: bits differ from the oracle"
+        return int(rows.sum() * cols.sum())
+    atol, rtol = TOLERANCE[wl.out_dtype]
+    gamma = wl.H * U_FP32 / (1.0 - wl.H * U_FP32) + 2.0 ** -23
+    x = np.abs(np_cast_input(np.ascontiguousarray(wl.x), wl.x_dtype, wl.w_dtype))
+    ra = np.full(wl.T, -1, dtype=np.int64)
+    for s, n, a in zip(wl.start, wl.lens, wl.idx):
+        if 0 <= a < wl.L and n > 0:
+            ra[s:s + n] = a
+    act = np.nonzero(rows)[0]
+    n_checked = 0
+    for y, a_s, b_s, off, ref in zip(ys, wl.lora_a, wl.lora_b, wl.offsets, refs):
+        N = b_s.shape[1]
+        av = np.abs(np_values(a_s, wl.w_dtype))
+        bv = np.abs(np_values(b_s, wl.w_dtype))
+        yv = np.abs(np_values(y, wl.w_dtype))
+        extra = np.zeros((wl.T, N))
+        for a in np.unique(ra[act]):
+            m = ra == a
+            e = abs(wl.scale) * gamma * (x[m] @ av[a].T)
+            delta = ulp(2.0 * (yv[m] + e), wl.w_dtype) + e
+            extra[m] = delta @ bv[a].T
+        got = np_values(np.ascontiguousarray(cand_bits[act][:, off:off + N]), wl.out_dtype)
+        exp = ref[act]
+        assert np.isfinite(got).all(), f"{wl.name}: non-finite values"
+        err = np.abs(got - exp)
+        tol = atol + rtol * np.abs(exp) + extra[act]
+        bad = np.argwhere(err > tol)
+        assert bad.size == 0, (f"{wl.name}: {len(bad)} values out of tolerance, first at "
+                               f"{tuple(bad[0])}, worst err/tol {float(np.max(err / tol)):.3g}")
+        n_checked += err.size
+    return n_checked

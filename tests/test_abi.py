@@ -235,3 +235,78 @@ def test_shrink_multi_slice_checks():
     st = sg.lib.sgmv_shrink_multi_slice(Matrix(FAKE, F16, 10, 64, 64), None, 1, FAKE, FAKE, FAKE,
                                         2, 6, 1.0, None)
     assert st == INVALID
+
+
+# --------------------------------------------------------------------------
+# Fused LoRA delta (shrink and expand in one call).
+# --------------------------------------------------------------------------
+
+def fslice(rank=16, hidden=64, n=64, off=0, num=2, dt=F16, bdt=None, a_ptr=FAKE, b_ptr=FAKE):
+    return sg.FusedSliceDesc(Stack(a_ptr, dt, num, rank, hidden),
+                             Stack(b_ptr, dt if bdt is None else bdt, num, n, rank), off)
+
+
+def fused(slices=None, x=None, out=None, meta=(FAKE, FAKE, FAKE), batches=2, max_len=6, n=None,
+          add=0):
+    slices = slices if slices is not None else [fslice()]
+    x = x or Matrix(FAKE, F16, 10, 64, 64)
+    out = out or Matrix(FAKE, F16, 10, 192, 192)
+    arr = (sg.FusedSliceDesc * max(len(slices), 1))(*slices)
+    st = sg.lib.sgmv_fused_shrink_expand(x, arr, len(slices) if n is None else n, out, *meta,
+                                         batches, max_len, 1.0, add, None)
+    return st, sg.lib.sgmv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(n=0), INVALID, "num_slices"),
+    (dict(slices=[fslice(off=64 * i) for i in range(4)]), INVALID, "num_slices"),
+    (dict(slices=[fslice(hidden=32)]), INVALID, "lora_a"),
+    (dict(slices=[sg.FusedSliceDesc(Stack(FAKE, F16, 2, 16, 64), Stack(FAKE, F16, 2, 64, 8), 0)]),
+     INVALID, "lora_b"),
+    (dict(slices=[sg.FusedSliceDesc(Stack(FAKE, F16, 2, 16, 64), Stack(FAKE, F16, 3, 64, 16), 0)]),
+     INVALID, "lora_b"),
+    (dict(slices=[fslice(off=129)]), INVALID, "window"),
+    (dict(slices=[fslice(off=-1)]), INVALID, "window"),
+    (dict(slices=[fslice(), fslice(off=32)]), INVALID, "overlap"),
+    (dict(slices=[fslice(), fslice(off=64, rank=8)]), INVALID, "match slice 0"),
+    (dict(slices=[fslice(), fslice(off=64, num=3)]), INVALID, "match slice 0"),
+    (dict(out=Matrix(FAKE, F16, 9, 192, 192)), INVALID, "rows"),
+    (dict(out=Matrix(FAKE, F16, 10, 192, 191)), INVALID, "row stride"),
+    (dict(x=Matrix(FAKE, F16, 10, 64, 63)), INVALID, "row stride"),
+    (dict(batches=-1), INVALID, "batches"),
+    (dict(max_len=-1), INVALID, "max_seq_len"),
+    (dict(batches=1 << 20), UNSUPPORTED, "batches"),
+    (dict(x=Matrix(FAKE, 7, 10, 64, 64)), INVALID, "dtype"),
+    (dict(slices=[fslice(dt=F32)]), UNSUPPORTED, "16-bit"),
+    (dict(slices=[fslice(bdt=BF16)]), UNSUPPORTED, "16-bit"),
+    (dict(x=Matrix(FAKE, BF16, 10, 64, 64)), UNSUPPORTED, "dtype or float32"),
+    (dict(meta=(FAKE, 0, FAKE)), INVALID, "metadata"),
+    (dict(x=Matrix(0, F16, 10, 64, 64)), INVALID, "null data"),
+    (dict(slices=[fslice(a_ptr=0)]), INVALID, "null data"),
+    # shapes the fused kernels do not take
+    (dict(slices=[fslice(rank=12)]), UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+    (dict(slices=[fslice(rank=136)]), UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+    (dict(slices=[fslice(rank=128), fslice(rank=128, off=64), fslice(rank=128, off=128)]),
+     UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+    (dict(slices=[fslice(n=60)]), UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+    (dict(slices=[fslice(off=4)]), UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+    (dict(slices=[fslice(hidden=60)], x=Matrix(FAKE, F16, 10, 60, 60)), UNSUPPORTED,
+     "run sgmv_shrink_multi_slice"),
+    (dict(x=Matrix(FAKE + 2, F16, 10, 64, 64)), UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+    (dict(slices=[fslice(b_ptr=FAKE + 8)]), UNSUPPORTED, "run sgmv_shrink_multi_slice"),
+])
+def test_fused_invalid_arguments_rejected_before_launch(kw, status, frag):
+    st, msg = fused(**kw)
+    assert st == status, msg
+    assert frag in msg
+
+
+def test_fused_no_op_calls():
+    assert fused(batches=0) == (OK, "")
+    assert fused(x=Matrix(FAKE, F16, 0, 64, 64), out=Matrix(FAKE, F16, 0, 192, 192)) == (OK, "")
+    assert fused(slices=[fslice(n=0)]) == (OK, "")
+    assert fused(meta=(0, 0, 0), batches=0) == (OK, "")
+    st = sg.lib.sgmv_fused_shrink_expand(Matrix(FAKE, F16, 10, 64, 64), None, 1,
+                                         Matrix(FAKE, F16, 10, 192, 192), FAKE, FAKE, FAKE, 2, 6,
+                                         1.0, 0, None)
+    assert st == INVALID
