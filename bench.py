@@ -50,7 +50,7 @@ def log(msg):
 SHARED_SOURCES = ("sgmv_common.h", "sgmv_launch.h", "sgmv_host.h", "sgmv_host.cpp",
                   "sgmv_limits.h")
 FAMILY_SOURCES = {
-    "expand": ("sgmv_api.cpp", "sgmv_device.h", "sgmv_fast_ks", "sgmv_generic.hip"),
+    "expand": ("sgmv_api.cpp", "sgmv_device.h", "sgmv_fast_ks", "sgmv_generic.hip", "sgmv_valu"),
     "shrink": ("sgmv_shrink",),
     "fused": ("sgmv_fused", "sgmv_shrink.h", "sgmv_shrink_launch.h", "sgmv_device.h"),
 }
@@ -273,19 +273,22 @@ def _stream_library():
     lib = ctypes.CDLL(path)
     lib.sgmv_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
-                                      ctypes.c_void_p]
+                                      ctypes.c_int, ctypes.c_void_p]
     lib.sgmv_stream_probe.restype = ctypes.c_int
     return lib
 
 
-def stream_ceilings(read_bytes, write_bytes, reps=20, grids=(1024, 2048, 4096, 8192)):
+def stream_ceilings(read_bytes, write_bytes, reps=20,
+                    shapes=((1024, 1), (2048, 1), (4096, 1), (8192, 1), (1024, 4), (2048, 4),
+                            (4096, 4))):
     """Streaming ceilings for a traffic of `read_bytes` read and
     `write_bytes` written per launch, from the hand-written probe kernel in
     libsgmv_stream.so (16-byte buffer accesses, non-temporal loads,
     non-temporal device-scope stores -- the SGMV kernels' forms): GB/s of
     the reads alone, of the writes alone, and of both in one launch with the
     reads spread evenly among the writes.  Each figure is the best over a
-    few grid sizes of `reps` back-to-back launches, each on the next of
+    few launch shapes (grid size, accesses in flight per thread) of `reps`
+    back-to-back launches, each on the next of
     enough buffer copies that no launch finds its data in the caches (1 GiB
     and more).  Context for the HBM roofline, not the metric."""
     import torch
@@ -304,10 +307,10 @@ def stream_ceilings(read_bytes, write_bytes, reps=20, grids=(1024, 2048, 4096, 8
         if rb + wb == 0:
             return None
         best = 0.0
-        for blocks in grids:
+        for blocks, unroll in shapes:
             def launch(i):
                 rc = lib.sgmv_stream_probe(src[i % sets].data_ptr(), rb, dst[i % sets].data_ptr(),
-                                           wb, sink.data_ptr(), blocks, stream.cuda_stream)
+                                           wb, sink.data_ptr(), blocks, unroll, stream.cuda_stream)
                 if rc != 0:
                     raise RuntimeError(f"stream probe failed with HIP error {rc}")
             for i in range(3):

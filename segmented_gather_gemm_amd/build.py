@@ -29,7 +29,7 @@ SOURCES = [os.path.join(CSRC, f) for f in
             "sgmv_shrink_generic.hip", "sgmv_shrink_k1.hip", "sgmv_shrink_k2.hip",
             "sgmv_shrink_k4.hip", "sgmv_shrink_k8.hip", "sgmv_shrink_k16.hip",
             "sgmv_fused_api.cpp", "sgmv_fused_k1.hip", "sgmv_fused_k2.hip", "sgmv_fused_k4.hip",
-            "sgmv_fused_k8.hip")]
+            "sgmv_fused_k8.hip", "sgmv_valu.hip")]
 
 STREAM_SOURCE = os.path.join(CSRC, "sgmv_stream.hip")
 STREAM_LIBRARY = os.path.join(HERE, "libsgmv_stream.so")

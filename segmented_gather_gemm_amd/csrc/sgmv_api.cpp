@@ -245,6 +245,10 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   p.gather = gather;
   const void* kernel =
       pick_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0, K, fast, gather);
+#ifdef SGMV_EXPAND_VALU
+  if (fast && !gather && K <= 32)
+    kernel = valu_kernel(s0.inputs.dtype, s0.lora_b.dtype, out.dtype, add_inputs != 0);
+#endif
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no kernel for this dtype combination");
 
   // segment table, or the gathered table

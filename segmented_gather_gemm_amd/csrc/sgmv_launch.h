@@ -97,5 +97,9 @@ const void* fast_kernel_ks2(int xd, int wd, int od, bool add, bool gather);
 const void* fast_kernel_ks4(int xd, int wd, int od, bool add, bool gather);
 const void* fast_kernel_ks8(int xd, int wd, int od, bool add, bool gather);
 const void* generic_kernel(int xd, int wd, int od, bool add);
+// Vector-ALU form for rank <= 32 (sgmv_valu.hip), same shape requirements as
+// the fast kernels, no gathered tiles; the host takes it only in builds with
+// SGMV_EXPAND_VALU defined (a measurement of the matrix-core choice).
+const void* valu_kernel(int xd, int wd, int od, bool add);
 
 }  // namespace sgmv
