@@ -10,7 +10,9 @@ steps, captured in one HIP graph and replayed once between HIP events on the
 launch stream right behind the W warm-up steps (themselves one graph,
 preceded by a cache-evicting fill), bracketed by device synchronisation, so
 the timed steps start on a busy GPU and the host's submission is not
-timed.  Each step uses the next of S identical buffer sets
+timed; this is done five times and the median replay is reported (a
+single replay of a short graph varies by up to ~15% on MI355X), every
+replay listed in the JSON line.  Each step uses the next of S identical buffer sets
 (inputs, weights, output), S >= 2 and S * footprint >= 1 GiB, so no step
 finds its data in the 256 MB Infinity Cache or the L2s.
 
@@ -69,6 +71,19 @@ def kernel_source_hash(family: str = "expand") -> str:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+MAX_ROTATED_SETS = 4096
+
+
+def rotated_sets(footprint):
+    """Buffer sets to rotate so that consecutive steps touch >= 1 GiB of
+    distinct memory (none finds its data in the 256 MB Infinity Cache or the
+    L2s): max(2, ceil(1 GiB / footprint)), at most MAX_ROTATED_SETS -- a
+    workload of a few kilobytes (the two-sequence worked example) stays
+    cache-resident whatever the rotation, and is measured as launch
+    latency."""
+    return min(MAX_ROTATED_SETS, max(2, math.ceil((1 << 30) / max(1, footprint))))
 
 
 def byte_model(wl):
@@ -189,12 +204,14 @@ class _Flush:
 
 def time_steps_graph(step, steps, warmup, repeats=5):
     """The `warmup` untimed steps and exactly `steps` timed steps as two HIP
-    graphs, captured and uploaded ahead; then, on the launch stream, a
-    cache-evicting fill, the warm-up graph, an event, the timed graph and an
-    event, so the timed steps follow real work (the GPU is neither idle nor
-    waiting for the host when they start).  Then `repeats` more rounds of
-    the same give a median.  Returns (ms per step of the first timed replay,
-    wall seconds of it, median ms per step over the repeats)."""
+    graphs, captured and uploaded ahead; then, `repeats` times, on the launch
+    stream: a cache-evicting fill, the warm-up graph, an event, the timed
+    graph and an event -- so each timed replay follows real work (the GPU is
+    neither idle nor waiting for the host when it starts) and covers exactly
+    `steps` steps.  A single replay of a short graph (20 steps, ~2 ms) varies
+    by up to ~15% from one replay to the next on MI355X (clock and power
+    state), so the result is the median replay.  Returns (median ms per step,
+    wall seconds of the first replay, [ms per step of every replay])."""
     import statistics
     import torch
     torch.cuda.synchronize()
@@ -229,10 +246,9 @@ def time_steps_graph(step, steps, warmup, repeats=5):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps, time.perf_counter() - w0
 
-    ms, wall = one()
-    rep = [one()[0] for _ in range(repeats)]
+    runs = [one() for _ in range(max(1, repeats))]
     del flush
-    return ms, wall, statistics.median(rep)
+    return statistics.median(r[0] for r in runs), runs[0][1], [r[0] for r in runs]
 
 
 def time_single_launches(step, reps=50, flush_bytes=1 << 30):
@@ -534,13 +550,13 @@ def run_shrink(args):
     log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
     ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
     log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
-    ms_median = None
+    replays = None
     if args.eager:
         ms, wall, mode = ms_eager, wall_eager, "eager"
     else:
         log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
-        ms, wall, ms_median = time_steps_graph(step, args.steps, args.warmup)
-        mode = "hip-graph replay"
+        ms, wall, replays = time_steps_graph(step, args.steps, args.warmup)
+        mode = "hip-graph replay (median of 5 timed replays of the K steps)"
     log("bench: single launches after a cache flush")
     ms_single = time_single_launches(step)
     sec = ms * 1e-3
@@ -596,7 +612,7 @@ def run_shrink(args):
             "call": (f"{len(wl.lora_a)} x sgmv_shrink" if split else
                      "sgmv_shrink_multi_slice"),
             "launch": mode,
-            "batch_median_us_per_step": None if ms_median is None else round(ms_median * 1e3, 3),
+            "timed_replays_us_per_step": None if replays is None else [round(r * 1e3, 3) for r in replays],
             "eager_us_per_step": round(ms_eager * 1e3, 3),
             "single_launch_after_flush_us": round(ms_single * 1e3, 3),
         },
@@ -748,7 +764,7 @@ def run_fused(args):
     model_bytes, read_bytes, t_act, distinct = fused_byte_model(wl)
     fp = (wl.x.nbytes + sum(a.nbytes for a in wl.lora_a) + sum(b.nbytes for b in wl.lora_b) +
           wl.out0.nbytes)
-    nsets = max(2, math.ceil((1 << 30) / fp))
+    nsets = rotated_sets(fp)
     log(f"bench: {len(wl.lora_a)} slice(s), T={wl.T} (active {t_act}), hidden {wl.H} -> rank "
         f"{wl.K} -> {[b.shape[1] for b in wl.lora_b]}, {distinct} distinct adapters, "
         f"{model_bytes / 1e6:.2f} MB per call, {nsets} rotated buffer sets of {fp / 1e6:.1f} MB")
@@ -761,13 +777,13 @@ def run_fused(args):
     log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
     ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
     log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
-    ms_median = None
+    replays = None
     if args.eager:
         ms, wall, mode = ms_eager, wall_eager, "eager"
     else:
         log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
-        ms, wall, ms_median = time_steps_graph(step, args.steps, args.warmup)
-        mode = "hip-graph replay"
+        ms, wall, replays = time_steps_graph(step, args.steps, args.warmup)
+        mode = "hip-graph replay (median of 5 timed replays of the K steps)"
     log("bench: single launches after a cache flush")
     ms_single = time_single_launches(step)
     sec = ms * 1e-3
@@ -823,7 +839,7 @@ def run_fused(args):
             "call": ("sgmv_shrink_multi_slice + sgmv_expand_multi_slice" if args.unfused else
                      "sgmv_fused_shrink_expand"),
             "launch": mode,
-            "batch_median_us_per_step": None if ms_median is None else round(ms_median * 1e3, 3),
+            "timed_replays_us_per_step": None if replays is None else [round(r * 1e3, 3) for r in replays],
             "eager_us_per_step": round(ms_eager * 1e3, 3),
             "single_launch_after_flush_us": round(ms_single * 1e3, 3),
         },
@@ -888,7 +904,7 @@ def main():
     wl = W.WORKLOADS[args.workload](args.seed)
     model_bytes, t_act, distinct = byte_model(wl)
     fp = footprint_bytes(wl)
-    nsets = max(2, math.ceil((1 << 30) / fp))
+    nsets = rotated_sets(fp)
     log(f"bench: {len(wl.slices)} slice(s), T={wl.T} (active {t_act}), rank {wl.K}, "
         f"{distinct} distinct adapters, {model_bytes / 1e6:.2f} MB per call, "
         f"{nsets} rotated buffer sets of {fp / 1e6:.1f} MB")
@@ -902,13 +918,13 @@ def main():
     log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (eager launches)")
     ms_eager, wall_eager = time_steps(step, args.steps, args.warmup)
     log(f"bench: eager {ms_eager * 1e3:.2f} us per step")
-    ms_median = None
+    replays = None
     if args.eager:
         ms, wall, mode = ms_eager, wall_eager, "eager"
     else:
         log(f"bench: {args.warmup} warm-up + {args.steps} timed steps (HIP-graph replay)")
-        ms, wall, ms_median = time_steps_graph(step, args.steps, args.warmup)
-        mode = "hip-graph replay"
+        ms, wall, replays = time_steps_graph(step, args.steps, args.warmup)
+        mode = "hip-graph replay (median of 5 timed replays of the K steps)"
     log("bench: single launches after a cache flush")
     ms_single = time_single_launches(step)
     sec = ms * 1e-3
@@ -968,7 +984,7 @@ def main():
                      "sgmv_expand_slice" if len(wl.slices) == 1 else
                      f"{len(wl.slices)} x sgmv_expand_slice" if split else "sgmv_expand_multi_slice"),
             "launch": mode,
-            "batch_median_us_per_step": None if ms_median is None else round(ms_median * 1e3, 3),
+            "timed_replays_us_per_step": None if replays is None else [round(r * 1e3, 3) for r in replays],
             "eager_us_per_step": round(ms_eager * 1e3, 3),
             "single_launch_after_flush_us": round(ms_single * 1e3, 3),
         },
