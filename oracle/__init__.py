@@ -39,7 +39,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsgmv_oracle.so")
+# ORACLE_LIBRARY names another build of sgmv_oracle.c (the mutation test
+# loads deliberately broken copies to show that the pins catch them).
+_LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "libsgmv_oracle.so")
 
 DTYPE_CODES = {"f16": 0, "bf16": 1, "f32": 2}
 _STORAGE = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32}
