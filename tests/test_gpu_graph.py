@@ -1,5 +1,6 @@
 """HIP-graph capture of the C-ABI calls: a captured sgmv_expand_slice /
-sgmv_expand_multi_slice replayed several times, with eager work and
+sgmv_expand_multi_slice, sgmv_shrink / sgmv_shrink_multi_slice or
+sgmv_fused_shrink_expand replayed several times, with eager work and
 synchronisation between replays, gives the eager result on every replay
 (the library records no memset or allocation, only kernel launches)."""
 import numpy as np
@@ -66,3 +67,28 @@ def test_shrink_graph_replays_match_eager(multi, T):
         torch.cuda.synchronize()
         for a, b in zip(other, eager):
             assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("add", [False, True])
+def test_fused_graph_replays_match_eager(add):
+    """sgmv_fused_shrink_expand captured once and replayed."""
+    import torch
+    from gpu_util import DeviceFused, assert_fused_parity
+    wl = W.fused_custom([90, 3, 0, 150, 64, 1], [1, 0, 1, -1, 2, 0], H=512, K=32, L=3,
+                        slices=[(0, 256), (256, 128), (384, 128)], H_out=520, add=add, seed=33)
+    df = DeviceFused(wl)
+    eager = to_host_bits(df.run())
+    assert assert_fused_parity(wl, eager) > 0
+    out = df.fresh_out()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        df.run(out)
+    for replay in range(4):
+        out.copy_(df.out0)                       # eager reset between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), eager), f"replay {replay}"
+        other = to_host_bits(df.run())           # eager work in between
+        torch.cuda.synchronize()
+        assert np.array_equal(other, eager)
