@@ -254,8 +254,8 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   // segment table, or the gathered table
   const size_t lds =
       (size_t)(gather ? batches + 2 * L + 1 : 4 * batches + 1) * sizeof(int32_t);
-  int capacity = 0;
-  hipError_t e = device_capacity(kernel, lds, &capacity);
+  int capacity = 0, cus = 0;
+  hipError_t e = device_capacity(kernel, lds, &capacity, &cus);
   if (e != hipSuccess)
     return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
   // About kUnitsPerWorkgroup units per workgroup at least: a workgroup that
@@ -266,6 +266,7 @@ sgmv_status check_and_launch(const sgmv_slice* slices, int num_slices, sgmv_matr
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
+  p.cus = cus;
 
   void* args[] = {&p};
   e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "sgmv_launch.h"
+#include "sgmv_limits.h"
 
 namespace sgmv {
 namespace dev {
@@ -429,18 +430,15 @@ __device__ __forceinline__ int32_t build_tile_table(const P& p, const SegTable& 
 // 64-bit division is a long scalar sequence that every wave of a compute
 // unit would queue for on the shared scalar ALU.
 
-// This workgroup's contiguous range [begin, end) of the U units (sizes differ
-// by at most one); workgroup ids are remapped so each XCD gets one contiguous
-// eighth of the range.
+// This workgroup's contiguous range [begin, end) of the U units
+// (limits::unit_span: balanced shares per XCD while every unit can have a
+// compute unit of its own, XCD-major contiguous ranges otherwise).
 template <typename P>
 __device__ __forceinline__ void unit_range(const P& p, uint32_t U, uint32_t* begin,
                                            uint32_t* end) {
-  const uint32_t bid = blockIdx.x;
-  const uint32_t G = (uint32_t)p.grid;
-  const uint32_t lw = (G >= 16 && (G & 7) == 0) ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-  const uint32_t q = U / G, r = U - q * G;
-  *begin = lw * q + (lw < r ? lw : r);
-  *end = *begin + q + (lw < r ? 1 : 0);
+  const limits::UnitSpan s = limits::unit_span(U, (uint32_t)p.grid, (uint32_t)p.cus, blockIdx.x);
+  *begin = s.begin;
+  *end = s.end;
 }
 
 // Largest b in [0, n) with table[b] <= key (table non-decreasing, table[0] =

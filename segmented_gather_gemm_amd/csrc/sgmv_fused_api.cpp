@@ -185,8 +185,8 @@ sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice*
   p.steps = (int32_t)((steps + turn - 1) / turn * turn);
 
   const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);
-  int capacity = 0;
-  hipError_t e = device_capacity(kernel, lds, &capacity);
+  int capacity = 0, cus = 0;
+  hipError_t e = device_capacity(kernel, lds, &capacity, &cus);
   if (e != hipSuccess)
     return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
   if (capacity < 1)
@@ -202,6 +202,7 @@ sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice*
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
+  p.cus = cus;
   void* args[] = {&p};
   e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
   if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

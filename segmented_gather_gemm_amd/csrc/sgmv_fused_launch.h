@@ -42,6 +42,7 @@ struct FusedParams {
   int32_t K;              // rank, the same for every slice
   int32_t num_slices;
   int32_t grid;
+  int32_t cus;            // compute units of the device
   int32_t steps;          // 32-wide hidden steps per unit, whole turns of the ring
   int32_t sort_slots;
   int32_t per_token;      // always 0

@@ -32,7 +32,8 @@ std::mutex g_mu;
 std::map<int, int> g_cus;
 std::map<std::tuple<int, const void*, size_t>, int> g_occupancy;
 
-hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups) {
+hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups,
+                           int* compute_units) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -54,6 +55,7 @@ hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups
     occ = g_occupancy.emplace(key, blocks > 0 ? blocks : 0).first;
   }
   *workgroups = cu->second * occ->second;
+  if (compute_units) *compute_units = cu->second;
   return hipSuccess;
 }
 

@@ -25,8 +25,10 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Workgroups of `kernel` (block of sgmv::kThreads threads, `lds_bytes` of
 // dynamic LDS) that fit the current device at once: compute units times
 // resident blocks per unit, queried once per (device, kernel, LDS bucket);
-// 0 when one workgroup does not fit a compute unit.
-hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups);
+// 0 when one workgroup does not fit a compute unit.  The device's compute
+// unit count goes to *compute_units when that is not null.
+hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups,
+                           int* compute_units = nullptr);
 
 }  // namespace host
 }  // namespace sgmv

@@ -74,6 +74,7 @@ struct Params {
   int32_t num_slices;
   int32_t total_tiles;  // column tiles over all slices
   int32_t grid;         // workgroups launched
+  int32_t cus;          // compute units of the device
   int32_t band_tiles;   // row tiles per band of the fast kernels' walk
   int32_t chunk_units;  // fast kernels: units per chunk of the strided assignment
   int32_t sort_slots;   // order the segment table by adapter (batches <= kSortMaxBatches)

@@ -95,8 +95,8 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
     p.steps = (int32_t)((per_wave + turn - 1) / turn * turn);
   }
   const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);
-  int capacity = 0;
-  hipError_t e = device_capacity(kernel, lds, &capacity);
+  int capacity = 0, cus = 0;
+  hipError_t e = device_capacity(kernel, lds, &capacity, &cus);
   if (e != hipSuccess)
     return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
   // Units are tiles of active segments: at most ceil(T / rows) + min(batches,
@@ -108,6 +108,7 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
+  p.cus = cus;
   void* args[] = {&p};
   e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
   if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

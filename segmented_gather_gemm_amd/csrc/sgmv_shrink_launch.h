@@ -34,6 +34,7 @@ struct ShrinkParams {
   int32_t K;              // rank, the same for every slice
   int32_t num_slices;
   int32_t grid;
+  int32_t cus;            // compute units of the device
   int32_t steps;          // fast kernels: 32-wide hidden steps per wave (split-H) or per unit (split-T)
   int32_t sort_slots;
   int32_t per_token;

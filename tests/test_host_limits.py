@@ -1,5 +1,6 @@
-"""Host-side size predicates of the library's kernel choices, compiled with
-the host compiler and checked at their boundaries (no GPU needed)."""
+"""Host-side size predicates of the library's kernel choices and the kernels'
+unit assignment (sgmv_limits.h), compiled with the host compiler and checked
+at their boundaries (no GPU needed)."""
 import os
 import subprocess
 
@@ -63,3 +64,80 @@ def test_shrink_lora_a_offset_bound_named_shapes(probe):
     cases = [(256, 8 << 20), (128, 8 << 20), (256, (1 << 22) - 1), (256, 1 << 22),
              (16, 4096), (32, 4096), (64, 4096), (128, 8192)]
     assert probe(cases) == [False, False, True, False, True, True, True, True]
+
+
+SPAN_PROBE = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "sgmv_limits.h"
+// argv: U G cus -> one line "begin end" per workgroup
+int main(int argc, char** argv) {
+  const unsigned U = atoi(argv[1]), G = atoi(argv[2]), cus = atoi(argv[3]);
+  for (unsigned bid = 0; bid < G; ++bid) {
+    const sgmv::limits::UnitSpan s = sgmv::limits::unit_span(U, G, cus, bid);
+    printf("%u %u\n", s.begin, s.end);
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def spans(tmp_path_factory):
+    d = tmp_path_factory.mktemp("spans")
+    src = d / "span.cpp"
+    src.write_text(SPAN_PROBE)
+    exe = d / "span"
+    subprocess.run(["g++", "-std=c++17", "-O1", f"-I{CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+
+    def run(U, G, cus):
+        out = subprocess.run([str(exe), str(U), str(G), str(cus)], check=True,
+                             capture_output=True, text=True).stdout.split()
+        v = [int(t) for t in out]
+        return list(zip(v[0::2], v[1::2]))
+    return run
+
+
+# (units, grid, compute units): the named shrink and fused launches (e.g. 298
+# units of 64 rows in a grid of 320 or 256), grids above and below the unit
+# count, grids that are not multiples of 8, empty launches
+SPAN_CASES = [(U, G, 256) for U in (0, 1, 7, 8, 9, 84, 182, 192, 255, 256, 257, 298, 319, 512,
+                                   1000, 12345)
+              for G in (1, 3, 8, 16, 24, 112, 192, 256, 320, 416, 768)] + \
+             [(100, 128, 64), (64, 128, 64), (65, 128, 64), (300, 304, 304)]
+
+
+@pytest.mark.parametrize("U,G,cus", SPAN_CASES)
+def test_unit_spans_partition_and_balance(spans, U, G, cus):
+    sp = spans(U, G, cus)
+    assert len(sp) == G
+    # every unit exactly once, each workgroup a contiguous range
+    covered = sorted(u for b, e in sp for u in range(b, e))
+    assert covered == list(range(U))
+    sizes = [e - b for b, e in sp]
+    xcd_grid = G >= 16 and G % 8 == 0
+    if xcd_grid and U <= G and U <= cus:
+        # one unit per workgroup at most, equal shares per XCD (workgroup i on
+        # XCD i % 8), and only workgroups of the first wave (i < cus) busy
+        assert max(sizes, default=0) <= 1
+        per_xcd = [sum(sizes[x::8]) for x in range(8)]
+        assert max(per_xcd) - min(per_xcd) <= 1
+        assert all(s == 0 for s in sizes[cus:])
+        # each XCD's units are one contiguous run, XCD x before XCD x + 1
+        for x in range(8):
+            own = sorted(u for b, e in sp[x::8] for u in range(b, e))
+            assert own == list(range(own[0], own[0] + len(own))) if own else True
+    else:
+        # contiguous ranges in XCD-major order (plain order for other grids),
+        # sizes q or q + 1 with the larger ones first
+        order = sorted(range(G), key=lambda i: ((i % 8) * (G // 8) + i // 8) if xcd_grid else i)
+        pos = 0
+        for i in order:
+            b, e = sp[i]
+            assert b == pos
+            pos = e
+        q = U // G
+        ordered = [sizes[i] for i in order]
+        assert all(s in (q, q + 1) for s in ordered)
+        assert ordered == sorted(ordered, reverse=True)
