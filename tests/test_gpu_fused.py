@@ -136,3 +136,16 @@ def test_fused_named_workloads(name):
     rep = assert_parity(ew, fused)
     t_act = int(wl.lens[wl.active_mask()].sum())
     assert rep.checked_values == t_act * sum(b.shape[1] for b in wl.lora_b)
+
+
+@pytest.mark.parametrize("units", [255, 256, 257])
+def test_fused_unit_assignment_around_the_compute_unit_count(units):
+    """`units` segments of 64 tokens, one fused unit each, in a grid sized from
+    ceil(T / 64) + segments: both branches of the unit assignment (even
+    shares per XCD while every unit has a compute unit; XCD after XCD
+    beyond)."""
+    lens = [64] * units
+    idx = [i % 5 for i in range(units)]
+    wl = W.fused_custom(lens, idx, H=128, K=32, L=5, slices=[(0, 256), (256, 128)], H_out=400,
+                        add=units % 2 == 1, seed=units)
+    assert assert_fused_parity(wl, to_host_bits(DeviceFused(wl).run())) > 0

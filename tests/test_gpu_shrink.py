@@ -239,3 +239,17 @@ def test_shrink_multi_slice_with_a_misaligned_output_equals_single_calls():
                        wl.max_seq_len, wl.scale)
         assert np.array_equal(to_host_bits(outs[i]), to_host_bits(alone)), i
     assert assert_shrink_parity(wl, [to_host_bits(o) for o in outs]) > 0
+
+
+@pytest.mark.parametrize("units", [255, 256, 257])
+def test_shrink_unit_assignment_around_the_compute_unit_count(units):
+    """`units` segments of 64 tokens, each one split-T unit, in a grid of about
+    twice as many workgroups (the host sizes it from ceil(T / 64) + segments):
+    up to the compute unit count the units are spread evenly over the XCDs,
+    beyond it they fill XCD after XCD (unit_span in sgmv_limits.h).  Every
+    row of every unit is compared with the oracle."""
+    lens = [64] * units
+    idx = [i % 7 for i in range(units)]  # every segment active: exactly `units` units
+    wl = W.shrink_custom(lens, idx, H=256, K=64, L=7, slices=2, x_dtype="bf16", a_dtype="bf16",
+                         out_dtype="f32", seed=units)
+    assert run_and_check(wl) > 0
