@@ -11,7 +11,9 @@ compiled at run time.  Packed-fp32 VALU instructions are disabled for every
 HIP translation unit.
 
 It also builds libsgmv_stream.so (csrc/sgmv_stream.hip), the benchmark's
-streaming-bandwidth probe, which is not part of the operation.
+streaming-bandwidth probe, which is not part of the operation, and
+examples/sgmv_c_client, a plain C-ABI client of libsgmv (HIP runtime and
+include/sgmv.h only) that the GPU tests run.
 """
 import os
 import subprocess
@@ -33,6 +35,8 @@ SOURCES = [os.path.join(CSRC, f) for f in
 
 STREAM_SOURCE = os.path.join(CSRC, "sgmv_stream.hip")
 STREAM_LIBRARY = os.path.join(HERE, "libsgmv_stream.so")
+CLIENT_SOURCE = os.path.join(HERE, "examples", "sgmv_c_client.cpp")
+CLIENT = os.path.join(HERE, "examples", "sgmv_c_client")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -90,6 +94,17 @@ def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY) -> str:
         if stream_proc.returncode != 0:
             raise RuntimeError(f"hipcc failed on {STREAM_SOURCE}:\n{_diagnostics(out)}")
         os.replace(stream_tmp, STREAM_LIBRARY)
+        if output == LIBRARY:
+            # the C client links the in-tree library (found next to it at run time)
+            client_tmp = CLIENT + ".tmp%d" % os.getpid()
+            cmd = [HIPCC, "-O2", "-std=c++17", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
+                   CLIENT_SOURCE, "-o", client_tmp, f"-L{HERE}", "-lsgmv",
+                   "-Wl,-rpath,$ORIGIN/.."]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {CLIENT_SOURCE}:\n"
+                                   f"{_diagnostics(res.stdout + res.stderr)}")
+            os.replace(client_tmp, CLIENT)
     finally:
         if stream_proc.poll() is None:
             stream_proc.wait()
