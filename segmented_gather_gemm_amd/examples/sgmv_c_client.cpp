@@ -5,19 +5,23 @@
 // own: the GPU tests prepare the files from a seeded workload and check the
 // result with the oracle.
 //
-// usage: sgmv_c_client expand <dir>
-//   <dir>/problem.txt  "T K N H L offset x_dtype w_dtype out_dtype add batches"
-//   <dir>/x.bin (T x K, x_dtype), w.bin (L x N x K, w_dtype), out0.bin (T x H,
-//   out_dtype), start.bin, lens.bin, idx.bin (int64[batches])
-//   -> <dir>/out.bin (T x H, out_dtype), from sgmv_expand_slice
-// usage: sgmv_c_client shrink <dir>
-//   <dir>/problem.txt  "T H K L x_dtype a_dtype out_dtype scale batches"
-//   <dir>/x.bin (T x H), a.bin (L x K x H), out0.bin (T x K), start.bin,
-//   lens.bin, idx.bin
-//   -> <dir>/out.bin (T x K), from sgmv_shrink
-// Dtype codes are sgmv_dtype's (0 f16, 1 bf16, 2 f32).  Exit status 0 on
-// success; 1 with a message on stderr for any failure (bad arguments or
-// files, a HIP error, a library status other than SGMV_OK).
+// usage: sgmv_c_client <mode> <dir>, mode one of
+//   expand  sgmv_expand_slice.  problem.txt: "T K N H L offset xd wd od add
+//           batches"; x.bin (T x K, xd), w.bin (L x N x K, wd)
+//   multi   sgmv_expand_multi_slice.  problem.txt: "T K H L S xd wd od add
+//           batches", then S lines "N offset"; x<i>.bin (T x K, xd) and
+//           w<i>.bin (L x N_i x K, wd) per slice i
+//   shrink  sgmv_shrink.  problem.txt: "T H K L xd wd od scale batches";
+//           x.bin (T x H, xd), a.bin (L x K x H, wd)
+//   fused   sgmv_fused_shrink_expand.  problem.txt: "T H K L S xd wd od add
+//           batches scale H_out", then S lines "N offset"; x.bin (T x H,
+//           xd), a<i>.bin (L x K x H, wd), b<i>.bin (L x N_i x K, wd)
+// and, for every mode, out0.bin (the prior output: T x H for expand and
+// multi, T x K for shrink, T x H_out for fused, od) and start.bin,
+// lens.bin, idx.bin (int64[batches]); the result goes to out.bin in
+// out0.bin's layout.  Dtype codes are sgmv_dtype's (0 f16, 1 bf16, 2 f32).
+// Exit status 0 on success; 1 with a message on stderr for any failure (bad
+// arguments or files, a HIP error, a library status other than SGMV_OK).
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -70,16 +74,23 @@ bool hip_ok(hipError_t e, const char* what) {
   return false;
 }
 
-// Device copies of host buffers, freed on destruction.
-struct DeviceBuffers {
+bool library_ok(sgmv_status st, const char* call) {
+  if (st == SGMV_OK) return true;
+  fprintf(stderr, "sgmv_c_client: %s returned %d: %s\n", call, (int)st, sgmv_last_error());
+  return false;
+}
+
+// Device copies of host buffers and a stream, released on destruction.
+struct Device {
   std::vector<void*> ptrs;
-  ~DeviceBuffers() {
+  hipStream_t stream = nullptr;
+  ~Device() {
+    if (stream) (void)hipStreamDestroy(stream);
     for (void* p : ptrs) (void)hipFree(p);
   }
   void* upload(const std::vector<char>& host) {
     void* p = nullptr;
-    const size_t n = host.size() ? host.size() : 1;
-    if (!hip_ok(hipMalloc(&p, n), "hipMalloc")) return nullptr;
+    if (!hip_ok(hipMalloc(&p, host.size() ? host.size() : 1), "hipMalloc")) return nullptr;
     ptrs.push_back(p);
     if (!host.empty() && !hip_ok(hipMemcpy(p, host.data(), host.size(), hipMemcpyHostToDevice),
                                  "hipMemcpy to device"))
@@ -88,127 +99,228 @@ struct DeviceBuffers {
   }
 };
 
-bool library_ok(sgmv_status st, const char* call) {
-  if (st == SGMV_OK) return true;
-  fprintf(stderr, "sgmv_c_client: %s returned %d: %s\n", call, (int)st, sgmv_last_error());
+// The segment metadata of a problem, on the host and the device.
+struct Segments {
+  std::vector<char> start, lens, idx;
+  const int64_t *d_start = nullptr, *d_lens = nullptr, *d_idx = nullptr;
+  int64_t max_len = 0;
+  bool load(const std::string& dir, int64_t batches, Device* dev) {
+    if (!read_file(dir + "/start.bin", &start, batches * 8) ||
+        !read_file(dir + "/lens.bin", &lens, batches * 8) ||
+        !read_file(dir + "/idx.bin", &idx, batches * 8))
+      return false;
+    for (int64_t b = 0; b < batches; ++b) {
+      int64_t v;
+      memcpy(&v, lens.data() + 8 * b, 8);
+      if (v > max_len) max_len = v;
+    }
+    d_start = static_cast<const int64_t*>(dev->upload(start));
+    d_lens = static_cast<const int64_t*>(dev->upload(lens));
+    d_idx = static_cast<const int64_t*>(dev->upload(idx));
+    return d_start && d_lens && d_idx;
+  }
+};
+
+FILE* open_problem(const std::string& dir) {
+  FILE* f = fopen((dir + "/problem.txt").c_str(), "r");
+  if (!f) fprintf(stderr, "sgmv_c_client: cannot open %s/problem.txt\n", dir.c_str());
+  return f;
+}
+
+bool bad_problem(const char* mode) {
+  fprintf(stderr, "sgmv_c_client: bad %s problem.txt\n", mode);
   return false;
 }
 
-int run_expand(const std::string& dir) {
+// Reads `count` "N offset" lines into widths / offsets.
+bool read_windows(FILE* f, int count, std::vector<int64_t>* widths,
+                  std::vector<int64_t>* offsets) {
+  for (int i = 0; i < count; ++i) {
+    long long n, off;
+    if (fscanf(f, "%lld %lld", &n, &off) != 2 || n < 0 || off < 0) return false;
+    widths->push_back(n);
+    offsets->push_back(off);
+  }
+  return true;
+}
+
+// Waits for the stream, copies the output back and writes out.bin.
+bool finish(Device* dev, void* d_out, std::vector<char>* out, const std::string& dir) {
+  return hip_ok(hipStreamSynchronize(dev->stream), "hipStreamSynchronize") &&
+         hip_ok(hipMemcpy(out->data(), d_out, out->size(), hipMemcpyDeviceToHost),
+                "hipMemcpy to host") &&
+         write_file(dir + "/out.bin", *out);
+}
+
+bool run_expand(const std::string& dir) {
   long long T, K, N, H, L, off, add, batches;
   int xd, wd, od;
-  FILE* f = fopen((dir + "/problem.txt").c_str(), "r");
-  if (!f) {
-    fprintf(stderr, "sgmv_c_client: cannot open %s/problem.txt\n", dir.c_str());
-    return 1;
-  }
+  FILE* f = open_problem(dir);
+  if (!f) return false;
   const int n = fscanf(f, "%lld %lld %lld %lld %lld %lld %d %d %d %lld %lld", &T, &K, &N, &H, &L,
                        &off, &xd, &wd, &od, &add, &batches);
   fclose(f);
   if (n != 11 || T < 0 || K < 1 || N < 0 || H < 1 || L < 1 || off < 0 || batches < 0 ||
-      !known(xd) || !known(wd) || !known(od)) {
-    fprintf(stderr, "sgmv_c_client: bad expand problem.txt\n");
-    return 1;
-  }
-  std::vector<char> x, w, out, start, lens, idx;
+      !known(xd) || !known(wd) || !known(od))
+    return bad_problem("expand");
+  std::vector<char> x, w, out;
   if (!read_file(dir + "/x.bin", &x, T * K * elem_size(xd)) ||
       !read_file(dir + "/w.bin", &w, L * N * K * elem_size(wd)) ||
-      !read_file(dir + "/out0.bin", &out, T * H * elem_size(od)) ||
-      !read_file(dir + "/start.bin", &start, batches * 8) ||
-      !read_file(dir + "/lens.bin", &lens, batches * 8) ||
-      !read_file(dir + "/idx.bin", &idx, batches * 8))
-    return 1;
-  DeviceBuffers dev;
+      !read_file(dir + "/out0.bin", &out, T * H * elem_size(od)))
+    return false;
+  Device dev;
+  Segments seg;
+  if (!seg.load(dir, batches, &dev)) return false;
   void* dx = dev.upload(x);
   void* dw = dev.upload(w);
   void* dout = dev.upload(out);
-  void* dstart = dev.upload(start);
-  void* dlens = dev.upload(lens);
-  void* didx = dev.upload(idx);
-  if (!dx || !dw || !dout || !dstart || !dlens || !didx) return 1;
-  hipStream_t stream;
-  if (!hip_ok(hipStreamCreate(&stream), "hipStreamCreate")) return 1;
+  if (!dx || !dw || !dout || !hip_ok(hipStreamCreate(&dev.stream), "hipStreamCreate"))
+    return false;
   const sgmv_matrix mx = {dx, xd, T, K, K};
   const sgmv_stack mw = {dw, wd, L, N, K};
   const sgmv_matrix mo = {dout, od, T, H, H};
-  int64_t max_len = 0;
-  for (long long b = 0; b < batches; ++b) {
-    int64_t v;
-    memcpy(&v, lens.data() + 8 * b, 8);
-    if (v > max_len) max_len = v;
-  }
-  const sgmv_status st = sgmv_expand_slice(
-      mx, mw, mo, static_cast<const int64_t*>(dstart), static_cast<const int64_t*>(dlens),
-      static_cast<const int64_t*>(didx), batches, max_len, off, N, (int)add, stream);
-  bool ok = library_ok(st, "sgmv_expand_slice") &&
-            hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize") &&
-            hip_ok(hipMemcpy(out.data(), dout, out.size(), hipMemcpyDeviceToHost),
-                   "hipMemcpy to host");
-  (void)hipStreamDestroy(stream);
-  return ok && write_file(dir + "/out.bin", out) ? 0 : 1;
+  return library_ok(sgmv_expand_slice(mx, mw, mo, seg.d_start, seg.d_lens, seg.d_idx, batches,
+                                      seg.max_len, off, N, (int)add, dev.stream),
+                    "sgmv_expand_slice") &&
+         finish(&dev, dout, &out, dir);
 }
 
-int run_shrink(const std::string& dir) {
-  long long T, H, K, L, batches;
-  int xd, ad, od;
-  float scale;
-  FILE* f = fopen((dir + "/problem.txt").c_str(), "r");
-  if (!f) {
-    fprintf(stderr, "sgmv_c_client: cannot open %s/problem.txt\n", dir.c_str());
-    return 1;
+bool run_multi(const std::string& dir) {
+  long long T, K, H, L, add, batches;
+  int S, xd, wd, od;
+  FILE* f = open_problem(dir);
+  if (!f) return false;
+  std::vector<int64_t> widths, offsets;
+  const int n = fscanf(f, "%lld %lld %lld %lld %d %d %d %d %lld %lld", &T, &K, &H, &L, &S, &xd,
+                       &wd, &od, &add, &batches);
+  const bool windows = n == 10 && S >= 1 && S <= SGMV_MAX_SLICES &&
+                       read_windows(f, S, &widths, &offsets);
+  fclose(f);
+  if (!windows || T < 0 || K < 1 || H < 1 || L < 1 || batches < 0 || !known(xd) ||
+      !known(wd) || !known(od))
+    return bad_problem("multi");
+  Device dev;
+  Segments seg;
+  if (!seg.load(dir, batches, &dev)) return false;
+  std::vector<sgmv_slice> slices(S);
+  for (int i = 0; i < S; ++i) {
+    std::vector<char> x, w;
+    if (!read_file(dir + "/x" + std::to_string(i) + ".bin", &x, T * K * elem_size(xd)) ||
+        !read_file(dir + "/w" + std::to_string(i) + ".bin", &w,
+                   L * widths[i] * K * elem_size(wd)))
+      return false;
+    void* dx = dev.upload(x);
+    void* dw = dev.upload(w);
+    if (!dx || !dw) return false;
+    slices[i].inputs = {dx, xd, T, K, K};
+    slices[i].lora_b = {dw, wd, L, widths[i], K};
+    slices[i].slice_offset = offsets[i];
+    slices[i].slice_size = widths[i];
   }
-  const int n = fscanf(f, "%lld %lld %lld %lld %d %d %d %f %lld", &T, &H, &K, &L, &xd, &ad, &od,
+  std::vector<char> out;
+  if (!read_file(dir + "/out0.bin", &out, T * H * elem_size(od))) return false;
+  void* dout = dev.upload(out);
+  if (!dout || !hip_ok(hipStreamCreate(&dev.stream), "hipStreamCreate")) return false;
+  const sgmv_matrix mo = {dout, od, T, H, H};
+  return library_ok(sgmv_expand_multi_slice(slices.data(), S, mo, seg.d_start, seg.d_lens,
+                                            seg.d_idx, batches, seg.max_len, (int)add,
+                                            dev.stream),
+                    "sgmv_expand_multi_slice") &&
+         finish(&dev, dout, &out, dir);
+}
+
+bool run_shrink(const std::string& dir) {
+  long long T, H, K, L, batches;
+  int xd, wd, od;
+  float scale;
+  FILE* f = open_problem(dir);
+  if (!f) return false;
+  const int n = fscanf(f, "%lld %lld %lld %lld %d %d %d %f %lld", &T, &H, &K, &L, &xd, &wd, &od,
                        &scale, &batches);
   fclose(f);
-  if (n != 9 || T < 0 || H < 1 || K < 1 || L < 1 || batches < 0 || !known(xd) || !known(ad) ||
-      !known(od)) {
-    fprintf(stderr, "sgmv_c_client: bad shrink problem.txt\n");
-    return 1;
-  }
-  std::vector<char> x, a, out, start, lens, idx;
+  if (n != 9 || T < 0 || H < 1 || K < 1 || L < 1 || batches < 0 || !known(xd) || !known(wd) ||
+      !known(od))
+    return bad_problem("shrink");
+  std::vector<char> x, a, out;
   if (!read_file(dir + "/x.bin", &x, T * H * elem_size(xd)) ||
-      !read_file(dir + "/a.bin", &a, L * K * H * elem_size(ad)) ||
-      !read_file(dir + "/out0.bin", &out, T * K * elem_size(od)) ||
-      !read_file(dir + "/start.bin", &start, batches * 8) ||
-      !read_file(dir + "/lens.bin", &lens, batches * 8) ||
-      !read_file(dir + "/idx.bin", &idx, batches * 8))
-    return 1;
-  DeviceBuffers dev;
+      !read_file(dir + "/a.bin", &a, L * K * H * elem_size(wd)) ||
+      !read_file(dir + "/out0.bin", &out, T * K * elem_size(od)))
+    return false;
+  Device dev;
+  Segments seg;
+  if (!seg.load(dir, batches, &dev)) return false;
   void* dx = dev.upload(x);
   void* da = dev.upload(a);
   void* dout = dev.upload(out);
-  void* dstart = dev.upload(start);
-  void* dlens = dev.upload(lens);
-  void* didx = dev.upload(idx);
-  if (!dx || !da || !dout || !dstart || !dlens || !didx) return 1;
-  hipStream_t stream;
-  if (!hip_ok(hipStreamCreate(&stream), "hipStreamCreate")) return 1;
+  if (!dx || !da || !dout || !hip_ok(hipStreamCreate(&dev.stream), "hipStreamCreate"))
+    return false;
   const sgmv_matrix mx = {dx, xd, T, H, H};
-  const sgmv_stack ma = {da, ad, L, K, H};
+  const sgmv_stack ma = {da, wd, L, K, H};
   const sgmv_matrix mo = {dout, od, T, K, K};
-  int64_t max_len = 0;
-  for (long long b = 0; b < batches; ++b) {
-    int64_t v;
-    memcpy(&v, lens.data() + 8 * b, 8);
-    if (v > max_len) max_len = v;
+  return library_ok(sgmv_shrink(mx, ma, mo, seg.d_start, seg.d_lens, seg.d_idx, batches,
+                                seg.max_len, scale, dev.stream),
+                    "sgmv_shrink") &&
+         finish(&dev, dout, &out, dir);
+}
+
+bool run_fused(const std::string& dir) {
+  long long T, H, K, L, add, batches, H_out;
+  int S, xd, wd, od;
+  float scale;
+  FILE* f = open_problem(dir);
+  if (!f) return false;
+  std::vector<int64_t> widths, offsets;
+  const int n = fscanf(f, "%lld %lld %lld %lld %d %d %d %d %lld %lld %f %lld", &T, &H, &K, &L, &S,
+                       &xd, &wd, &od, &add, &batches, &scale, &H_out);
+  const bool windows = n == 12 && S >= 1 && S <= SGMV_MAX_FUSED_SLICES &&
+                       read_windows(f, S, &widths, &offsets);
+  fclose(f);
+  if (!windows || T < 0 || H < 1 || K < 1 || L < 1 || batches < 0 || H_out < 1 || !known(xd) ||
+      !known(wd) || !known(od))
+    return bad_problem("fused");
+  Device dev;
+  Segments seg;
+  if (!seg.load(dir, batches, &dev)) return false;
+  std::vector<char> x;
+  if (!read_file(dir + "/x.bin", &x, T * H * elem_size(xd))) return false;
+  void* dx = dev.upload(x);
+  if (!dx) return false;
+  std::vector<sgmv_fused_slice> slices(S);
+  for (int i = 0; i < S; ++i) {
+    std::vector<char> a, b;
+    if (!read_file(dir + "/a" + std::to_string(i) + ".bin", &a, L * K * H * elem_size(wd)) ||
+        !read_file(dir + "/b" + std::to_string(i) + ".bin", &b,
+                   L * widths[i] * K * elem_size(wd)))
+      return false;
+    void* da = dev.upload(a);
+    void* db = dev.upload(b);
+    if (!da || !db) return false;
+    slices[i].lora_a = {da, wd, L, K, H};
+    slices[i].lora_b = {db, wd, L, widths[i], K};
+    slices[i].slice_offset = offsets[i];
   }
-  const sgmv_status st = sgmv_shrink(mx, ma, mo, static_cast<const int64_t*>(dstart),
-                                     static_cast<const int64_t*>(dlens),
-                                     static_cast<const int64_t*>(didx), batches, max_len, scale,
-                                     stream);
-  bool ok = library_ok(st, "sgmv_shrink") &&
-            hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize") &&
-            hip_ok(hipMemcpy(out.data(), dout, out.size(), hipMemcpyDeviceToHost),
-                   "hipMemcpy to host");
-  (void)hipStreamDestroy(stream);
-  return ok && write_file(dir + "/out.bin", out) ? 0 : 1;
+  std::vector<char> out;
+  if (!read_file(dir + "/out0.bin", &out, T * H_out * elem_size(od))) return false;
+  void* dout = dev.upload(out);
+  if (!dout || !hip_ok(hipStreamCreate(&dev.stream), "hipStreamCreate")) return false;
+  const sgmv_matrix mx = {dx, xd, T, H, H};
+  const sgmv_matrix mo = {dout, od, T, H_out, H_out};
+  return library_ok(sgmv_fused_shrink_expand(mx, slices.data(), S, mo, seg.d_start, seg.d_lens,
+                                             seg.d_idx, batches, seg.max_len, scale, (int)add,
+                                             dev.stream),
+                    "sgmv_fused_shrink_expand") &&
+         finish(&dev, dout, &out, dir);
 }
 
 }  // namespace
 
 int main(int argc, char** argv) {
-  if (argc != 3 || (strcmp(argv[1], "expand") != 0 && strcmp(argv[1], "shrink") != 0)) {
-    fprintf(stderr, "usage: sgmv_c_client expand|shrink <dir>\n");
+  const char* modes[] = {"expand", "multi", "shrink", "fused"};
+  int mode = -1;
+  for (int i = 0; i < 4 && argc == 3; ++i)
+    if (strcmp(argv[1], modes[i]) == 0) mode = i;
+  if (mode < 0) {
+    fprintf(stderr, "usage: sgmv_c_client expand|multi|shrink|fused <dir>\n");
     return 1;
   }
   if (sgmv_abi_version() != SGMV_ABI_VERSION) {
@@ -216,5 +328,10 @@ int main(int argc, char** argv) {
             SGMV_ABI_VERSION);
     return 1;
   }
-  return strcmp(argv[1], "expand") == 0 ? run_expand(argv[2]) : run_shrink(argv[2]);
+  const std::string dir = argv[2];
+  const bool ok = mode == 0   ? run_expand(dir)
+                  : mode == 1 ? run_multi(dir)
+                  : mode == 2 ? run_shrink(dir)
+                              : run_fused(dir);
+  return ok ? 0 : 1;
 }

@@ -22,6 +22,10 @@ def test_usage_errors(tmp_path):
     assert r.returncode == 1 and "usage" in r.stderr
     r = run_client("transpose", tmp_path, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+    for mode in ("multi", "shrink", "fused"):
+        (tmp_path / "problem.txt").write_text("1 2\n")
+        r = run_client(mode, tmp_path, timeout=60)
+        assert r.returncode == 1 and f"bad {mode} problem.txt" in r.stderr
 
 
 def test_missing_and_malformed_files(tmp_path):

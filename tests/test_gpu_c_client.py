@@ -1,14 +1,17 @@
 """The C-ABI boundary driven by a plain C++ client: examples/sgmv_c_client
 loads libsgmv with only the HIP runtime and include/sgmv.h in the process
-(no Python, no torch), allocates with hipMalloc, enqueues sgmv_expand_slice
-or sgmv_shrink on a stream of its own and copies the result back.  The
-problems are seeded workloads written to files; the results are compared
-with the oracle as in the other parity tests."""
+(no Python, no torch), allocates with hipMalloc, enqueues sgmv_expand_slice,
+sgmv_expand_multi_slice, sgmv_shrink or sgmv_fused_shrink_expand (the
+descriptor arrays laid out by the header itself) on a stream of its own and
+copies the result back.  The problems are seeded workloads written to
+files; the results are compared with the oracle as in the other parity
+tests."""
 import pytest
 
 import sgmv_workloads as W
-from c_client_util import read_out, run_client, write_expand, write_shrink
-from gpu_util import assert_parity, assert_shrink_parity
+from c_client_util import (read_out, run_client, write_expand, write_fused, write_multi,
+                           write_shrink)
+from gpu_util import assert_fused_parity, assert_parity, assert_shrink_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -55,3 +58,26 @@ def test_c_client_reports_a_rejected_call(tmp_path):
     r = run_client("expand", tmp_path)
     assert r.returncode == 1
     assert "sgmv_expand_slice returned 1" in r.stderr
+
+
+@pytest.mark.parametrize("name", ["gqa_qkv", "custom3"])
+def test_c_client_multi_slice_matches_oracle(tmp_path, name):
+    wl = (W.WORKLOADS["gqa_qkv"](0) if name == "gqa_qkv" else
+          W.custom([40, 3, 0, 19, 70], [1, 0, 1, -1, 0], K=32, N=256, H=600, off=16, L=2,
+                   add=True, seed=43, extra_slices=[(300, 70), (400, 136)], name="custom3"))
+    print(f"case {wl.name} slices={len(wl.slices)} via the C client", flush=True)
+    write_multi(tmp_path, wl)
+    r = run_client("multi", tmp_path)
+    assert r.returncode == 0, r.stderr
+    assert_parity(wl, read_out(tmp_path, wl.out0.shape, wl.out_dtype))
+
+
+@pytest.mark.parametrize("add", [False, True])
+def test_c_client_fused_matches_oracle(tmp_path, add):
+    wl = W.fused_custom([90, 3, 0, 150, 64, 1], [1, 0, 1, -1, 2, 0], H=512, K=32, L=3,
+                        slices=[(0, 256), (256, 128), (384, 128)], H_out=520, add=add, seed=44)
+    print(f"case fused add={add} via the C client", flush=True)
+    write_fused(tmp_path, wl)
+    r = run_client("fused", tmp_path)
+    assert r.returncode == 0, r.stderr
+    assert assert_fused_parity(wl, read_out(tmp_path, wl.out0.shape, wl.out_dtype)) > 0
