@@ -26,6 +26,7 @@
 #ifndef SGMV_H
 #define SGMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -33,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SGMV_ABI_VERSION 4
+#define SGMV_ABI_VERSION 5
 #define SGMV_MAX_SLICES 8      /* slices per multi-slice call                       */
 #define SGMV_MAX_RANK 256      /* largest rank the register-tiled kernels take; larger
                                   ranks (any size) run on the generic kernel */
@@ -192,6 +193,22 @@ typedef struct {
  *               as for sgmv_expand_slice, with the same device-side
  *               preconditions.
  * scale         fp32 factor applied to every sum (1 for the plain product).
+ * workspace, workspace_bytes:
+ *               NULL and 0, or a device buffer of at least
+ *               sgmv_shrink_workspace_bytes() bytes, 16-byte aligned, whose
+ *               contents are zero before its first use (hipMemset once);
+ *               every call leaves the buffer ready for the next one.  With
+ *               it, large batches (more 64-token units than the device has
+ *               compute units, at most twice as many) run balanced: the
+ *               units beyond one per compute unit are split over the hidden
+ *               size into parts whose fp32 partial sums go through the
+ *               workspace and are added in a fixed order, so results are
+ *               deterministic but may differ in rounding from a call
+ *               without one (bit for bit equal on integer-valued data).
+ *               Calls that may run at the same time (other streams) need
+ *               workspaces of their own; it must not overlap any other
+ *               argument.  A misaligned or short workspace returns
+ *               SGMV_ERR_INVALID_ARGUMENT.
  *
  * Kernel choice (results are the same within tolerance, and bit for bit on
  * integer-valued data): the register-tiled kernels take rank % 8 == 0,
@@ -207,13 +224,15 @@ typedef struct {
 sgmv_status sgmv_shrink(sgmv_matrix inputs, sgmv_stack lora_a, sgmv_matrix out,
                         const int64_t* b_seq_start_loc, const int64_t* seq_lens,
                         const int64_t* lora_indices, int64_t batches, int64_t max_seq_len,
-                        float scale, hipStream_t stream);
+                        float scale, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /*
  * sgmv_shrink_multi_slice -- several LoRA-A projections of the same inputs
  * (the Q, K and V, or gate and up, adapters of a fused layer) in one call
  * that reads the inputs once.  Equal, bit for bit, to calling sgmv_shrink
- * once per slice.  slices: host array of 1..SGMV_MAX_SLICES descriptors,
+ * once per slice (with the same workspace argument, null or not).  slices:
+ * host array of 1..SGMV_MAX_SLICES descriptors,
  * read during the call only; all share rank, lora_num, the lora_a dtype and
  * the output dtype; outputs must not overlap each other.
  */
@@ -221,7 +240,12 @@ sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice*
                                     int num_slices, const int64_t* b_seq_start_loc,
                                     const int64_t* seq_lens, const int64_t* lora_indices,
                                     int64_t batches, int64_t max_seq_len, float scale,
+                                    void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* Bytes of the workspace sgmv_shrink and sgmv_shrink_multi_slice take on
+ * the current device (16 MiB + 1 KiB on a 256-compute-unit MI355X). */
+sgmv_status sgmv_shrink_workspace_bytes(size_t* bytes);
 
 /* One slice of a fused LoRA delta for sgmv_fused_shrink_expand. */
 typedef struct {
@@ -249,7 +273,8 @@ typedef struct {
  * result of sgmv_shrink_multi_slice into outputs of the weights' dtype
  * followed by sgmv_expand_multi_slice on those outputs (bit for bit equal
  * to them when the shrink takes its large-batch form, i.e. from 64 units of
- * 64 tokens); sums in fp32, each result rounded once (nearest even) to the
+ * 64 tokens, and runs without a workspace: with one, its parts round
+ * differently); sums in fp32, each result rounded once (nearest even) to the
  * output dtype; float32 inputs rounded to the weight dtype first.  Rows of
  * index -1 segments, rows outside every segment and columns outside the
  * windows are left untouched.

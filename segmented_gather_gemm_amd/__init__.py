@@ -31,8 +31,8 @@ MAX_FUSED_SLICES = 3
 
 # Every symbol include/sgmv.h declares.
 EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_bgmv_expand_slice",
-                    "sgmv_shrink", "sgmv_shrink_multi_slice", "sgmv_fused_shrink_expand",
-                    "sgmv_last_error", "sgmv_abi_version")
+                    "sgmv_shrink", "sgmv_shrink_multi_slice", "sgmv_shrink_workspace_bytes",
+                    "sgmv_fused_shrink_expand", "sgmv_last_error", "sgmv_abi_version")
 
 
 class Matrix(ctypes.Structure):
@@ -95,11 +95,15 @@ def _load_library() -> ctypes.CDLL:
     lib.sgmv_expand_multi_slice.restype = ctypes.c_int
     lib.sgmv_bgmv_expand_slice.argtypes = [Matrix, Stack, Matrix, p, i64, i64, ctypes.c_int, p]
     lib.sgmv_bgmv_expand_slice.restype = ctypes.c_int
-    lib.sgmv_shrink.argtypes = [Matrix, Stack, Matrix, p, p, p, i64, i64, ctypes.c_float, p]
+    lib.sgmv_shrink.argtypes = [Matrix, Stack, Matrix, p, p, p, i64, i64, ctypes.c_float, p,
+                                ctypes.c_size_t, p]
     lib.sgmv_shrink.restype = ctypes.c_int
     lib.sgmv_shrink_multi_slice.argtypes = [Matrix, ctypes.POINTER(ShrinkSliceDesc), ctypes.c_int,
-                                            p, p, p, i64, i64, ctypes.c_float, p]
+                                            p, p, p, i64, i64, ctypes.c_float, p,
+                                            ctypes.c_size_t, p]
     lib.sgmv_shrink_multi_slice.restype = ctypes.c_int
+    lib.sgmv_shrink_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.sgmv_shrink_workspace_bytes.restype = ctypes.c_int
     lib.sgmv_fused_shrink_expand.argtypes = [Matrix, ctypes.POINTER(FusedSliceDesc), ctypes.c_int,
                                              Matrix, p, p, p, i64, i64, ctypes.c_float,
                                              ctypes.c_int, p]
@@ -284,23 +288,67 @@ def _stack_a(w, what: str) -> Stack:
     return Stack(w.data_ptr(), _dtype_code(w), w.shape[0], w.shape[1], w.shape[2])
 
 
+def shrink_workspace_bytes(device=None) -> int:
+    """Bytes of the workspace the shrink calls take on `device` (default:
+    the current one)."""
+    device = _torch.device("cuda", _torch.cuda.current_device()) if device is None else \
+        _torch.device(device)
+    n = ctypes.c_size_t()
+    rc = _call_on(device, lib.sgmv_shrink_workspace_bytes, ctypes.byref(n))
+    if rc != SGMV_OK:
+        _raise(rc)
+    return n.value
+
+
+# One zero-filled shrink workspace per device, made on first use.
+_WORKSPACES = {}
+
+
+def _workspace(device, workspace):
+    """(pointer, bytes) for a shrink call's `workspace` argument: True = this
+    device's shared buffer (made and zero-filled on first use; a first use
+    inside a graph capture runs without one, since the fill would run only at
+    replay), None or False = none, a uint8 tensor = the caller's buffer (zero
+    before its first use)."""
+    if workspace is None or workspace is False:
+        return None, 0
+    if workspace is True:
+        ws = _WORKSPACES.get(device.index)
+        if ws is None:
+            if _torch.cuda.is_current_stream_capturing():
+                return None, 0
+            ws = _torch.zeros(shrink_workspace_bytes(device), dtype=_torch.uint8, device=device)
+            _torch.cuda.synchronize(device)
+            _WORKSPACES[device.index] = ws
+        return ws.data_ptr(), ws.numel()
+    if not _torch.is_tensor(workspace) or workspace.device != device or \
+            workspace.dtype != _torch.uint8 or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return workspace.data_ptr(), workspace.numel()
+
+
 def sgmv_shrink(inputs, lora_a_weights, output_tensor, b_seq_start_loc, seq_len_tensor,
-                lora_indices_tensor, batches: int, max_seq_length: int, scaling: float = 1.0):
+                lora_indices_tensor, batches: int, max_seq_length: int, scaling: float = 1.0,
+                workspace=True):
     """LoRA-A projection, in place: output_tensor[start_b + m] =
     scaling * inputs[start_b + m] @ lora_a_weights[lora_indices[b]].T for every
     segment b with index != -1 (other rows untouched); lora_a_weights is
-    (lora_num, rank, hidden).  Enqueued on the current stream."""
+    (lora_num, rank, hidden).  Enqueued on the current stream.  `workspace`:
+    True (the device's shared buffer: calls that may run concurrently on
+    other streams pass buffers of their own), None (large batches run
+    unbalanced) or a zero-initialised uint8 tensor of shrink_workspace_bytes()."""
     return sgmv_shrink_multi_slice(inputs, [(lora_a_weights, output_tensor)], b_seq_start_loc,
                                    seq_len_tensor, lora_indices_tensor, batches, max_seq_length,
-                                   scaling)
+                                   scaling, workspace)
 
 
 def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_seq_start_loc,
                             seq_len_tensor, lora_indices_tensor, batches: int,
-                            max_seq_length: int, scaling: float = 1.0):
+                            max_seq_length: int, scaling: float = 1.0, workspace=True):
     """Several LoRA-A projections of the same inputs (e.g. Q, K, V) reading
     the inputs once.  ``slices``: sequence of (lora_a_weights, output_tensor).
-    Bit-identical to one sgmv_shrink call per slice."""
+    Bit-identical to one sgmv_shrink call per slice with the same
+    `workspace` choice."""
     if not 1 <= len(slices) <= MAX_SLICES:
         raise ValueError(f"1..{MAX_SLICES} slices, got {len(slices)}")
     device, (start, lens, idx) = _common(inputs, [
@@ -314,10 +362,11 @@ def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_s
             raise ValueError(f"slice {i} must be on {device}")
         arr[i] = ShrinkSliceDesc(_stack_a(w, f"slice {i} lora_a"), _matrix(o, f"slice {i} output"))
     x = _matrix(inputs, "inputs")
+    ws, ws_bytes = _workspace(device, workspace)
     stream = _stream(device)
     rc = _call_on(device, lib.sgmv_shrink_multi_slice, x, arr, len(slices), start.data_ptr(),
                   lens.data_ptr(), idx.data_ptr(), int(batches), int(max_seq_length),
-                  float(scaling), stream)
+                  float(scaling), ws, ws_bytes, stream)
     if rc != SGMV_OK:
         _raise(rc)
     return [o for _, o in slices]
@@ -366,6 +415,7 @@ def abi_version() -> int:
 
 
 __all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "bgmv_expand_slice", "sgmv_shrink",
+           "shrink_workspace_bytes",
            "sgmv_shrink_multi_slice", "sgmv_fused_shrink_expand", "abi_version", "SgmvError",
            "lib", "Matrix", "Stack", "SliceDesc", "ShrinkSliceDesc", "FusedSliceDesc",
            "EXPORTED_SYMBOLS", "LIBRARY_PATH"]

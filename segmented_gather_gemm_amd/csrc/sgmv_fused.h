@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void fused_shrink_expand(const FusedParam
     // the previous unit's reads of y_lds before these writes.
     {
       f32x4 acc[Core::kTok][Core::kKt];
-      core.run(su, acc);
+      core.run(su, acc, 0, p.steps);
       __syncthreads();
 #pragma unroll
       for (int h = 0; h < Core::kTok; ++h)

@@ -32,6 +32,31 @@ std::mutex g_mu;
 std::map<int, int> g_cus;
 std::map<std::tuple<int, const void*, size_t>, int> g_occupancy;
 
+// The entry for `dev` in g_cus, filled on first use (g_mu held).
+static hipError_t cached_cus(int dev, std::map<int, int>::iterator* it) {
+  auto cu = g_cus.find(dev);
+  if (cu == g_cus.end()) {
+    int n = 0;
+    const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cu = g_cus.emplace(dev, n > 0 ? n : 1).first;
+  }
+  *it = cu;
+  return hipSuccess;
+}
+
+hipError_t device_compute_units(int* compute_units) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_mu);
+  std::map<int, int>::iterator cu;
+  e = cached_cus(dev, &cu);
+  if (e != hipSuccess) return e;
+  *compute_units = cu->second;
+  return hipSuccess;
+}
+
 hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups,
                            int* compute_units) {
   int dev = 0;
@@ -39,13 +64,9 @@ hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups
   if (e != hipSuccess) return e;
   const size_t bucket = (lds_bytes + 4095) / 4096 * 4096;
   std::lock_guard<std::mutex> lock(g_mu);
-  auto cu = g_cus.find(dev);
-  if (cu == g_cus.end()) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    cu = g_cus.emplace(dev, n > 0 ? n : 1).first;
-  }
+  std::map<int, int>::iterator cu;
+  e = cached_cus(dev, &cu);
+  if (e != hipSuccess) return e;
   const auto key = std::make_tuple(dev, kernel, bucket);
   auto occ = g_occupancy.find(key);
   if (occ == g_occupancy.end()) {

@@ -30,5 +30,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 hipError_t device_capacity(const void* kernel, size_t lds_bytes, int* workgroups,
                            int* compute_units = nullptr);
 
+// The current device's compute-unit count (cached per device, as above).
+hipError_t device_compute_units(int* compute_units);
+
 }  // namespace host
 }  // namespace sgmv

@@ -1,6 +1,6 @@
 // sgmv_limits.h -- size predicates of libsgmv's kernel choices and the
 // work-assignment arithmetic of its kernels, kept free of HIP headers so
-// that they can be checked on any host (the constexpr function below is
+// that they can be checked on any host (the constexpr functions below are
 // also compiled for the device).  Internal to libsgmv.
 #pragma once
 
@@ -68,6 +68,61 @@ constexpr UnitSpan unit_span(uint32_t U, uint32_t G, uint32_t cus, uint32_t bid)
   const uint32_t q = n / m, r = n - q * m;
   const uint32_t b = base + i * q + (i < r ? i : r);
   return UnitSpan{b, b + q + (i < r ? 1u : 0u)};
+}
+
+// Balanced split-T shrink (calls that bring a workspace).  With C compute
+// units (C % 8 == 0) and C < U <= 2 C units of 64 tokens, some compute
+// units would run two units where the others run one, and those set the
+// time (a unit alone takes ~40 us at hidden 4096, two resident ~52-60).
+// Instead workgroups 0..C-1 take one unit each (unit_span over the first C
+// units), and the E = U - C other units are cut into P parts over the
+// hidden steps, taken by workgroups C, C + 1, ...: part r of unit C + e is
+// workgroup C + e P + r.  Parts write fp32 partial sums to the workspace;
+// the last part of a unit to finish adds them in part order and stores the
+// result, so every compute unit holds about U / C units of work.
+// P = min(C / E, kShrinkMaxParts, ceil(h_steps / 4)).  plan.P == 0: the
+// call does not qualify (workspace-free launch, U outside (C, 2 C], a grid
+// below 2 C, or P < 2: with more than 1.5 C units whole overflow units on
+// workgroups C.. measured 4-5% slower than unit_span's XCD-major fill) and
+// the units are split by unit_span.
+#ifndef SGMV_SHRINK_MAX_PARTS
+#define SGMV_SHRINK_MAX_PARTS 4
+#endif
+constexpr uint32_t kShrinkMaxParts = SGMV_SHRINK_MAX_PARTS;
+// Workspace bytes of one part's partial sums: 64 tokens x 256 rows (16 k
+// tiles, the most one launch takes) of fp32.
+constexpr uint32_t kShrinkPartBytes = 64u * 256u * 4u;
+
+struct PartPlan {
+  uint32_t E, P;  // overflow units, parts per overflow unit
+};
+constexpr PartPlan part_plan(uint32_t U, uint32_t C, uint32_t G, uint32_t h_steps) {
+  if (C < 8 || (C & 7) != 0 || U <= C || U > 2 * C || G < 2 * C || h_steps == 0)
+    return PartPlan{0, 0};
+  const uint32_t E = U - C, n4 = (h_steps + 3) / 4;
+  uint32_t P = C / E;
+  if (P > kShrinkMaxParts) P = kShrinkMaxParts;
+  if (P > n4) P = n4;
+  return P < 2 ? PartPlan{0, 0} : PartPlan{E, P};
+}
+
+// Hidden steps [lo, hi) of part r of P (hi may pass h_steps: loads there
+// read nothing): boundaries on multiples of 4 steps, so that they fall on
+// pipeline-block boundaries of every kernel shape and depend only on the
+// hidden size, P and r.
+struct StepSpan {
+  int32_t lo, hi;
+};
+constexpr StepSpan part_steps(uint32_t r, uint32_t P, uint32_t h_steps) {
+  const uint32_t n4 = (h_steps + 3) / 4;
+  return StepSpan{int32_t(4 * (r * n4 / P)), int32_t(4 * ((r + 1) * n4 / P))};
+}
+
+// Workspace layout: C 32-bit part counters (zero between calls), padded to
+// 256 bytes, then C parts of kShrinkPartBytes.
+constexpr int64_t shrink_workspace_counter_bytes(int64_t C) { return (4 * C + 255) / 256 * 256; }
+constexpr int64_t shrink_workspace_bytes(int64_t C) {
+  return shrink_workspace_counter_bytes(C) + C * int64_t(kShrinkPartBytes);
 }
 
 }  // namespace limits

@@ -26,6 +26,11 @@
 //    workgroup and shared through LDS; wave t owns tokens 16 t .. 16 t + 15,
 //    or, with an even number of k tiles (at least 4), 32 tokens and half of
 //    the k tiles, so that each fragment read from LDS feeds two MFMAs.
+//    With a caller's workspace and between C and 2 C units (C compute
+//    units), the units past the first C are cut into parts over the hidden
+//    steps that run beside the whole units, and the last part of each adds
+//    the parts' fp32 sums in part order (limits::part_plan, reduce_parts),
+//    so that no compute unit runs two whole units while others run one.
 //
 // The contraction is y^T = A . x^T on the matrix cores
 // (v_mfma_f32_16x16x32_{bf16,f16}): 16 lora_A rows are the A operand, the 16
@@ -365,6 +370,7 @@ struct SplitTCore {
   static constexpr int xb = XD == F32 ? 4 : 2;
   static constexpr int kBuf = kT * kB;  // fragments of one block
   static constexpr bool kGrid = kT >= 4 && kT % 2 == 0;
+  static constexpr int32_t kTurn = Sh::kRingT * kB;  // hidden steps per turn of the ring
   static constexpr int kTok = kGrid ? 2 : 1;       // token tiles per wave
   static constexpr int kKt = kGrid ? kT / 2 : kT;  // k tiles per wave
   static constexpr int kXBuf = kGrid ? 2 : 1;
@@ -379,7 +385,7 @@ struct SplitTCore {
   ALds& a_lds;
   XLds& x_lds;
   int lane, wave, tw, th, kh, g, j, lr, lb;
-  int32_t H, n_steps, h_steps;
+  int32_t H, h_steps;
   uint32_t xrb;
   uint32_t x_lane[2];
   int x_slot[2];
@@ -402,7 +408,6 @@ struct SplitTCore {
     g = lane >> 4;
     j = lane & 15;
     H = p.H;
-    n_steps = p.steps;  // loop positions per unit, a multiple of kD kB
     h_steps = (H + 31) >> 5;  // hidden steps
     xrb = (uint32_t)p.x_row_bytes;  // 64 rows span < 2 GiB (host)
     // Input loads of a block, xq < kB: rows 16 tw + 8 (xq & 1) .. + 7 over
@@ -434,13 +439,18 @@ struct SplitTCore {
     r_slot = frag_slot(j, g);  // this lane's slot when reading a fragment
   }
 
-  __device__ __forceinline__ void run(const ShrinkUnit<NS>& su, f32x4 (&acc)[kTok][kKt]) {
+  // Hidden steps [s_lo, s_hi) of the unit (s_lo a multiple of kB; the
+  // whole unit is [0, steps)); loads at or past min(s_hi, hidden steps)
+  // read nothing, so their MFMAs add zeros.
+  __device__ __forceinline__ void run(const ShrinkUnit<NS>& su, f32x4 (&acc)[kTok][kKt],
+                                      int32_t s_lo, int32_t s_hi) {
+    const int32_t lim = s_hi < h_steps ? s_hi : h_steps;
     auto load_block = [&](Block& blk, int32_t v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int xq = 0; xq < kB; ++xq) {
         // the lane's 8 elements: step 2 (xq >> 1) + lb / 4 of the block
         const int32_t step = v0 + 2 * (xq >> 1) + (lb >> 2);
-        const bool ok = step < h_steps && 32 * step + 8 * (lb & 3) < H;
+        const bool ok = step < lim && 32 * step + 8 * (lb & 3) < H;
         const uint32_t span = (uint32_t)(32 * (step - (lb >> 2)) * xb);
         buf_load8<XD, kStreamLoad>(su.x, ok ? x_lane[xq & 1] + span : kOut, blk.x[xq]);
       }
@@ -448,7 +458,7 @@ struct SplitTCore {
       for (int q = 0; q < kP; ++q) {
         // the 128-byte span starts at the block's step 2 sp (even)
         const int32_t step = v0 + a_step[q];
-        const bool ok = step < h_steps && 32 * step + 8 * (lb & 3) < H;
+        const bool ok = step < lim && 32 * step + 8 * (lb & 3) < H;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           buf_load8<WD>(su.a[s], ok ? a_lane[q] + (uint32_t)(64 * (step - (lb >> 2))) : kOut,
@@ -498,10 +508,10 @@ struct SplitTCore {
     Block ring[kD];
 #pragma unroll
     for (int d = 0; d + 1 < kD; ++d) {
-      load_block(ring[d], d * kB);
+      load_block(ring[d], s_lo + d * kB);
       __builtin_amdgcn_sched_barrier(0);
     }
-    for (int32_t s = 0; s < n_steps; s += kD * kB) {
+    for (int32_t s = s_lo; s < s_hi; s += kD * kB) {
 #pragma unroll
       for (int d = 0; d < kD; ++d) {
         load_block(ring[(d + kD - 1) % kD], s + (d + kD - 1) * kB);
@@ -514,6 +524,85 @@ struct SplitTCore {
   }
 };
 
+// Cache policy of the parts workspace accesses: device scope (sc1), as
+// atomics at that scope use, so that every XCD sees them in memory.
+constexpr int kDevScope = 0x10;
+
+// Balanced split-T (limits::part_plan): this workgroup's part `part` of P of
+// an overflow unit has its fp32 sums in acc.  Publish them to part slot q
+// (q - part .. q - part + P - 1 are the unit's parts) of the workspace, wait
+// until they are written, and count the part in at the unit's counter.
+// The last part to arrive clears the counter, puts in sum the sum of all P
+// parts' slots taken in part order (the same order and values whichever
+// part ends last) and returns true; the others return false and leave.
+// Slot layout: [wave][token tile h][k tile i][lane], 16 bytes each.
+template <typename Core>
+__device__ __forceinline__ bool reduce_parts(const ShrinkParams& p, uint32_t P, uint32_t e,
+                                             uint32_t part, uint32_t q, int32_t* flag,
+                                             const f32x4 (&acc)[Core::kTok][Core::kKt],
+                                             f32x4 (&sum)[Core::kTok][Core::kKt]) {
+  constexpr int kTok = Core::kTok, kKt = Core::kKt;
+  static_assert(kWaves * kTok * kKt * 1024 <= (int)limits::kShrinkPartBytes, "part slot size");
+  uint32_t* counters = static_cast<uint32_t*>(p.ws);
+  char* slots = static_cast<char*>(p.ws) + limits::shrink_workspace_counter_bytes(p.cus);
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  auto slot_off = [&](int h, int i) __attribute__((always_inline)) {
+    return (uint32_t)(((wave * kTok + h) * kKt + i) * 1024 + lane * 16);
+  };
+  {
+    const rsrc_t mine = make_rsrc(slots + (int64_t)q * limits::kShrinkPartBytes,
+                                  limits::kShrinkPartBytes);
+#pragma unroll
+    for (int h = 0; h < kTok; ++h)
+#pragma unroll
+      for (int i = 0; i < kKt; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[h][i]), mine,
+                                               (int)slot_off(h, i), 0, kDevScope);
+  }
+  // every wave's slot stores complete before the count
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = (int32_t)__hip_atomic_fetch_add(&counters[e], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (uniform(*flag) != (int32_t)P - 1) return false;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[e], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Sum in part order, reading every part (this one's too, written above)
+  // back from the workspace, so that acc (the MFMA accumulators) is dead;
+  // kR parts' loads in flight.
+  constexpr int kR = kTok * kKt <= 8 ? 2 : 1;
+  const uint32_t first = q - part;
+  for (uint32_t r0 = 0; r0 < P; r0 += kR) {
+    f32x4 v[kR][kTok][kKt];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const uint32_t r = r0 + k < P ? r0 + k : r0;
+      const rsrc_t slot = make_rsrc(slots + (int64_t)(first + r) * limits::kShrinkPartBytes,
+                                    limits::kShrinkPartBytes);
+#pragma unroll
+      for (int h = 0; h < kTok; ++h)
+#pragma unroll
+        for (int i = 0; i < kKt; ++i)
+          v[k][h][i] = __builtin_bit_cast(
+              f32x4,
+              __builtin_amdgcn_raw_buffer_load_b128(slot, (int)slot_off(h, i), 0, kDevScope));
+    }
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      if (r0 + k < P) {
+#pragma unroll
+        for (int h = 0; h < kTok; ++h)
+#pragma unroll
+          for (int i = 0; i < kKt; ++i)
+            sum[h][i] = r0 + k == 0 ? v[k][h][i] : sum[h][i] + v[k][h][i];
+      }
+    }
+  }
+  return true;
+}
+
 template <int XD, int WD, int OD, int K16, int NS>
 __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p) {
   using Core = SplitTCore<XD, WD, K16, NS>;
@@ -525,23 +614,65 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
   const SegTable tab = seg_table(lds, p.batches);
   const int32_t U = build_tile_table(p, tab, wave_total, kShrinkTokensSplitT);
   if (U == 0) return;
-  uint32_t u, u_end;
-  unit_range(p, (uint32_t)U, &u, &u_end);
+  // Units, and the hidden steps of each, this workgroup runs: unit_span, or
+  // (a workspace and C < U <= 2 C) one whole unit on each of the first C
+  // workgroups and the parts of the other units on the next ones.
+  const uint32_t C = (uint32_t)p.cus;
+  const limits::PartPlan plan =
+      p.ws ? limits::part_plan((uint32_t)U, C, (uint32_t)p.grid, (uint32_t)((p.H + 31) >> 5))
+           : limits::PartPlan{0, 0};
+  uint32_t u, u_end, q = 0, part = 0;
+  int32_t s_lo = 0, s_hi = p.steps;
+  if (plan.P == 0) {
+    unit_range(p, (uint32_t)U, &u, &u_end);
+  } else if (blockIdx.x < C) {
+    const limits::UnitSpan sp = limits::unit_span(C, C, C, blockIdx.x);
+    u = sp.begin;
+    u_end = sp.end;
+  } else {
+    q = blockIdx.x - C;
+    if (q >= plan.E * plan.P) return;
+    u = C + q / plan.P;
+    u_end = u + 1;
+    part = q % plan.P;
+    const limits::StepSpan ss = limits::part_steps(part, plan.P, (uint32_t)((p.H + 31) >> 5));
+    s_lo = ss.lo;
+    s_hi = ss.hi;
+  }
   if (u >= u_end) return;
 
   Core core(p, a_lds, x_lds);
   int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
-  for (; u < u_end; ++u) {
-    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
-    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kShrinkTokensSplitT);
-    f32x4 acc[Core::kTok][Core::kKt];
-    core.run(su, acc);
+  auto store_unit = [&](int32_t row0, int32_t rows, const f32x4 (&v)[Core::kTok][Core::kKt])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < Core::kTok; ++h)
 #pragma unroll
       for (int i = 0; i < Core::kKt; ++i)
-        shrink_store<OD, K16>(p, core.k_tile(i), su.row0, su.rows, 16 * core.tok_tile(h), core.j,
-                              core.g, acc[h][i]);
+        shrink_store<OD, K16>(p, core.k_tile(i), row0, rows, 16 * core.tok_tile(h), core.j,
+                              core.g, v[h][i]);
+  };
+  // A part (one unit, hidden steps [s_lo, s_hi)) leaves the loop after its
+  // contraction and reduces outside it, where no register the loop keeps
+  // live is needed.
+  const bool is_part = plan.P != 0 && blockIdx.x >= C;
+  f32x4 acc[Core::kTok][Core::kKt];
+  int32_t row0 = 0, rows = 0;
+  for (; u < u_end; ++u) {
+    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
+    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kShrinkTokensSplitT);
+    core.run(su, acc, s_lo, s_hi);
+    if (is_part) {
+      row0 = su.row0;
+      rows = su.rows;
+      break;
+    }
+    store_unit(su.row0, su.rows, acc);
+  }
+  if (is_part) {
+    f32x4 sum[Core::kTok][Core::kKt];
+    if (reduce_parts<Core>(p, plan.P, u - C, part, q, &wave_total[0], acc, sum))
+      store_unit(row0, rows, sum);
   }
 }
 

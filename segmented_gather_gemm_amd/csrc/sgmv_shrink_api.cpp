@@ -48,7 +48,7 @@ int next_pow2(int v) {
 sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices, int first,
                           int count, const int64_t* start, const int64_t* lens,
                           const int64_t* idx, int64_t batches, float scale, bool fast,
-                          bool split_t, hipStream_t stream) {
+                          bool split_t, void* workspace, hipStream_t stream) {
   using namespace sgmv;
   const sgmv_shrink_slice& s0 = slices[first];
   const int64_t K = s0.lora_a.rows;
@@ -105,10 +105,16 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
   const int64_t units =
       (x.rows + tile_rows - 1) / tile_rows + (batches < x.rows ? batches : x.rows);
   int64_t grid = units < capacity ? units : capacity;
+  // With a workspace, split-T batches that may have more units than compute
+  // units get at least two workgroups per compute unit, so that the kernel
+  // can balance C < U <= 2 C units (limits::part_plan); the choice depends
+  // only on the unit bound and the device, never on the slices' kernel.
+  if (fast && split_t && workspace && units > cus && grid < 2 * (int64_t)cus) grid = 2 * (int64_t)cus;
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
   p.cus = cus;
+  p.ws = fast && split_t ? workspace : nullptr;
   void* args[] = {&p};
   e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
   if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -118,7 +124,8 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
 sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slices,
                                     int num_slices, const int64_t* start, const int64_t* lens,
                                     const int64_t* idx, int64_t batches, int64_t max_seq_len,
-                                    float scale, hipStream_t stream) {
+                                    float scale, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
   using namespace sgmv;
   if (num_slices < 1 || num_slices > SGMV_MAX_SLICES)
     return fail(SGMV_ERR_INVALID_ARGUMENT, "num_slices must be in 1..%d, got %d",
@@ -177,6 +184,17 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
   for (int i = 0; i < num_slices; ++i)
     if (!slices[i].out.data || (!slices[i].lora_a.data && L > 0))
       return fail(SGMV_ERR_INVALID_ARGUMENT, "slice %d: null data pointer", i);
+  if (workspace) {
+    int cus = 0;
+    const hipError_t e = device_compute_units(&cus);
+    if (e != hipSuccess)
+      return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+    const int64_t need = sgmv::limits::shrink_workspace_bytes(cus);
+    if (!aligned16(workspace) || (int64_t)workspace_bytes < need)
+      return fail(SGMV_ERR_INVALID_ARGUMENT,
+                  "workspace must be 16-byte aligned and hold %lld bytes (got %zu)",
+                  (long long)need, workspace_bytes);
+  }
 
   // Fast kernels: 16-byte blocks everywhere, hidden < 2^26, a unit's rows
   // (64) of inputs or outputs spanning less than 2 GiB, and the lora_A rows
@@ -212,7 +230,7 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
     while (first + count < num_slices && count < limit && fast_slice(first + count) == fast)
       ++count;
     const sgmv_status st = shrink_launch(x, slices, first, count, start, lens, idx, batches,
-                                         scale, fast, split_t, stream);
+                                         scale, fast, split_t, workspace, stream);
     if (st != SGMV_OK) return st;
     first += count;
   }
@@ -227,22 +245,35 @@ extern "C" {
 sgmv_status sgmv_shrink(sgmv_matrix inputs, sgmv_stack lora_a, sgmv_matrix out,
                         const int64_t* b_seq_start_loc, const int64_t* seq_lens,
                         const int64_t* lora_indices, int64_t batches, int64_t max_seq_len,
-                        float scale, hipStream_t stream) {
+                        float scale, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   sgmv_shrink_slice s;
   s.lora_a = lora_a;
   s.out = out;
   return shrink_check_and_launch(inputs, &s, 1, b_seq_start_loc, seq_lens, lora_indices, batches,
-                                 max_seq_len, scale, stream);
+                                 max_seq_len, scale, workspace, workspace_bytes, stream);
 }
 
 sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice* slices,
                                     int num_slices, const int64_t* b_seq_start_loc,
                                     const int64_t* seq_lens, const int64_t* lora_indices,
                                     int64_t batches, int64_t max_seq_len, float scale,
+                                    void* workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
   if (!slices) return fail(SGMV_ERR_INVALID_ARGUMENT, "slices pointer is null");
   return shrink_check_and_launch(inputs, slices, num_slices, b_seq_start_loc, seq_lens,
-                                 lora_indices, batches, max_seq_len, scale, stream);
+                                 lora_indices, batches, max_seq_len, scale, workspace,
+                                 workspace_bytes, stream);
+}
+
+sgmv_status sgmv_shrink_workspace_bytes(size_t* bytes) {
+  if (!bytes) return fail(SGMV_ERR_INVALID_ARGUMENT, "bytes pointer is null");
+  int cus = 0;
+  const hipError_t e = device_compute_units(&cus);
+  if (e != hipSuccess) return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  *bytes = (size_t)sgmv::limits::shrink_workspace_bytes(cus);
+  g_error.clear();
+  return SGMV_OK;
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@ struct ShrinkParams {
   const int64_t* start;
   const int64_t* lens;
   const int64_t* idx;
+  void* ws;               // split-T parts workspace (limits::part_plan), or null
   int64_t x_row_bytes;
   int64_t T;
   int32_t H;              // hidden size (< 2^26)
@@ -50,7 +51,8 @@ struct ShrinkParams {
 //  * split-T: a unit is 64 tokens, 16 per wave; every wave runs all hidden
 //    steps and the lora_A rows of a block of steps are loaded once per
 //    workgroup into LDS and read by all four waves -- a quarter of split-H's
-//    lora_A traffic per input row.
+//    lora_A traffic per input row.  With a workspace (ShrinkParams::ws),
+//    batches of C < U <= 2 C units run balanced (limits::part_plan).
 // Template shape: K16 = 16-row tiles of K per slice (1, 2, 4, 8, 16), NS =
 // slices per launch (1..3), K16 * NS <= 16.
 constexpr int kShrinkMaxSlicesPerLaunch = 3;

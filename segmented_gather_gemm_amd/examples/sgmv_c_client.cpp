@@ -11,8 +11,9 @@
 //   multi   sgmv_expand_multi_slice.  problem.txt: "T K H L S xd wd od add
 //           batches", then S lines "N offset"; x<i>.bin (T x K, xd) and
 //           w<i>.bin (L x N_i x K, wd) per slice i
-//   shrink  sgmv_shrink.  problem.txt: "T H K L xd wd od scale batches";
-//           x.bin (T x H, xd), a.bin (L x K x H, wd)
+//   shrink  sgmv_shrink with a workspace of sgmv_shrink_workspace_bytes().
+//           problem.txt: "T H K L xd wd od scale batches"; x.bin (T x H,
+//           xd), a.bin (L x K x H, wd)
 //   fused   sgmv_fused_shrink_expand.  problem.txt: "T H K L S xd wd od add
 //           batches scale H_out", then S lines "N offset"; x.bin (T x H,
 //           xd), a<i>.bin (L x K x H, wd), b<i>.bin (L x N_i x K, wd)
@@ -94,6 +95,16 @@ struct Device {
     ptrs.push_back(p);
     if (!host.empty() && !hip_ok(hipMemcpy(p, host.data(), host.size(), hipMemcpyHostToDevice),
                                  "hipMemcpy to device"))
+      return nullptr;
+    return p;
+  }
+  // A zero-filled device buffer of `bytes`.
+  void* zeros(size_t bytes) {
+    void* p = nullptr;
+    if (!hip_ok(hipMalloc(&p, bytes ? bytes : 1), "hipMalloc")) return nullptr;
+    ptrs.push_back(p);
+    if (!hip_ok(hipMemset(p, 0, bytes), "hipMemset") ||
+        !hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize"))
       return nullptr;
     return p;
   }
@@ -254,11 +265,16 @@ bool run_shrink(const std::string& dir) {
   void* dout = dev.upload(out);
   if (!dx || !da || !dout || !hip_ok(hipStreamCreate(&dev.stream), "hipStreamCreate"))
     return false;
+  size_t ws_bytes = 0;
+  if (!library_ok(sgmv_shrink_workspace_bytes(&ws_bytes), "sgmv_shrink_workspace_bytes"))
+    return false;
+  void* ws = dev.zeros(ws_bytes);
+  if (!ws) return false;
   const sgmv_matrix mx = {dx, xd, T, H, H};
   const sgmv_stack ma = {da, wd, L, K, H};
   const sgmv_matrix mo = {dout, od, T, K, K};
   return library_ok(sgmv_shrink(mx, ma, mo, seg.d_start, seg.d_lens, seg.d_idx, batches,
-                                seg.max_len, scale, dev.stream),
+                                seg.max_len, scale, ws, ws_bytes, dev.stream),
                     "sgmv_shrink") &&
          finish(&dev, dout, &out, dir);
 }

@@ -133,19 +133,20 @@ class DeviceShrink:
     def fresh_outs(self):
         return [_device_clone(o) for o in self.outs0]
 
-    def run(self, outs=None, multi=True, idx=None):
-        """One multi-slice call, or one sgmv_shrink call per slice."""
+    def run(self, outs=None, multi=True, idx=None, workspace=True):
+        """One multi-slice call, or one sgmv_shrink call per slice (`workspace`
+        as the binding takes it: True = the device's shared buffer)."""
         import segmented_gather_gemm_amd as sg
         wl = self.wl
         outs = self.fresh_outs() if outs is None else outs
         idx = self.idx if idx is None else idx
         if multi:
             sg.sgmv_shrink_multi_slice(self.x, list(zip(self.a, outs)), self.start, self.lens,
-                                       idx, wl.batches, wl.max_seq_len, wl.scale)
+                                       idx, wl.batches, wl.max_seq_len, wl.scale, workspace)
         else:
             for a, o in zip(self.a, outs):
                 sg.sgmv_shrink(self.x, a, o, self.start, self.lens, idx, wl.batches,
-                               wl.max_seq_len, wl.scale)
+                               wl.max_seq_len, wl.scale, workspace)
         return outs
 
 
@@ -253,9 +254,12 @@ class DeviceFused:
                                     wl.max_seq_len, wl.scale, wl.add)
         return out
 
-    def run_two(self, out=None):
+    def run_two(self, out=None, workspace=None):
         """The two-call path: sgmv_shrink_multi_slice into weight-dtype
-        projections, then sgmv_expand_multi_slice of them."""
+        projections, then sgmv_expand_multi_slice of them.  Without a
+        workspace (the default here) the shrink sums every hidden step in one
+        accumulator, as the fused kernel does, so the two paths agree bit for
+        bit; with one, large batches add hidden parts in another order."""
         import torch
         import segmented_gather_gemm_amd as sg
         wl = self.wl
@@ -263,7 +267,7 @@ class DeviceFused:
         ys = [torch.zeros((wl.T, wl.K), dtype=torch_dtype(wl.w_dtype), device=out.device)
               for _ in wl.lora_a]
         sg.sgmv_shrink_multi_slice(self.x, list(zip(self.a, ys)), self.start, self.lens,
-                                   self.idx, wl.batches, wl.max_seq_len, wl.scale)
+                                   self.idx, wl.batches, wl.max_seq_len, wl.scale, workspace)
         sg.sgmv_expand_multi_slice([(y, b, off) for y, b, off in zip(ys, self.b, wl.offsets)],
                                    out, self.start, self.lens, self.idx, wl.batches,
                                    wl.max_seq_len, wl.add)

@@ -173,11 +173,12 @@ def test_one_hip_runtime_in_process():
 # LoRA-A projection (shrink).
 # --------------------------------------------------------------------------
 
-def shrink(x=None, a=None, out=None, meta=(FAKE, FAKE, FAKE), batches=2, max_len=6, scale=1.0):
+def shrink(x=None, a=None, out=None, meta=(FAKE, FAKE, FAKE), batches=2, max_len=6, scale=1.0,
+           ws=None, ws_bytes=0):
     x = x or Matrix(FAKE, F16, 10, 64, 64)
     a = a or Stack(FAKE, F16, 2, 8, 64)
     out = out or Matrix(FAKE, F16, 10, 8, 8)
-    st = sg.lib.sgmv_shrink(x, a, out, *meta, batches, max_len, scale, None)
+    st = sg.lib.sgmv_shrink(x, a, out, *meta, batches, max_len, scale, ws, ws_bytes, None)
     return st, sg.lib.sgmv_last_error().decode()
 
 
@@ -223,7 +224,7 @@ def test_shrink_multi_slice_checks():
         arr = (sg.ShrinkSliceDesc * max(len(slices), 1))(*slices)
         st = sg.lib.sgmv_shrink_multi_slice(Matrix(FAKE, F16, 10, 64, 64), arr,
                                             len(slices) if n is None else n, FAKE, FAKE, FAKE,
-                                            batches, 6, 1.0, None)
+                                            batches, 6, 1.0, None, 0, None)
         return st, sg.lib.sgmv_last_error().decode()
 
     assert multi_shrink([sl(), sl(rank=16)])[0] == INVALID
@@ -233,8 +234,19 @@ def test_shrink_multi_slice_checks():
     assert multi_shrink([sl()], n=0)[0] == INVALID
     assert multi_shrink([sl(), sl()], batches=0) == (OK, "")
     st = sg.lib.sgmv_shrink_multi_slice(Matrix(FAKE, F16, 10, 64, 64), None, 1, FAKE, FAKE, FAKE,
-                                        2, 6, 1.0, None)
+                                        2, 6, 1.0, None, 0, None)
     assert st == INVALID
+
+
+def test_shrink_workspace_checks_follow_the_argument_checks():
+    """A workspace never masks an argument error, and no-op calls ignore it
+    (the workspace's own size and alignment checks need the device's compute
+    unit count: tests/test_gpu_shrink.py)."""
+    st, msg = shrink(a=Stack(FAKE, F16, 2, 8, 32), ws=FAKE, ws_bytes=1)
+    assert st == INVALID and "hidden" in msg
+    assert shrink(batches=0, ws=FAKE + 3, ws_bytes=1) == (OK, "")
+    assert sg.lib.sgmv_shrink_workspace_bytes(None) == INVALID
+    assert "bytes pointer" in sg.lib.sgmv_last_error().decode()
 
 
 # --------------------------------------------------------------------------

@@ -34,9 +34,22 @@ def test_c_client_expand_matches_oracle(tmp_path, case):
     assert_parity(wl, got)
 
 
-@pytest.mark.parametrize("name", ["shrink_tiny", "shrink_q_proj"])
+def _shrink_case(name):
+    if name == "shrink_tiny":
+        return W.shrink_tiny(0)
+    if name == "balanced":
+        # more 64-token units than compute units: parts through the workspace
+        import torch
+        units = torch.cuda.get_device_properties(0).multi_processor_count + 42
+        return W.shrink_custom([64] * units, [i % 5 for i in range(units)], H=512, K=64, L=5,
+                               slices=1, x_dtype="bf16", a_dtype="bf16", out_dtype="f32",
+                               seed=units)
+    return W.SHRINK_WORKLOADS[name](0)
+
+
+@pytest.mark.parametrize("name", ["shrink_tiny", "shrink_q_proj", "balanced"])
 def test_c_client_shrink_matches_oracle(tmp_path, name):
-    wl = W.shrink_tiny(0) if name == "shrink_tiny" else W.SHRINK_WORKLOADS[name](0)
+    wl = _shrink_case(name)
     print(f"case {wl.name} T={wl.T} via the C client", flush=True)
     write_shrink(tmp_path, wl)
     r = run_client("shrink", tmp_path)

@@ -69,6 +69,38 @@ def test_shrink_graph_replays_match_eager(multi, T):
             assert np.array_equal(a, b)
 
 
+def test_shrink_balanced_graph_replays_match_eager():
+    """A balanced split-T call (more 64-token units than compute units, parts
+    added through the shared workspace) captured and replayed with eager
+    calls in between: every replay leaves the workspace counters at zero for
+    the next call, eager or replayed."""
+    import torch
+    from gpu_util import DeviceShrink, assert_shrink_parity
+    C = torch.cuda.get_device_properties(0).multi_processor_count
+    units = C + 42
+    wl = W.shrink_custom([64] * units, [i % 5 for i in range(units)], H=1024, K=64, L=5,
+                         slices=2, x_dtype="bf16", a_dtype="bf16", out_dtype="f32", seed=units)
+    dw = DeviceShrink(wl)
+    eager = [to_host_bits(o) for o in dw.run()]
+    assert assert_shrink_parity(wl, eager) > 0
+    outs = dw.fresh_outs()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        dw.run(outs)
+    for replay in range(4):
+        for o, o0 in zip(outs, dw.outs0):
+            o.copy_(o0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert np.array_equal(to_host_bits(o), eager[i]), f"replay {replay} slice {i}"
+        other = [to_host_bits(o) for o in dw.run()]
+        torch.cuda.synchronize()
+        for a, b in zip(other, eager):
+            assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("add", [False, True])
 def test_fused_graph_replays_match_eager(add):
     """sgmv_fused_shrink_expand captured once and replayed."""

@@ -18,11 +18,11 @@ from gpu_util import DeviceShrink, assert_shrink_parity, to_host_bits
 pytestmark = pytest.mark.gpu
 
 
-def run_and_check(wl, rows=None, multi=True, exact=False):
+def run_and_check(wl, rows=None, multi=True, exact=False, workspace=True):
     print(f"case {wl.name} T={wl.T} H={wl.H} K={wl.K} slices={len(wl.lora_a)} "
-          f"dtypes={wl.x_dtype}/{wl.a_dtype}/{wl.out_dtype}", flush=True)
+          f"dtypes={wl.x_dtype}/{wl.a_dtype}/{wl.out_dtype} workspace={workspace}", flush=True)
     dw = DeviceShrink(wl)
-    outs = [to_host_bits(o) for o in dw.run(multi=multi)]
+    outs = [to_host_bits(o) for o in dw.run(multi=multi, workspace=workspace)]
     return assert_shrink_parity(wl, outs, rows=rows, exact=exact)
 
 
@@ -245,11 +245,115 @@ def test_shrink_multi_slice_with_a_misaligned_output_equals_single_calls():
 def test_shrink_unit_assignment_around_the_compute_unit_count(units):
     """`units` segments of 64 tokens, each one split-T unit, in a grid of about
     twice as many workgroups (the host sizes it from ceil(T / 64) + segments):
-    up to the compute unit count the units are spread evenly over the XCDs,
-    beyond it they fill XCD after XCD (unit_span in sgmv_limits.h).  Every
-    row of every unit is compared with the oracle."""
+    without a workspace, up to the compute unit count the units are spread
+    evenly over the XCDs, beyond it they fill XCD after XCD (unit_span in
+    sgmv_limits.h).  Every row of every unit is compared with the oracle."""
     lens = [64] * units
     idx = [i % 7 for i in range(units)]  # every segment active: exactly `units` units
     wl = W.shrink_custom(lens, idx, H=256, K=64, L=7, slices=2, x_dtype="bf16", a_dtype="bf16",
                          out_dtype="f32", seed=units)
+    assert run_and_check(wl, workspace=None) > 0
+
+
+def compute_units():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def units_workload(units, seed, values="normal", H=1024, K=64, slices=2,
+                   dts=("bf16", "bf16", "f32")):
+    """`units` active segments of 64 tokens (exactly that many split-T
+    units), adapters cycling over 7."""
+    lens = [64] * units
+    idx = [i % 7 for i in range(units)]
+    return W.shrink_custom(lens, idx, H=H, K=K, L=7, slices=slices, x_dtype=dts[0],
+                           a_dtype=dts[1], out_dtype=dts[2], values=values, seed=seed)
+
+
+# Units beyond the compute units C: 1 (8 parts each), C/6 (6 parts), C/4 (4),
+# C/2 (2), C/2 + 1 and C (one part each: unit_span instead), C + 1 (more than
+# 2 C units: unit_span).
+BALANCE_EXTRA = [1, 42, 64, 128, 129, 256, 257]
+
+
+@pytest.mark.parametrize("extra", BALANCE_EXTRA)
+def test_shrink_balanced_parts_around_twice_the_compute_units(extra):
+    """With the workspace, C < U <= 2 C units run as one whole unit per
+    compute unit plus the other units cut into hidden parts whose fp32 sums
+    are added through the workspace (limits::part_plan); every row of every
+    unit is compared with the oracle."""
+    C = compute_units()
+    wl = units_workload(C + extra, seed=extra)
     assert run_and_check(wl) > 0
+
+
+@pytest.mark.parametrize("extra", [1, 42, 128, 129])
+def test_shrink_balanced_integer_data_bit_exact_and_equal_without_workspace(extra):
+    """On integer-valued data every fp32 partial sum is exact, so the
+    balanced call, the call without a workspace and the oracle agree bit for
+    bit (hidden 1000: a partial last step, and parts of unequal length)."""
+    C = compute_units()
+    wl = units_workload(C + extra, seed=100 + extra, values="int", H=1000, K=24, slices=3,
+                        dts=("f16", "f16", "bf16"))
+    dw = DeviceShrink(wl)
+    bal = [to_host_bits(o) for o in dw.run(workspace=True)]
+    plain = [to_host_bits(o) for o in dw.run(workspace=None)]
+    for a, b in zip(bal, plain):
+        assert np.array_equal(a, b)
+    assert assert_shrink_parity(wl, bal, exact=True) > 0
+
+
+def test_shrink_balanced_multi_slice_equals_single_calls():
+    """Part boundaries depend only on the hidden size and the part count, so
+    a three-slice call (one launch of 6 k tiles) equals three single calls
+    (2 k tiles each, another pipeline shape) bit for bit on random data."""
+    C = compute_units()
+    wl = units_workload(C + 42, seed=7, H=4096, K=32, slices=3, dts=("bf16", "bf16", "bf16"))
+    dw = DeviceShrink(wl)
+    a = [to_host_bits(o) for o in dw.run(multi=True)]
+    b = [to_host_bits(o) for o in dw.run(multi=False)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert assert_shrink_parity(wl, a) > 0
+
+
+def test_shrink_balanced_repeated_calls_and_a_callers_workspace():
+    """Calls in a row on the shared workspace (each leaves its counters at
+    zero for the next), a smaller batch after a larger one, and a caller's
+    own zero-filled workspace all give the same results."""
+    import torch
+    import segmented_gather_gemm_amd as sg
+    C = compute_units()
+    big = units_workload(C + 30, seed=31)
+    small = units_workload(C + 5, seed=32)
+    dbig, dsmall = DeviceShrink(big), DeviceShrink(small)
+    first = [to_host_bits(o) for o in dbig.run()]
+    assert assert_shrink_parity(big, first) > 0
+    assert assert_shrink_parity(small, [to_host_bits(o) for o in dsmall.run()]) > 0
+    again = [to_host_bits(o) for o in dbig.run()]
+    ws = torch.zeros(sg.shrink_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    own = [to_host_bits(o) for o in dbig.run(workspace=ws)]
+    for x, y, z in zip(first, again, own):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
+    counter_bytes = (4 * C + 255) // 256 * 256
+    assert not bool(ws[:counter_bytes].any())  # the counters are back at zero
+
+
+def test_shrink_workspace_size_and_alignment_checked():
+    import ctypes
+    import torch
+    import segmented_gather_gemm_amd as sg
+    C = compute_units()
+    need = sg.shrink_workspace_bytes()
+    assert need == (4 * C + 255) // 256 * 256 + C * 64 * 256 * 4
+    wl = units_workload(C + 1, seed=3)
+    dw = DeviceShrink(wl)
+    ws = torch.zeros(need + 16, dtype=torch.uint8, device="cuda")
+    for ptr, n, frag in ((ws.data_ptr(), need - 1, "hold"), (ws.data_ptr() + 8, need, "aligned")):
+        out = dw.fresh_outs()[0]
+        st = sg.lib.sgmv_shrink(sg._matrix(dw.x, "x"), sg._stack_a(dw.a[0], "a"),
+                                sg._matrix(out, "out"), dw.start.data_ptr(), dw.lens.data_ptr(),
+                                dw.idx.data_ptr(), wl.batches, wl.max_seq_len,
+                                ctypes.c_float(wl.scale), ptr, n, None)
+        assert st == sg.SGMV_ERR_INVALID_ARGUMENT
+        assert frag in sg.lib.sgmv_last_error().decode()

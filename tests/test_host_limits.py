@@ -141,3 +141,76 @@ def test_unit_spans_partition_and_balance(spans, U, G, cus):
         ordered = [sizes[i] for i in order]
         assert all(s in (q, q + 1) for s in ordered)
         assert ordered == sorted(ordered, reverse=True)
+
+
+PART_PROBE = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "sgmv_limits.h"
+// argv: U C G h_steps -> "max_parts E P counter_bytes workspace_bytes", then
+// one line "lo hi" per part
+int main(int argc, char** argv) {
+  const unsigned U = atoi(argv[1]), C = atoi(argv[2]), G = atoi(argv[3]), h = atoi(argv[4]);
+  const sgmv::limits::PartPlan pl = sgmv::limits::part_plan(U, C, G, h);
+  printf("%u %u %u %lld %lld\n", sgmv::limits::kShrinkMaxParts, pl.E, pl.P,
+         (long long)sgmv::limits::shrink_workspace_counter_bytes(C),
+         (long long)sgmv::limits::shrink_workspace_bytes(C));
+  for (unsigned r = 0; r < pl.P; ++r) {
+    const sgmv::limits::StepSpan s = sgmv::limits::part_steps(r, pl.P, h);
+    printf("%d %d\n", s.lo, s.hi);
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def parts(tmp_path_factory):
+    d = tmp_path_factory.mktemp("parts")
+    src = d / "part.cpp"
+    src.write_text(PART_PROBE)
+    exe = d / "part"
+    subprocess.run(["g++", "-std=c++17", "-O1", f"-I{CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+
+    def run(U, C, G, h):
+        out = subprocess.run([str(exe), str(U), str(C), str(G), str(h)], check=True,
+                             capture_output=True, text=True).stdout.split("\n")
+        kmax, E, P, cb, wb = (int(t) for t in out[0].split())
+        spans = [tuple(int(t) for t in line.split()) for line in out[1:] if line.strip()]
+        return kmax, E, P, cb, wb, spans
+    return run
+
+
+# (units, compute units, grid, hidden steps): around C and 2 C units (the
+# named shrink batches have 298 and 319 units of 64 tokens on 256 compute
+# units), grids below 2 C, hidden sizes with fewer 4-step groups than parts
+PART_CASES = [(U, 256, G, h) for U in (0, 255, 256, 257, 298, 319, 320, 384, 385, 450, 512, 513)
+              for G in (256, 504, 512, 768) for h in (1, 3, 4, 7, 32, 128, 256)] + \
+             [(100, 64, 128, 128), (304 + 30, 304, 608, 128), (20, 12, 24, 128)]
+
+
+@pytest.mark.parametrize("U,C,G,h", PART_CASES)
+def test_part_plan_and_step_spans(parts, U, C, G, h):
+    kmax, E, P, cb, wb, spans = parts(U, C, G, h)
+    n4 = (h + 3) // 4
+    qualifies = C >= 8 and C % 8 == 0 and C < U <= 2 * C and G >= 2 * C
+    want_p = min(C // (U - C), kmax, n4) if qualifies else 0
+    if want_p < 2:
+        assert (E, P) == (0, 0) and spans == []
+    else:
+        assert (E, P) == (U - C, want_p)
+        # the parts fit the workgroups after the first C (grid >= 2 C)
+        assert E * P <= C and C + E * P <= G
+        # spans: contiguous, non-empty, on multiples of 4 steps, covering
+        # every hidden step; they depend on (P, h) only
+        assert spans[0][0] == 0
+        for (lo, hi), (lo2, _) in zip(spans, spans[1:]):
+            assert hi == lo2
+        for lo, hi in spans:
+            assert lo % 4 == 0 and hi % 4 == 0 and hi > lo
+        assert spans[-1][1] == 4 * n4 >= h
+    # workspace: one 32-bit counter per compute unit (padded to 256 bytes),
+    # then one 64 KiB slot per possible part
+    assert cb % 256 == 0 and 4 * C <= cb < 4 * C + 256
+    assert wb == cb + C * 64 * 256 * 4
