@@ -247,6 +247,28 @@ sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice*
  * the current device (16 MiB + 1 KiB on a 256-compute-unit MI355X). */
 sgmv_status sgmv_shrink_workspace_bytes(size_t* bytes);
 
+/*
+ * sgmv_shrink_multi_slice_noalloc -- sgmv_shrink_multi_slice for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the workspace is a static
+ * array inside the library (one copy per device, 20 MiB + 1280 bytes,
+ * covering devices of up to 320 compute units, held until the process
+ * ends) instead of an argument.  Each call first clears the array's part
+ * counters with a small kernel on `stream`, then runs exactly what
+ * sgmv_shrink_multi_slice with a workspace runs (same results, bit for
+ * bit).  Calls that may overlap on one device (several streams, or host
+ * threads) race on the shared array: serialise them.  Calls no allocating
+ * routine.  Returns what sgmv_shrink_multi_slice returns, and
+ * SGMV_ERR_UNSUPPORTED on a device with more than 320 compute units (the
+ * array would be too small).
+ */
+sgmv_status sgmv_shrink_multi_slice_noalloc(sgmv_matrix inputs, const sgmv_shrink_slice* slices,
+                                            int num_slices, const int64_t* b_seq_start_loc,
+                                            const int64_t* seq_lens,
+                                            const int64_t* lora_indices, int64_t batches,
+                                            int64_t max_seq_len, float scale,
+                                            hipStream_t stream);
+
 /* One slice of a fused LoRA delta for sgmv_fused_shrink_expand. */
 typedef struct {
   sgmv_stack lora_a;      /* (lora_num, rank, hidden)                     */

@@ -32,6 +32,7 @@ MAX_FUSED_SLICES = 3
 # Every symbol include/sgmv.h declares.
 EXPORTED_SYMBOLS = ("sgmv_expand_slice", "sgmv_expand_multi_slice", "sgmv_bgmv_expand_slice",
                     "sgmv_shrink", "sgmv_shrink_multi_slice", "sgmv_shrink_workspace_bytes",
+                    "sgmv_shrink_multi_slice_noalloc",
                     "sgmv_fused_shrink_expand", "sgmv_last_error", "sgmv_abi_version")
 
 
@@ -104,6 +105,10 @@ def _load_library() -> ctypes.CDLL:
     lib.sgmv_shrink_multi_slice.restype = ctypes.c_int
     lib.sgmv_shrink_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
     lib.sgmv_shrink_workspace_bytes.restype = ctypes.c_int
+    lib.sgmv_shrink_multi_slice_noalloc.argtypes = [Matrix, ctypes.POINTER(ShrinkSliceDesc),
+                                                    ctypes.c_int, p, p, p, i64, i64,
+                                                    ctypes.c_float, p]
+    lib.sgmv_shrink_multi_slice_noalloc.restype = ctypes.c_int
     lib.sgmv_fused_shrink_expand.argtypes = [Matrix, ctypes.POINTER(FusedSliceDesc), ctypes.c_int,
                                              Matrix, p, p, p, i64, i64, ctypes.c_float,
                                              ctypes.c_int, p]
@@ -342,13 +347,9 @@ def sgmv_shrink(inputs, lora_a_weights, output_tensor, b_seq_start_loc, seq_len_
                                    scaling, workspace)
 
 
-def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_seq_start_loc,
-                            seq_len_tensor, lora_indices_tensor, batches: int,
-                            max_seq_length: int, scaling: float = 1.0, workspace=True):
-    """Several LoRA-A projections of the same inputs (e.g. Q, K, V) reading
-    the inputs once.  ``slices``: sequence of (lora_a_weights, output_tensor).
-    Bit-identical to one sgmv_shrink call per slice with the same
-    `workspace` choice."""
+def _shrink_args(inputs, slices, b_seq_start_loc, seq_len_tensor, lora_indices_tensor,
+                 batches):
+    """(device, inputs matrix, slice descriptors, start, lens, idx) of a shrink call."""
     if not 1 <= len(slices) <= MAX_SLICES:
         raise ValueError(f"1..{MAX_SLICES} slices, got {len(slices)}")
     device, (start, lens, idx) = _common(inputs, [
@@ -361,12 +362,40 @@ def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_s
         if w.device != device or o.device != device:
             raise ValueError(f"slice {i} must be on {device}")
         arr[i] = ShrinkSliceDesc(_stack_a(w, f"slice {i} lora_a"), _matrix(o, f"slice {i} output"))
-    x = _matrix(inputs, "inputs")
+    return device, _matrix(inputs, "inputs"), arr, start, lens, idx
+
+
+def sgmv_shrink_multi_slice(inputs, slices: Sequence[Tuple[object, object]], b_seq_start_loc,
+                            seq_len_tensor, lora_indices_tensor, batches: int,
+                            max_seq_length: int, scaling: float = 1.0, workspace=True):
+    """Several LoRA-A projections of the same inputs (e.g. Q, K, V) reading
+    the inputs once.  ``slices``: sequence of (lora_a_weights, output_tensor).
+    Bit-identical to one sgmv_shrink call per slice with the same
+    `workspace` choice."""
+    device, x, arr, start, lens, idx = _shrink_args(inputs, slices, b_seq_start_loc,
+                                                    seq_len_tensor, lora_indices_tensor, batches)
     ws, ws_bytes = _workspace(device, workspace)
     stream = _stream(device)
     rc = _call_on(device, lib.sgmv_shrink_multi_slice, x, arr, len(slices), start.data_ptr(),
                   lens.data_ptr(), idx.data_ptr(), int(batches), int(max_seq_length),
                   float(scaling), ws, ws_bytes, stream)
+    if rc != SGMV_OK:
+        _raise(rc)
+    return [o for _, o in slices]
+
+
+def sgmv_shrink_multi_slice_noalloc(inputs, slices: Sequence[Tuple[object, object]],
+                                    b_seq_start_loc, seq_len_tensor, lora_indices_tensor,
+                                    batches: int, max_seq_length: int, scaling: float = 1.0):
+    """sgmv_shrink_multi_slice on the library's static workspace (for callers
+    that cannot allocate; calls that may overlap on one device race on it).
+    Equal bit for bit to sgmv_shrink_multi_slice with a workspace."""
+    device, x, arr, start, lens, idx = _shrink_args(inputs, slices, b_seq_start_loc,
+                                                    seq_len_tensor, lora_indices_tensor, batches)
+    stream = _stream(device)
+    rc = _call_on(device, lib.sgmv_shrink_multi_slice_noalloc, x, arr, len(slices),
+                  start.data_ptr(), lens.data_ptr(), idx.data_ptr(), int(batches),
+                  int(max_seq_length), float(scaling), stream)
     if rc != SGMV_OK:
         _raise(rc)
     return [o for _, o in slices]
@@ -415,7 +444,7 @@ def abi_version() -> int:
 
 
 __all__ = ["sgmv_expand_slice", "sgmv_expand_multi_slice", "bgmv_expand_slice", "sgmv_shrink",
-           "shrink_workspace_bytes",
+           "shrink_workspace_bytes", "sgmv_shrink_multi_slice_noalloc",
            "sgmv_shrink_multi_slice", "sgmv_fused_shrink_expand", "abi_version", "SgmvError",
            "lib", "Matrix", "Stack", "SliceDesc", "ShrinkSliceDesc", "FusedSliceDesc",
            "EXPORTED_SYMBOLS", "LIBRARY_PATH"]

@@ -9,6 +9,11 @@
 // hidden), out-by-in like lora_B.
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
 #include "sgmv.h"
 #include "sgmv_host.h"
 #include "sgmv_limits.h"
@@ -121,11 +126,68 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
   return SGMV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free variant (sgmv_shrink_multi_slice_noalloc): the workspace
+// is a static device array of the library, one copy per device, held until
+// the process ends.
+// ---------------------------------------------------------------------------
+
+// Largest compute-unit count the static workspace covers (MI355X: 256).
+constexpr int kNoAllocMaxCus = 320;
+constexpr int64_t kNoAllocBytes = sgmv::limits::shrink_workspace_bytes(kNoAllocMaxCus);
+
+// In host code `scratch` is a host-side stand-in, not a device address:
+// only the address hipGetSymbolAddress gives (noalloc_workspace) may reach a
+// kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;  // device -> address of its copy of scratch
+
+// The current device's copy of scratch, looked up on the first call on that
+// device (with it current) and kept.
+hipError_t noalloc_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    it = g_scratch.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
+
+// Zero n part counters (a kernel, not a memset, so that graph capture records
+// a kernel node).
+__global__ void zero_counters(uint32_t* counters, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) counters[i] = 0u;
+}
+
+// Clears the part counters at the start of `workspace` on `stream`.
+sgmv_status clear_workspace_counters(void* workspace, hipStream_t stream) {
+  int cus = 0;
+  hipError_t e = device_compute_units(&cus);
+  if (e != hipSuccess) return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  const int n = (int)(sgmv::limits::shrink_workspace_counter_bytes(cus) / 4);
+  hipLaunchKernelGGL(zero_counters, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(workspace), n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(SGMV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SGMV_OK;
+}
+
 sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slices,
                                     int num_slices, const int64_t* start, const int64_t* lens,
                                     const int64_t* idx, int64_t batches, int64_t max_seq_len,
                                     float scale, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+                                    bool clear_counters, hipStream_t stream) {
   using namespace sgmv;
   if (num_slices < 1 || num_slices > SGMV_MAX_SLICES)
     return fail(SGMV_ERR_INVALID_ARGUMENT, "num_slices must be in 1..%d, got %d",
@@ -223,6 +285,10 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
   if (fast_per_launch > kShrinkMaxSlicesPerLaunch) fast_per_launch = kShrinkMaxSlicesPerLaunch;
   const bool split_t =
       (x.rows + kShrinkTokensSplitT - 1) / kShrinkTokensSplitT >= SGMV_SHRINK_SPLIT_T_MIN_UNITS;
+  if (clear_counters && workspace) {
+    const sgmv_status st = clear_workspace_counters(workspace, stream);
+    if (st != SGMV_OK) return st;
+  }
   for (int first = 0; first < num_slices;) {
     const bool fast = fast_slice(first);
     const int limit = fast ? fast_per_launch : num_slices;
@@ -251,7 +317,7 @@ sgmv_status sgmv_shrink(sgmv_matrix inputs, sgmv_stack lora_a, sgmv_matrix out,
   s.lora_a = lora_a;
   s.out = out;
   return shrink_check_and_launch(inputs, &s, 1, b_seq_start_loc, seq_lens, lora_indices, batches,
-                                 max_seq_len, scale, workspace, workspace_bytes, stream);
+                                 max_seq_len, scale, workspace, workspace_bytes, false, stream);
 }
 
 sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice* slices,
@@ -263,7 +329,32 @@ sgmv_status sgmv_shrink_multi_slice(sgmv_matrix inputs, const sgmv_shrink_slice*
   if (!slices) return fail(SGMV_ERR_INVALID_ARGUMENT, "slices pointer is null");
   return shrink_check_and_launch(inputs, slices, num_slices, b_seq_start_loc, seq_lens,
                                  lora_indices, batches, max_seq_len, scale, workspace,
-                                 workspace_bytes, stream);
+                                 workspace_bytes, false, stream);
+}
+
+sgmv_status sgmv_shrink_multi_slice_noalloc(sgmv_matrix inputs, const sgmv_shrink_slice* slices,
+                                            int num_slices, const int64_t* b_seq_start_loc,
+                                            const int64_t* seq_lens,
+                                            const int64_t* lora_indices, int64_t batches,
+                                            int64_t max_seq_len, float scale,
+                                            hipStream_t stream) {
+  if (!slices) return fail(SGMV_ERR_INVALID_ARGUMENT, "slices pointer is null");
+  int cus = 0;
+  hipError_t e = device_compute_units(&cus);
+  if (e != hipSuccess) return fail(SGMV_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  const int64_t need = sgmv::limits::shrink_workspace_bytes(cus);
+  if (need > kNoAllocBytes)
+    return fail(SGMV_ERR_UNSUPPORTED,
+                "the static workspace covers %d compute units (%lld bytes); this device has %d "
+                "(use sgmv_shrink_multi_slice with a workspace)",
+                kNoAllocMaxCus, (long long)kNoAllocBytes, cus);
+  void* ws = nullptr;
+  e = noalloc_workspace(&ws);
+  if (e != hipSuccess)
+    return fail(SGMV_ERR_HIP, "static workspace lookup failed: %s", hipGetErrorString(e));
+  return shrink_check_and_launch(inputs, slices, num_slices, b_seq_start_loc, seq_lens,
+                                 lora_indices, batches, max_seq_len, scale, ws, (size_t)need,
+                                 true, stream);
 }
 
 sgmv_status sgmv_shrink_workspace_bytes(size_t* bytes) {

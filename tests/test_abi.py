@@ -238,6 +238,13 @@ def test_shrink_multi_slice_checks():
     assert st == INVALID
 
 
+def test_shrink_noalloc_rejects_a_null_slice_array_first():
+    st = sg.lib.sgmv_shrink_multi_slice_noalloc(Matrix(FAKE, F16, 10, 64, 64), None, 1, FAKE,
+                                                FAKE, FAKE, 2, 6, 1.0, None)
+    assert st == INVALID
+    assert "slices pointer" in sg.lib.sgmv_last_error().decode()
+
+
 def test_shrink_workspace_checks_follow_the_argument_checks():
     """A workspace never masks an argument error, and no-op calls ignore it
     (the workspace's own size and alignment checks need the device's compute
