@@ -198,13 +198,15 @@ typedef struct {
  *               sgmv_shrink_workspace_bytes() bytes, 16-byte aligned, whose
  *               contents are zero before its first use (hipMemset once);
  *               every call leaves the buffer ready for the next one.  With
- *               it, large batches (more 64-token units than the device has
- *               compute units, at most twice as many) run balanced: the
- *               units beyond one per compute unit are split over the hidden
- *               size into parts whose fp32 partial sums go through the
- *               workspace and are added in a fixed order, so results are
- *               deterministic but may differ in rounding from a call
- *               without one (bit for bit equal on integer-valued data).
+ *               it, batches of 64-token units run balanced when there are
+ *               more units than the device has compute units (at most twice
+ *               as many: the units beyond one per compute unit are split)
+ *               or at most half as many (every unit is split): units are
+ *               split over the hidden size into parts whose fp32 partial
+ *               sums go through the workspace and are added in a fixed
+ *               order, so results are deterministic but may differ in
+ *               rounding from a call without one (bit for bit equal on
+ *               integer-valued data).
  *               Calls that may run at the same time (other streams) need
  *               workspaces of their own; it must not overlap any other
  *               argument.  A misaligned or short workspace returns

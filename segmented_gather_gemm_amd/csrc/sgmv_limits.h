@@ -70,21 +70,31 @@ constexpr UnitSpan unit_span(uint32_t U, uint32_t G, uint32_t cus, uint32_t bid)
   return UnitSpan{b, b + q + (i < r ? 1u : 0u)};
 }
 
-// Balanced split-T shrink (calls that bring a workspace).  With C compute
-// units (C % 8 == 0) and C < U <= 2 C units of 64 tokens, some compute
-// units would run two units where the others run one, and those set the
-// time (a unit alone takes ~40 us at hidden 4096, two resident ~52-60).
-// Instead workgroups 0..C-1 take one unit each (unit_span over the first C
-// units), and the E = U - C other units are cut into P parts over the
-// hidden steps, taken by workgroups C, C + 1, ...: part r of unit C + e is
-// workgroup C + e P + r.  Parts write fp32 partial sums to the workspace;
-// the last part of a unit to finish adds them in part order and stores the
-// result, so every compute unit holds about U / C units of work.
-// P = min(C / E, kShrinkMaxParts, ceil(h_steps / 4)).  plan.P == 0: the
-// call does not qualify (workspace-free launch, U outside (C, 2 C], a grid
-// below 2 C, or P < 2: with more than 1.5 C units whole overflow units on
-// workgroups C.. measured 4-5% slower than unit_span's XCD-major fill) and
-// the units are split by unit_span.
+// Balanced split-T shrink (calls that bring a workspace; C compute units,
+// C % 8 == 0; a unit alone takes ~40 us at hidden 4096 whatever else runs
+// beside it, so the time is set by the compute units with the most work):
+//  * C < U <= 2 C units: some compute units would run two units where the
+//    others run one.  Workgroups 0..C-1 take one unit each (W = C whole
+//    units, unit_span over them) and the E = U - C other units are cut into
+//    P = min(C / E, kShrinkMaxParts, ceil(h_steps / 4)) parts over the
+//    hidden steps;
+//  * U <= C / 2: most compute units would idle while each unit takes a
+//    unit's time.  Every unit is cut into P = min(C / U, ...) parts (W = 0,
+//    E = U).
+// The E P parts, in unit order, go to workgroups W, W + 1, ... XCD by XCD
+// (part_item): XCD x takes the x-th of 8 contiguous shares (sizes differ by
+// at most one, at most C / 8), so that neighbouring units -- one segment's,
+// or one adapter's in an adapter-ordered table -- and so their lora_A rows
+// stay on one XCD's L2 (a unit's parts straddle two XCDs only at a share's
+// end; dealing consecutive parts to consecutive XCDs instead measured
+// slower on batches where neighbouring units share an adapter: 128 units
+// of 64 tokens, 34.0 against 39.8 us).  Parts write fp32 partial sums to
+// the workspace; the last part of a unit to finish adds them in part order
+// and stores the result.  plan.P == 0: the call does not qualify
+// (workspace-free launch, C / 2 < U <= C or U > 2 C, a grid below W + C, or
+// P < 2: with more than 1.5 C units whole overflow units on workgroups C..
+// measured 4-5% slower than unit_span's XCD-major fill) and the units are
+// split by unit_span.
 #ifndef SGMV_SHRINK_MAX_PARTS
 #define SGMV_SHRINK_MAX_PARTS 4
 #endif
@@ -94,16 +104,35 @@ constexpr uint32_t kShrinkMaxParts = SGMV_SHRINK_MAX_PARTS;
 constexpr uint32_t kShrinkPartBytes = 64u * 256u * 4u;
 
 struct PartPlan {
-  uint32_t E, P;  // overflow units, parts per overflow unit
+  uint32_t W, E, P;  // whole units (on workgroups 0..W-1), overflow units, parts per overflow unit
 };
 constexpr PartPlan part_plan(uint32_t U, uint32_t C, uint32_t G, uint32_t h_steps) {
-  if (C < 8 || (C & 7) != 0 || U <= C || U > 2 * C || G < 2 * C || h_steps == 0)
-    return PartPlan{0, 0};
-  const uint32_t E = U - C, n4 = (h_steps + 3) / 4;
+  if (C < 8 || (C & 7) != 0 || U == 0 || U > 2 * C || h_steps == 0) return PartPlan{0, 0, 0};
+  const uint32_t W = U > C ? C : 0, E = U - W, n4 = (h_steps + 3) / 4;
   uint32_t P = C / E;
   if (P > kShrinkMaxParts) P = kShrinkMaxParts;
   if (P > n4) P = n4;
-  return P < 2 ? PartPlan{0, 0} : PartPlan{E, P};
+  if (P < 2 || G < W + C) return PartPlan{0, 0, 0};
+  return PartPlan{W, E, P};
+}
+
+// The part workgroup `bid` (>= plan.W) runs: part `part` of unit `unit`,
+// with workspace slot (unit - W) P + part, or nothing (valid false).  bid
+// and bid - W have the same XCD (W % 8 == 0); XCD x's share of the parts
+// (slot order) is [x E P/8, (x + 1) E P/8), taken by its workgroups in
+// order of (bid - W) / 8.
+struct PartItem {
+  uint32_t unit, part;
+  bool valid;
+};
+constexpr PartItem part_item(const PartPlan& pl, uint32_t bid) {
+  const uint32_t k = bid - pl.W, x = k & 7, j = k >> 3, I = pl.E * pl.P;
+  const uint32_t share = I >> 3, extra = I & 7;
+  const uint32_t base = x * share + (x < extra ? x : extra);
+  const uint32_t n = share + (x < extra ? 1u : 0u);
+  if (j >= n) return PartItem{0, 0, false};
+  const uint32_t slot = base + j;
+  return PartItem{pl.W + slot / pl.P, slot % pl.P, true};
 }
 
 // Hidden steps [lo, hi) of part r of P (hi may pass h_steps: loads there

@@ -28,9 +28,11 @@
 //    the k tiles, so that each fragment read from LDS feeds two MFMAs.
 //    With a caller's workspace and between C and 2 C units (C compute
 //    units), the units past the first C are cut into parts over the hidden
-//    steps that run beside the whole units, and the last part of each adds
-//    the parts' fp32 sums in part order (limits::part_plan, reduce_parts),
-//    so that no compute unit runs two whole units while others run one.
+//    steps that run beside the whole units, so that no compute unit runs
+//    two whole units while others run one; with at most C / 2 units, every
+//    unit is cut into parts, so that the idle compute units share the work.
+//    The last part of each unit adds the parts' fp32 sums in part order
+//    (limits::part_plan, reduce_parts).
 //
 // The contraction is y^T = A . x^T on the matrix cores
 // (v_mfma_f32_16x16x32_{bf16,f16}): 16 lora_A rows are the A operand, the 16
@@ -615,26 +617,28 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
   const int32_t U = build_tile_table(p, tab, wave_total, kShrinkTokensSplitT);
   if (U == 0) return;
   // Units, and the hidden steps of each, this workgroup runs: unit_span, or
-  // (a workspace and C < U <= 2 C) one whole unit on each of the first C
+  // (a workspace; limits::part_plan) one whole unit on each of the first W
   // workgroups and the parts of the other units on the next ones.
   const uint32_t C = (uint32_t)p.cus;
   const limits::PartPlan plan =
       p.ws ? limits::part_plan((uint32_t)U, C, (uint32_t)p.grid, (uint32_t)((p.H + 31) >> 5))
-           : limits::PartPlan{0, 0};
+           : limits::PartPlan{0, 0, 0};
+  const uint32_t W = plan.W;
   uint32_t u, u_end, q = 0, part = 0;
   int32_t s_lo = 0, s_hi = p.steps;
   if (plan.P == 0) {
     unit_range(p, (uint32_t)U, &u, &u_end);
-  } else if (blockIdx.x < C) {
-    const limits::UnitSpan sp = limits::unit_span(C, C, C, blockIdx.x);
+  } else if (blockIdx.x < W) {
+    const limits::UnitSpan sp = limits::unit_span(W, W, C, blockIdx.x);
     u = sp.begin;
     u_end = sp.end;
   } else {
-    q = blockIdx.x - C;
-    if (q >= plan.E * plan.P) return;
-    u = C + q / plan.P;
+    const limits::PartItem it = limits::part_item(plan, blockIdx.x);
+    if (!it.valid) return;
+    u = it.unit;
     u_end = u + 1;
-    part = q % plan.P;
+    part = it.part;
+    q = (u - W) * plan.P + part;
     const limits::StepSpan ss = limits::part_steps(part, plan.P, (uint32_t)((p.H + 31) >> 5));
     s_lo = ss.lo;
     s_hi = ss.hi;
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
   // A part (one unit, hidden steps [s_lo, s_hi)) leaves the loop after its
   // contraction and reduces outside it, where no register the loop keeps
   // live is needed.
-  const bool is_part = plan.P != 0 && blockIdx.x >= C;
+  const bool is_part = plan.P != 0 && blockIdx.x >= W;
   f32x4 acc[Core::kTok][Core::kKt];
   int32_t row0 = 0, rows = 0;
   for (; u < u_end; ++u) {
@@ -671,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_t(const ShrinkParams p)
   }
   if (is_part) {
     f32x4 sum[Core::kTok][Core::kKt];
-    if (reduce_parts<Core>(p, plan.P, u - C, part, q, &wave_total[0], acc, sum))
+    if (reduce_parts<Core>(p, plan.P, u - W, part, q, &wave_total[0], acc, sum))
       store_unit(row0, rows, sum);
   }
 }

@@ -110,11 +110,15 @@ sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices,
   const int64_t units =
       (x.rows + tile_rows - 1) / tile_rows + (batches < x.rows ? batches : x.rows);
   int64_t grid = units < capacity ? units : capacity;
-  // With a workspace, split-T batches that may have more units than compute
-  // units get at least two workgroups per compute unit, so that the kernel
-  // can balance C < U <= 2 C units (limits::part_plan); the choice depends
-  // only on the unit bound and the device, never on the slices' kernel.
-  if (fast && split_t && workspace && units > cus && grid < 2 * (int64_t)cus) grid = 2 * (int64_t)cus;
+  // With a workspace, split-T launches get a workgroup per compute unit at
+  // least, and two when the batch may have more units than compute units,
+  // so that the kernel can balance its units (limits::part_plan); the
+  // choice depends only on the unit bound and the device, never on the
+  // slices' kernel.
+  if (fast && split_t && workspace) {
+    const int64_t least = (units > cus ? 2 : 1) * (int64_t)cus;
+    if (grid < least) grid = least;
+  }
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;

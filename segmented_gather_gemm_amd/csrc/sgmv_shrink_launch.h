@@ -52,7 +52,8 @@ struct ShrinkParams {
 //    steps and the lora_A rows of a block of steps are loaded once per
 //    workgroup into LDS and read by all four waves -- a quarter of split-H's
 //    lora_A traffic per input row.  With a workspace (ShrinkParams::ws),
-//    batches of C < U <= 2 C units run balanced (limits::part_plan).
+//    batches of C < U <= 2 C or U <= C / 2 units run balanced
+//    (limits::part_plan).
 // Template shape: K16 = 16-row tiles of K per slice (1, 2, 4, 8, 16), NS =
 // slices per launch (1..3), K16 * NS <= 16.
 constexpr int kShrinkMaxSlicesPerLaunch = 3;

@@ -287,6 +287,46 @@ def test_shrink_balanced_parts_around_twice_the_compute_units(extra):
     assert run_and_check(wl) > 0
 
 
+# Small split-T batches (at least 64 units of 64 tokens): C/4 units (4 parts
+# each), about C/3 (3), C/2.56 and C/2 (2), C/2 + 1 (one part: unit_span).
+SMALL_UNITS = [64, 85, 100, 128, 129]
+
+
+@pytest.mark.parametrize("units", SMALL_UNITS)
+def test_shrink_balanced_small_batches_every_unit_in_parts(units):
+    """With the workspace and at most C / 2 units, every unit is cut into
+    hidden parts so that the idle compute units share the work
+    (limits::part_plan); every row compared with the oracle."""
+    C = compute_units()
+    wl = units_workload(units * C // 256, seed=500 + units)
+    assert run_and_check(wl) > 0
+
+
+@pytest.mark.parametrize("units", [64, 100])
+def test_shrink_balanced_small_batches_integer_and_multi_slice(units):
+    """Small balanced batches: integer data bit for bit equal to the call
+    without a workspace and to the oracle, and a three-slice call equal to
+    its single calls on random data."""
+    C = compute_units()
+    n = units * C // 256
+    wl = units_workload(n, seed=600 + units, values="int", H=1000, K=24, slices=3,
+                        dts=("f16", "f16", "bf16"))
+    dw = DeviceShrink(wl)
+    bal = [to_host_bits(o) for o in dw.run(workspace=True)]
+    plain = [to_host_bits(o) for o in dw.run(workspace=None)]
+    for a, b in zip(bal, plain):
+        assert np.array_equal(a, b)
+    assert assert_shrink_parity(wl, bal, exact=True) > 0
+    wl2 = units_workload(n, seed=700 + units, H=4096, K=32, slices=3,
+                         dts=("bf16", "bf16", "bf16"))
+    dw2 = DeviceShrink(wl2)
+    multi = [to_host_bits(o) for o in dw2.run(multi=True)]
+    single = [to_host_bits(o) for o in dw2.run(multi=False)]
+    for a, b in zip(multi, single):
+        assert np.array_equal(a, b)
+    assert assert_shrink_parity(wl2, multi) > 0
+
+
 @pytest.mark.parametrize("extra", [1, 42, 128, 129])
 def test_shrink_balanced_integer_data_bit_exact_and_equal_without_workspace(extra):
     """On integer-valued data every fp32 partial sum is exact, so the

@@ -147,17 +147,22 @@ PART_PROBE = r"""
 #include <stdio.h>
 #include <stdlib.h>
 #include "sgmv_limits.h"
-// argv: U C G h_steps -> "max_parts E P counter_bytes workspace_bytes", then
-// one line "lo hi" per part
+// argv: U C G h_steps -> "max_parts W E P counter_bytes workspace_bytes",
+// then one line "lo hi" per part, then one line "bid unit part" per
+// workgroup bid >= W that runs a part
 int main(int argc, char** argv) {
   const unsigned U = atoi(argv[1]), C = atoi(argv[2]), G = atoi(argv[3]), h = atoi(argv[4]);
   const sgmv::limits::PartPlan pl = sgmv::limits::part_plan(U, C, G, h);
-  printf("%u %u %u %lld %lld\n", sgmv::limits::kShrinkMaxParts, pl.E, pl.P,
+  printf("%u %u %u %u %lld %lld\n", sgmv::limits::kShrinkMaxParts, pl.W, pl.E, pl.P,
          (long long)sgmv::limits::shrink_workspace_counter_bytes(C),
          (long long)sgmv::limits::shrink_workspace_bytes(C));
   for (unsigned r = 0; r < pl.P; ++r) {
     const sgmv::limits::StepSpan s = sgmv::limits::part_steps(r, pl.P, h);
-    printf("%d %d\n", s.lo, s.hi);
+    printf("S %d %d\n", s.lo, s.hi);
+  }
+  for (unsigned bid = pl.W; pl.P && bid < G; ++bid) {
+    const sgmv::limits::PartItem it = sgmv::limits::part_item(pl, bid);
+    if (it.valid) printf("I %u %u %u\n", bid, it.unit, it.part);
   }
   return 0;
 }
@@ -176,32 +181,48 @@ def parts(tmp_path_factory):
     def run(U, C, G, h):
         out = subprocess.run([str(exe), str(U), str(C), str(G), str(h)], check=True,
                              capture_output=True, text=True).stdout.split("\n")
-        kmax, E, P, cb, wb = (int(t) for t in out[0].split())
-        spans = [tuple(int(t) for t in line.split()) for line in out[1:] if line.strip()]
-        return kmax, E, P, cb, wb, spans
+        kmax, Wh, E, P, cb, wb = (int(t) for t in out[0].split())
+        spans = [tuple(int(t) for t in line.split()[1:]) for line in out[1:] if line[:1] == "S"]
+        items = [tuple(int(t) for t in line.split()[1:]) for line in out[1:] if line[:1] == "I"]
+        return kmax, Wh, E, P, cb, wb, spans, items
     return run
 
 
-# (units, compute units, grid, hidden steps): around C and 2 C units (the
-# named shrink batches have 298 and 319 units of 64 tokens on 256 compute
-# units), grids below 2 C, hidden sizes with fewer 4-step groups than parts
-PART_CASES = [(U, 256, G, h) for U in (0, 255, 256, 257, 298, 319, 320, 384, 385, 450, 512, 513)
-              for G in (256, 504, 512, 768) for h in (1, 3, 4, 7, 32, 128, 256)] + \
+# (units, compute units, grid, hidden steps): small batches (every unit in
+# parts up to C / 2 units), around C and 2 C units (the named shrink batches
+# have 298 and 319 units of 64 tokens on 256 compute units), grids too small
+# for the parts, hidden sizes with fewer 4-step groups than parts
+PART_CASES = [(U, 256, G, h) for U in (0, 1, 32, 64, 65, 85, 100, 128, 129, 255, 256, 257, 298,
+                                       319, 320, 384, 385, 450, 512, 513)
+              for G in (128, 256, 504, 512, 768) for h in (1, 3, 4, 7, 32, 128, 256)] + \
              [(100, 64, 128, 128), (304 + 30, 304, 608, 128), (20, 12, 24, 128)]
 
 
 @pytest.mark.parametrize("U,C,G,h", PART_CASES)
 def test_part_plan_and_step_spans(parts, U, C, G, h):
-    kmax, E, P, cb, wb, spans = parts(U, C, G, h)
+    kmax, Wh, E, P, cb, wb, spans, items = parts(U, C, G, h)
     n4 = (h + 3) // 4
-    qualifies = C >= 8 and C % 8 == 0 and C < U <= 2 * C and G >= 2 * C
-    want_p = min(C // (U - C), kmax, n4) if qualifies else 0
-    if want_p < 2:
-        assert (E, P) == (0, 0) and spans == []
+    ok = C >= 8 and C % 8 == 0 and 0 < U <= 2 * C
+    whole = C if U > C else 0
+    want_p = min(C // (U - whole), kmax, n4) if ok else 0
+    if want_p < 2 or G < whole + C:
+        assert (Wh, E, P) == (0, 0, 0) and spans == [] and items == []
     else:
-        assert (E, P) == (U - C, want_p)
-        # the parts fit the workgroups after the first C (grid >= 2 C)
-        assert E * P <= C and C + E * P <= G
+        # C < U <= 2 C: C whole units, the rest in parts; U <= C / 2: all in parts
+        assert (Wh, E, P) == (whole, U - whole, want_p)
+        assert U > C or 2 * U <= C
+        # every part of every overflow unit exactly once, on the C workgroups
+        # after the whole units (one per compute unit); in slot order
+        # ((unit - W) P + part) XCD x (bid % 8) holds the x-th contiguous
+        # eighth of the parts, taken in order of (bid - W) / 8
+        assert sorted((u, r) for _, u, r in items) == \
+            [(u, r) for u in range(Wh, Wh + E) for r in range(P)]
+        assert all(Wh <= b < Wh + C for b, _, _ in items)
+        I = E * P
+        share, extra = I // 8, I % 8
+        for b, u, r in items:
+            x, j = (b - Wh) % 8, (b - Wh) // 8
+            assert (u - Wh) * P + r == x * share + min(x, extra) + j
         # spans: contiguous, non-empty, on multiples of 4 steps, covering
         # every hidden step; they depend on (P, h) only
         assert spans[0][0] == 0
