@@ -48,6 +48,16 @@ int next_pow2(int v) {
 #ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS
 #define SGMV_SHRINK_SPLIT_T_MIN_UNITS 64
 #endif
+// With a workspace the split-T kernel cuts the units of small batches into
+// hidden parts (limits::part_plan), and for ranks above 64 it then beats
+// split-H from this many units (measured, 16-63 units of 64 tokens, hidden
+// 4096-8192: rank 128 42 -> 25-36 us, rank 256 73 -> 26-34 us; ranks of 64
+// and below gain little or lose, so they keep the threshold above).  The
+// choice depends on the rank and the batch only, never on the slice count,
+// so a multi-slice call and its single calls take the same kernel form.
+#ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS_WIDE
+#define SGMV_SHRINK_SPLIT_T_MIN_UNITS_WIDE 16
+#endif
 
 // One launch over slices [first, first + count) of `slices` (already checked).
 sgmv_status shrink_launch(const sgmv_matrix& x, const sgmv_shrink_slice* slices, int first,
@@ -287,8 +297,9 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
   // reads the inputs again).
   int fast_per_launch = 16 / k16;
   if (fast_per_launch > kShrinkMaxSlicesPerLaunch) fast_per_launch = kShrinkMaxSlicesPerLaunch;
-  const bool split_t =
-      (x.rows + kShrinkTokensSplitT - 1) / kShrinkTokensSplitT >= SGMV_SHRINK_SPLIT_T_MIN_UNITS;
+  const int64_t units64 = (x.rows + kShrinkTokensSplitT - 1) / kShrinkTokensSplitT;
+  const bool split_t = units64 >= SGMV_SHRINK_SPLIT_T_MIN_UNITS ||
+                       (workspace && k16 >= 8 && units64 >= SGMV_SHRINK_SPLIT_T_MIN_UNITS_WIDE);
   if (clear_counters && workspace) {
     const sgmv_status st = clear_workspace_counters(workspace, stream);
     if (st != SGMV_OK) return st;

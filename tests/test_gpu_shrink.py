@@ -327,6 +327,26 @@ def test_shrink_balanced_small_batches_integer_and_multi_slice(units):
     assert assert_shrink_parity(wl2, multi) > 0
 
 
+@pytest.mark.parametrize("units,K,H", [(16, 128, 8192), (40, 256, 4096), (63, 72, 2048)])
+def test_shrink_wide_ranks_take_split_t_from_16_units_with_a_workspace(units, K, H):
+    """Ranks above 64 take the balanced split-T kernel from 16 units of 64
+    tokens when a workspace comes with the call (split-H without one): both
+    match the oracle, and on integer data they agree bit for bit."""
+    C = compute_units()
+    n = max(16, units * C // 256)
+    wl = units_workload(n, seed=800 + K, H=H, K=K, slices=1, dts=("f16", "f16", "f16"))
+    assert run_and_check(wl) > 0
+    assert run_and_check(wl, workspace=None) > 0
+    wi = units_workload(n, seed=900 + K, values="int", H=H, K=K, slices=1,
+                        dts=("bf16", "bf16", "f32"))
+    dw = DeviceShrink(wi)
+    bal = [to_host_bits(o) for o in dw.run(workspace=True)]
+    plain = [to_host_bits(o) for o in dw.run(workspace=None)]
+    for a, b in zip(bal, plain):
+        assert np.array_equal(a, b)
+    assert assert_shrink_parity(wi, bal, exact=True) > 0
+
+
 @pytest.mark.parametrize("extra", [1, 42, 128, 129])
 def test_shrink_balanced_integer_data_bit_exact_and_equal_without_workspace(extra):
     """On integer-valued data every fp32 partial sum is exact, so the
