@@ -167,7 +167,26 @@ def shrink_abs_dot(wl, si, rows, ra):
     return out
 
 
-def assert_shrink_parity(wl, cand_bits, rows=None, idx=None, exact=False):
+def shrink_sum_depth(wl):
+    """The most fp32 roundings an exact 16-bit product can pass through on
+    its way into a result of the kernel the library picks for this shrink
+    workload.  The register-tiled (MFMA) kernels -- taken, as at the ABI,
+    when rank and hidden are multiples of 8, every row stride is a multiple
+    of 16 bytes and one adapter's lora_A rows span less than 2 GiB (the test
+    buffers are 16-byte aligned) -- add a product into at most 32 others
+    inside one 32-wide MFMA step, then once per later step (ceil(H / 32)),
+    then at most 3 times where the split-H waves or the balanced split-T
+    parts are added (8 allowed): 32 + ceil(H / 32) + 8.  The generic kernel
+    accumulates the H products one after the other: H."""
+    x_ok = wl.x.strides[0] % 16 == 0 and all(o.strides[0] % 16 == 0 for o in wl.outs0)
+    p = 1
+    while p < (wl.K + 15) // 16:
+        p *= 2
+    fast = (wl.K % 8 == 0 and wl.H % 8 == 0 and x_ok and 32 * p * wl.H < 2 ** 31)
+    return min(wl.H, 32 + -(-wl.H // 32) + 8) if fast else wl.H
+
+
+def assert_shrink_parity(wl, cand_bits, rows=None, idx=None, exact=False, depth=None):
     """GPU outputs (one bits array per slice) vs the oracle: every computed
     value of an active row within tolerance of the exact value (non-finite
     exactly where the rounded exact value is), every other row bit-identical
@@ -177,12 +196,16 @@ def assert_shrink_parity(wl, cand_bits, rows=None, idx=None, exact=False):
 
     Tolerance: the output dtype's atol + rtol * |ref| (which covers the final
     rounding and the scale's rounding), plus the bound on fp32 summation of
-    the H exact 16-bit products in any order, gamma_H * |scale| * sum_h
-    |x_h a_h| with gamma_H = H u / (1 - H u), u = 2^-24 (the recursive
-    summation bound, which holds for every order and tree of additions).
+    the H exact 16-bit products, gamma_d * |scale| * sum_h |x_h a_h| with
+    gamma_d = d u / (1 - d u), u = 2^-24 and d the most roundings any
+    product passes through (shrink_sum_depth: 32 + ceil(H / 32) + 8 on the
+    MFMA kernels, H on the generic one; the recursive summation bound, which
+    holds for every order and grouping within that depth; ``depth`` overrides
+    it for buffers other than the workload's own).
     Returns the number of values checked."""
     atol, rtol = TOLERANCE[wl.out_dtype]
-    gamma = wl.H * U_FP32 / (1.0 - wl.H * U_FP32)
+    depth = shrink_sum_depth(wl) if depth is None else depth
+    gamma = depth * U_FP32 / (1.0 - depth * U_FP32)
     idx = wl.idx if idx is None else idx
     outs = [o.copy() for o in wl.outs0]
     refs = oracle.shrink(wl.x, wl.x_dtype, wl.lora_a, wl.a_dtype, outs, wl.out_dtype, wl.start,

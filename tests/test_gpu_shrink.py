@@ -238,7 +238,8 @@ def test_shrink_multi_slice_with_a_misaligned_output_equals_single_calls():
         sg.sgmv_shrink(dw.x, dw.a[i], alone, dw.start, dw.lens, dw.idx, wl.batches,
                        wl.max_seq_len, wl.scale)
         assert np.array_equal(to_host_bits(outs[i]), to_host_bits(alone)), i
-    assert assert_shrink_parity(wl, [to_host_bits(o) for o in outs]) > 0
+    # slice 1 ran on the generic kernel: its summation depth is the hidden size
+    assert assert_shrink_parity(wl, [to_host_bits(o) for o in outs], depth=wl.H) > 0
 
 
 @pytest.mark.parametrize("units", [255, 256, 257])

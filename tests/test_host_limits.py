@@ -235,3 +235,28 @@ def test_part_plan_and_step_spans(parts, U, C, G, h):
     # then one 64 KiB slot per possible part
     assert cb % 256 == 0 and 4 * C <= cb < 4 * C + 256
     assert wb == cb + C * 64 * 256 * 4
+
+
+def test_shrink_sum_depth_follows_the_kernel_choice():
+    """The GPU tests' shrink tolerance uses the most fp32 roundings a product
+    passes through: 32 + ceil(H / 32) + 8 where the MFMA kernels run (rank and
+    hidden multiples of 8, 16-byte row strides, lora_A span below 2 GiB), the
+    hidden size where the generic kernel runs."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    import sgmv_workloads as W
+    from gpu_util import shrink_sum_depth
+    assert shrink_sum_depth(W.SHRINK_WORKLOADS["shrink_gate_up"](0)) == 32 + 128 + 8
+    assert shrink_sum_depth(W.SHRINK_WORKLOADS["shrink_skewed"](0)) == 32 + 256 + 8
+    lens, idx = [10, 20], [0, 1]
+    assert shrink_sum_depth(W.shrink_custom(lens, idx, H=1000, K=24, L=2, seed=1)) == 32 + 32 + 8
+    # generic: hidden not a multiple of 8, rank not a multiple of 8, a padded row
+    # stride that is not a multiple of 16 bytes; a float32 output padded by 4
+    # columns keeps 16-byte rows
+    assert shrink_sum_depth(W.shrink_custom(lens, idx, H=1001, K=24, L=2, seed=1)) == 1001
+    assert shrink_sum_depth(W.shrink_custom(lens, idx, H=256, K=7, L=2, seed=1)) == 256
+    assert shrink_sum_depth(W.shrink_custom(lens, idx, H=1000, K=24, L=2, x_pad=3, seed=1)) == 1000
+    assert shrink_sum_depth(W.shrink_custom(lens, idx, H=1000, K=24, L=2, out_dtype="f32",
+                                            out_pad=4, seed=1)) == 72
+    # tiny hidden sizes: never more than H
+    assert shrink_sum_depth(W.shrink_custom(lens, idx, H=8, K=8, L=2, seed=1)) == 8
