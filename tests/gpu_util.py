@@ -315,11 +315,14 @@ def assert_fused_parity(wl, cand_bits, exact=False):
 
         atol + rtol |R| + sum_k delta_k |B[a][n][k]|,
         delta_k = ulp_w(2 (|y_k| + e_k)) + e_k,
-        e_k = |scale| (gamma_H + 2^-23) sum_h |x_h A[a][k][h]|,
+        e_k = |scale| (gamma_d + 2^-23) sum_h |x_h A[a][k][h]|,
 
     of the exact expand R of the oracle's projection y: the GPU's fp32
     projection differs from the exact one by at most e_k (summation of H
-    exact products in any order, then the scale's rounding), so its
+    exact products in any order and grouping in which no product meets more
+    than d = 32 + ceil(H / 32) + 8 roundings -- the fused kernel runs the
+    split-T MFMA contraction, see shrink_sum_depth -- then the scale's
+    rounding), so its
     rounding to the weight dtype can land at most delta_k from the oracle's;
     atol and rtol cover the expand's own fp32 sums and final rounding.
     Returns the number of values compared."""
@@ -339,7 +342,8 @@ def assert_fused_parity(wl, cand_bits, exact=False):
         assert np.array_equal(bits, ob), f"{wl.name}: bits differ from the oracle"
         return int(rows.sum() * cols.sum())
     atol, rtol = TOLERANCE[wl.out_dtype]
-    gamma = wl.H * U_FP32 / (1.0 - wl.H * U_FP32) + 2.0 ** -23
+    depth = min(wl.H, 32 + -(-wl.H // 32) + 8)
+    gamma = depth * U_FP32 / (1.0 - depth * U_FP32) + 2.0 ** -23
     x = np.abs(np_cast_input(np.ascontiguousarray(wl.x), wl.x_dtype, wl.w_dtype))
     ra = np.full(wl.T, -1, dtype=np.int64)
     for s, n, a in zip(wl.start, wl.lens, wl.idx):
