@@ -364,6 +364,28 @@ def test_shrink_balanced_integer_data_bit_exact_and_equal_without_workspace(extr
     assert assert_shrink_parity(wl, bal, exact=True) > 0
 
 
+@pytest.mark.parametrize("units,K,slices", [(None, 64, 2), (64, 32, 3), (16, 128, 1)])
+def test_shrink_balanced_float32_inputs(units, K, slices):
+    """float32 inputs (rounded to the weight dtype on the way into LDS) on
+    the balanced paths: C + 42 units (parts beside whole units), 64 units
+    (every unit in parts) and 16 units of rank 128 (split-T below 64 units),
+    against the oracle, and on integer data bit for bit equal to the call
+    without a workspace."""
+    C = compute_units()
+    n = C + 42 if units is None else max(16, units * C // 256)
+    wl = units_workload(n, seed=1000 + n + K, H=2048, K=K, slices=slices,
+                        dts=("f32", "bf16", "f32"))
+    assert run_and_check(wl) > 0
+    wi = units_workload(n, seed=1100 + n + K, values="int", H=2048, K=K, slices=slices,
+                        dts=("f32", "f16", "f32"))
+    dw = DeviceShrink(wi)
+    bal = [to_host_bits(o) for o in dw.run(workspace=True)]
+    plain = [to_host_bits(o) for o in dw.run(workspace=None)]
+    for a, b in zip(bal, plain):
+        assert np.array_equal(a, b)
+    assert assert_shrink_parity(wi, bal, exact=True) > 0
+
+
 def test_shrink_balanced_multi_slice_equals_single_calls():
     """Part boundaries depend only on the hidden size and the part count, so
     a three-slice call (one launch of 6 k tiles) equals three single calls
