@@ -630,6 +630,7 @@ def run_shrink(args):
             "rotated_buffer_sets": nsets,
             "call": (f"{len(wl.lora_a)} x sgmv_shrink" if split else
                      "sgmv_shrink_multi_slice"),
+            "workspace": "the binding's shared per-device buffer (balanced split-T batches)",
             "launch": mode,
             "timed_replays_us_per_step": None if replays is None else [round(r * 1e3, 3) for r in replays],
             "untimed_spin_up": None if replays is None else getattr(time_steps_graph, "spin_up", None),
@@ -858,6 +859,8 @@ def run_fused(args):
             "rotated_buffer_sets": nsets,
             "call": ("sgmv_shrink_multi_slice + sgmv_expand_multi_slice" if args.unfused else
                      "sgmv_fused_shrink_expand"),
+            "workspace": ("the shrink's: the binding's shared per-device buffer" if args.unfused
+                          else None),
             "launch": mode,
             "timed_replays_us_per_step": None if replays is None else [round(r * 1e3, 3) for r in replays],
             "untimed_spin_up": None if replays is None else getattr(time_steps_graph, "spin_up", None),
