@@ -386,6 +386,37 @@ def test_shrink_balanced_float32_inputs(units, K, slices):
     assert assert_shrink_parity(wi, bal, exact=True) > 0
 
 
+@pytest.mark.parametrize("target,seed", [(300, 1), (80, 2)])
+def test_shrink_balanced_ragged_segments(target, seed):
+    """Balanced batches built from ragged segments (1..200 tokens, so many
+    units hold fewer than 64 rows), index -1 and empty segments among them:
+    about `target` units on a 256-unit device (C + 44: parts beside whole
+    units; 80: every unit in parts).  Every row is compared with the oracle
+    and rows without an adapter keep their bits."""
+    C = compute_units()
+    rng = np.random.default_rng(seed)
+    want = target * C // 256
+    lens, idx, units = [], [], 0
+    while units < want:
+        n = int(rng.integers(0, 201))
+        a = -1 if rng.random() < 0.12 else int(rng.integers(0, 9))
+        lens.append(n)
+        idx.append(a)
+        if a >= 0:
+            units += -(-n // 64)
+    wl = W.shrink_custom(lens, idx, H=2048, K=48, L=9, slices=2, x_dtype="bf16",
+                         a_dtype="bf16", out_dtype="f32", seed=1200 + seed)
+    assert run_and_check(wl) > 0
+    wi = W.shrink_custom(lens, idx, H=2048, K=48, L=9, slices=2, x_dtype="f16", a_dtype="f16",
+                         out_dtype="f16", values="int", seed=1300 + seed)
+    dw = DeviceShrink(wi)
+    bal = [to_host_bits(o) for o in dw.run(workspace=True)]
+    plain = [to_host_bits(o) for o in dw.run(workspace=None)]
+    for a, b in zip(bal, plain):
+        assert np.array_equal(a, b)
+    assert assert_shrink_parity(wi, bal, exact=True) > 0
+
+
 def test_shrink_balanced_multi_slice_equals_single_calls():
     """Part boundaries depend only on the hidden size and the part count, so
     a three-slice call (one launch of 6 k tiles) equals three single calls
