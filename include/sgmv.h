@@ -295,13 +295,16 @@ typedef struct {
  *
  * with rne_w the nearest-even rounding to the weights' 16-bit dtype -- the
  * result of sgmv_shrink_multi_slice into outputs of the weights' dtype
- * followed by sgmv_expand_multi_slice on those outputs (bit for bit equal
- * to them when the shrink takes its large-batch form, i.e. from 64 units of
- * 64 tokens, and runs without a workspace: with one, its parts round
- * differently); sums in fp32, each result rounded once (nearest even) to the
- * output dtype; float32 inputs rounded to the weight dtype first.  Rows of
- * index -1 segments, rows outside every segment and columns outside the
- * windows are left untouched.
+ * followed by sgmv_expand_multi_slice on those outputs, bit for bit equal
+ * to them when the shrink runs without a workspace (with one, its parts
+ * round differently); sums in fp32, each result rounded once (nearest
+ * even) to the output dtype; float32 inputs rounded to the weight dtype
+ * first.  Rows of index -1 segments, rows outside every segment and
+ * columns outside the windows are left untouched.  The call takes the
+ * shrink's two forms by the shrink's rule: from 64 units of 64 tokens,
+ * 64-row units that each expand over every column; below (short prefill
+ * and decode batches), 16-row units, each expanded in column groups over
+ * about one work item per compute unit.
  *
  * inputs        device (total_tokens, hidden) f16/bf16/f32; read only.
  * slices        host array of 1..SGMV_MAX_FUSED_SLICES descriptors, read

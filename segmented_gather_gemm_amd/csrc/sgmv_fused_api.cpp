@@ -22,13 +22,13 @@ using namespace sgmv::host;
 using sgmv::limits::next_pow2;
 using sgmv::limits::shrink_fast_lora_a_fits;
 
-const void* pick_fused_kernel(int xd, int wd, int od, bool add, int k16, int ns) {
+const void* pick_fused_kernel(int xd, int wd, int od, bool add, int k16, int ns, bool split_h) {
   using namespace sgmv;
   switch (k16) {
-    case 1: return fused_kernel_k1(xd, wd, od, add, ns);
-    case 2: return fused_kernel_k2(xd, wd, od, add, ns);
-    case 4: return fused_kernel_k4(xd, wd, od, add, ns);
-    case 8: return fused_kernel_k8(xd, wd, od, add, ns);
+    case 1: return fused_kernel_k1(xd, wd, od, add, ns, split_h);
+    case 2: return fused_kernel_k2(xd, wd, od, add, ns, split_h);
+    case 4: return fused_kernel_k4(xd, wd, od, add, ns, split_h);
+    case 8: return fused_kernel_k8(xd, wd, od, add, ns, split_h);
     default: return nullptr;
   }
 }
@@ -174,15 +174,29 @@ sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice*
     d.tile_begin = tile_begin;
     tile_begin += (int32_t)((s.lora_b.rows + kTileCols - 1) / kTileCols);
   }
-  const void* kernel =
-      pick_fused_kernel(x.dtype, s0.lora_a.dtype, out.dtype, add_inputs != 0, (int)k16, num_slices);
+  // The projection's form follows the workspace-free shrink's rule (so the
+  // result equals that shrink followed by the expand, bit for bit):
+  // split-T from SGMV_SHRINK_SPLIT_T_MIN_UNITS units of 64 tokens, split-H
+  // below.
+  const bool split_h = (x.rows + kFusedTokens - 1) / kFusedTokens < SGMV_SHRINK_SPLIT_T_MIN_UNITS;
+  const void* kernel = pick_fused_kernel(x.dtype, s0.lora_a.dtype, out.dtype, add_inputs != 0,
+                                         (int)k16, num_slices, split_h);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no fused kernel for this dtype combination");
-  // every wave runs all hidden steps; loop positions in whole turns of the
-  // ring of blocks (as the split-T shrink)
   const int64_t steps = (H + 31) / 32;
-  const int64_t turn = shrink_ring(shrink_block_loads_t(x.dtype, (int)k16, num_slices)) *
-                       shrink_block_steps_t((int)k16 * num_slices);
-  p.steps = (int32_t)((steps + turn - 1) / turn * turn);
+  if (split_h) {
+    // each wave takes a quarter of the hidden steps; loop positions in whole
+    // turns of the ring (as the split-H shrink)
+    const int64_t per_wave = (steps + kWaves - 1) / kWaves;
+    const int64_t turn = shrink_ring(shrink_block_loads_h(x.dtype, (int)k16 * num_slices)) *
+                         shrink_block_steps_h(x.dtype, (int)k16 * num_slices);
+    p.steps = (int32_t)((per_wave + turn - 1) / turn * turn);
+  } else {
+    // every wave runs all hidden steps; loop positions in whole turns of the
+    // ring of blocks (as the split-T shrink)
+    const int64_t turn = shrink_ring(shrink_block_loads_t(x.dtype, (int)k16, num_slices)) *
+                         shrink_block_steps_t((int)k16 * num_slices);
+    p.steps = (int32_t)((steps + turn - 1) / turn * turn);
+  }
 
   const size_t lds = (size_t)(4 * batches + 1) * sizeof(int32_t);
   int capacity = 0, cus = 0;
@@ -194,11 +208,21 @@ sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice*
                 "%lld segments: the fused kernel's segment table and staging buffers exceed a "
                 "compute unit's LDS; run sgmv_shrink_multi_slice and sgmv_expand_multi_slice "
                 "instead", (long long)batches);
-  // Units are 64-row tiles of active segments: at most ceil(T / 64) +
-  // min(batches, T).  One per workgroup while they fit on the chip.
-  const int64_t units =
-      (x.rows + kFusedTokens - 1) / kFusedTokens + (batches < x.rows ? batches : x.rows);
-  int64_t grid = units < capacity ? units : capacity;
+  // Units are tiles of active segments: at most ceil(T / rows) + min(batches,
+  // T).  Split-T: one per workgroup while they fit on the chip.  Split-H:
+  // work items (a unit and a column group) up to about one per compute unit
+  // (the device sizes the groups from the actual unit count).
+  const int64_t rows = split_h ? kTileRows : kFusedTokens;
+  const int64_t units = (x.rows + rows - 1) / rows + (batches < x.rows ? batches : x.rows);
+  int64_t want = units;
+  if (split_h) {
+    // one item per compute unit (measured on fused_q_proj / fused_decode_qkv:
+    // two per compute unit double the projections a compute unit runs and
+    // lose 20-25%; one column group per unit loses 30% on fused_q_proj)
+    p.item_target = cus;
+    if (want < p.item_target) want = p.item_target;
+  }
+  int64_t grid = want < capacity ? want : capacity;
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;

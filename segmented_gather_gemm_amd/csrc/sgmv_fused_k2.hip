@@ -5,8 +5,8 @@
 
 namespace sgmv {
 
-const void* fused_kernel_k2(int xd, int wd, int od, bool add, int ns) {
-  return dev::fused_table<2>(xd, wd, od, add, ns);
+const void* fused_kernel_k2(int xd, int wd, int od, bool add, int ns, bool split_h) {
+  return dev::fused_table<2>(xd, wd, od, add, ns, split_h);
 }
 
 }  // namespace sgmv

@@ -49,6 +49,8 @@ struct FusedParams {
   int32_t gather;         // always 0
   float scale;
   int32_t total_tiles;    // 256-column tiles over all slices
+  int32_t item_target;    // split-H form: work items to aim for; a unit of U gets
+                          // max(1, min(total_tiles, item_target / U)) column groups
   void* out;              // (T, H_out), row stride out_row_bytes
   int64_t out_row_bytes;
   FusedSliceDesc s[kFusedMaxSlices];
@@ -56,12 +58,15 @@ struct FusedParams {
 
 // Fused kernels by dtype codes (inputs, weights, output), accumulate flag
 // and (k16, ns): k16 = 16-row k tiles per slice (1, 2, 4, 8), ns = slices
-// (1..3), k16 * ns <= 16; nullptr if there is none.  They need K % 8 == 0,
+// (1..3), k16 * ns <= 16; nullptr if there is none.  Two forms: split_h
+// (small batches: 16-row units, each in column groups sized from
+// p.item_target; the split-H shrink's contraction) or split-T (64-row units; the split-T
+// shrink's contraction).  They need K % 8 == 0,
 // H % 8 == 0, slice widths % 8 == 0 and 16-byte aligned rows, weight stacks
 // and output column windows.
-const void* fused_kernel_k1(int xd, int wd, int od, bool add, int ns);
-const void* fused_kernel_k2(int xd, int wd, int od, bool add, int ns);
-const void* fused_kernel_k4(int xd, int wd, int od, bool add, int ns);
-const void* fused_kernel_k8(int xd, int wd, int od, bool add, int ns);
+const void* fused_kernel_k1(int xd, int wd, int od, bool add, int ns, bool split_h);
+const void* fused_kernel_k2(int xd, int wd, int od, bool add, int ns, bool split_h);
+const void* fused_kernel_k4(int xd, int wd, int od, bool add, int ns, bool split_h);
+const void* fused_kernel_k8(int xd, int wd, int od, bool add, int ns, bool split_h);
 
 }  // namespace sgmv

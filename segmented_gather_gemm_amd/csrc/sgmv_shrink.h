@@ -160,16 +160,25 @@ struct SplitHBlock {
   u32x4 a[Sh::kBlockH][Sh::kTiles];
 };
 
-template <int XD, int WD, int OD, int K16, int NS>
-__global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p) {
+// The split-H contraction of one 16-token unit, shared by the shrink kernel
+// and the fused shrink-expand kernel for small batches: `run` leaves in
+// acc[i] this wave's fp32 partial sums over its quarter of the hidden steps
+// (k tile i of the launch is tile i % K16 of slice i / K16); `reduce` adds
+// the four waves' partial sums through LDS in wave order and hands each
+// finished fragment to emit(i, v), lane (j, g) holding k = 16 (i % K16) +
+// 4 g .. + 3 of token j.  The LDS buffers are the caller's (declared in the
+// kernel).  P: a parameter block with the ShrinkParams fields x_row_bytes,
+// H and s[].a.
+template <int XD, int WD, int K16, int NS>
+struct SplitHCore {
   using Sh = ShrinkShape<XD, K16, NS>;
   using Block = SplitHBlock<XD, K16, NS>;
-  constexpr int kW = kWaves;
-  constexpr int kT = Sh::kTiles;
-  constexpr int kB = Sh::kBlockH;
+  static constexpr int kW = kWaves;
+  static constexpr int kT = Sh::kTiles;
+  static constexpr int kB = Sh::kBlockH;
   // fragments added per LDS round: kW x kRound fragments of 1 KiB <= 32 KiB
-  constexpr int kRound = kT < 32 / kW ? kT : 32 / kW;
-  constexpr int xb = XD == F32 ? 4 : 2;
+  static constexpr int kRound = kT < 32 / kW ? kT : 32 / kW;
+  static constexpr int xb = XD == F32 ? 4 : 2;
   // Coalesced loads (up to 8 k tiles): load i of a block reads rows
   // i kRPI .. + kRPI - 1 of a 16-row tile, kLPR lanes per row covering the
   // block's kB steps contiguously (lane l: row l / kLPR, hidden block
@@ -177,52 +186,63 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
   // scatters them into MFMA operand order in its own LDS region (see
   // frag_slot) and reads the operands back.  More k tiles load operands
   // directly (16 rows x 64 bytes per load), which needs no LDS.
-  constexpr bool kCoal = kT <= 8;
-  constexpr int kLPR = 4 * kB;
-  constexpr int kRPI = 64 / kLPR;
+  static constexpr bool kCoal = kT <= 8;
+  static constexpr int kLPR = 4 * kB;
+  static constexpr int kRPI = 64 / kLPR;
   static_assert(!kCoal || (kB % 2 == 0 && kRPI * kB == 16), "coalesced block shape");
-  prefetch_params(p);
-  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
-  __shared__ int32_t wave_total[kW];
-  __shared__ f32x4 red[kW][kRound][64];
+  typedef f32x4 RedLds[kW][kRound][64];
   // per wave: the block's input fragments (steps 0 .. kB - 1), then each k
   // tile's ([tile + 1] kB + step)
-  __shared__ u32x4 stage[kCoal ? kW : 1][kCoal ? (kT + 1) * kB : 1][kCoal ? kFragSlots : 1];
-  const SegTable tab = seg_table(lds, p.batches);
-  const int32_t U = build_tile_table(p, tab, wave_total, kTileRows);
-  if (U == 0) return;
-  uint32_t u, u_end;
-  unit_range(p, (uint32_t)U, &u, &u_end);
-  if (u >= u_end) return;
+  typedef u32x4 StageLds[kCoal ? kW : 1][kCoal ? (kT + 1) * kB : 1][kCoal ? kFragSlots : 1];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int g = lane >> 4;  // lane group: hidden block 8 g of a step / k rows 4 g.. of a tile
-  const int j = lane & 15;  // token of the tile / lora_A row of a k tile
-  const int32_t H = p.H;
-  const uint32_t xrb = (uint32_t)p.x_row_bytes;  // 16 rows span < 2 GiB (host)
-  // The wave's hidden steps: [wave q, wave q + q) with q = ceil(steps / kW),
-  // run over p.steps >= q loop positions (the rest read nothing).
-  const int32_t q_steps = (((H + 31) >> 5) + kW - 1) / kW;
-  const int32_t s_beg = wave * q_steps;
-  // direct operand loads: row j, hidden block 8 g
-  const uint32_t x_lane = (uint32_t)j * xrb + (uint32_t)(8 * g * xb);
+  RedLds& red;
+  StageLds& stage;
+  int lane, wave, g, j, cr, cb, cst, cg, r_slot;
+  int32_t H, q_steps, s_beg;
+  uint32_t xrb, x_lane, xc_lane, ac_lane;
   uint32_t a_lane[K16];  // row 16 kt + j of a slice's lora_A[a], hidden block 8 g
+
+  template <typename P>
+  __device__ __forceinline__ SplitHCore(const P& p, RedLds& r, StageLds& s) : red(r), stage(s) {
+    lane = threadIdx.x & 63;
+    wave = uniform(threadIdx.x >> 6);
+    g = lane >> 4;  // lane group: hidden block 8 g of a step / k rows 4 g.. of a tile
+    j = lane & 15;  // token of the tile / lora_A row of a k tile
+    H = p.H;
+    xrb = (uint32_t)p.x_row_bytes;  // 16 rows span < 2 GiB (host)
+    // The wave's hidden steps: [wave q, wave q + q) with q = ceil(steps / kW),
+    // run over p.steps >= q loop positions (the rest read nothing).
+    q_steps = (((H + 31) >> 5) + kW - 1) / kW;
+    s_beg = wave * q_steps;
+    // direct operand loads: row j, hidden block 8 g
+    x_lane = (uint32_t)j * xrb + (uint32_t)(8 * g * xb);
 #pragma unroll
-  for (int kt = 0; kt < K16; ++kt)
-    a_lane[kt] = (uint32_t)(16 * kt + j) * (uint32_t)H * 2u + (uint32_t)(16 * g);
-  // coalesced loads: row cr of the load, hidden block cb of the block's span
-  const int cr = lane / kLPR, cb = lane % kLPR;
-  const int cst = cb >> 2, cg = cb & 3;  // its step within the block and block in the step
-  const uint32_t xc_lane = (uint32_t)cr * xrb + (uint32_t)(8 * cb * xb);
-  const uint32_t ac_lane = (uint32_t)cr * (uint32_t)H * 2u + (uint32_t)(16 * cb);
-  const int r_slot = frag_slot(j, g);
+    for (int kt = 0; kt < K16; ++kt)
+      a_lane[kt] = (uint32_t)(16 * kt + j) * (uint32_t)H * 2u + (uint32_t)(16 * g);
+    // coalesced loads: row cr of the load, hidden block cb of the block's span
+    cr = lane / kLPR;
+    cb = lane % kLPR;
+    cst = cb >> 2;  // its step within the block and block in the step
+    cg = cb & 3;
+    xc_lane = (uint32_t)cr * xrb + (uint32_t)(8 * cb * xb);
+    ac_lane = (uint32_t)cr * (uint32_t)H * 2u + (uint32_t)(16 * cb);
+    r_slot = frag_slot(j, g);
+  }
 
-  int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
-  for (; u < u_end; ++u) {
-    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
-    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kTileRows);
-
+  // The wave's partial sums of unit su over its hidden steps; `steps` loop
+  // positions (a multiple of the ring's turn).
+  __device__ __forceinline__ void run(const ShrinkUnit<NS>& su, f32x4 (&acc)[kT], int32_t steps) {
+    // the lane constants as locals of the loop (members captured through
+    // `this` cost registers in the ring loop)
+    const int32_t H = this->H, q_steps = this->q_steps, s_beg = this->s_beg;
+    const uint32_t xrb = this->xrb, x_lane = this->x_lane, xc_lane = this->xc_lane,
+                   ac_lane = this->ac_lane;
+    const int wave = this->wave, g = this->g, cr = this->cr, cst = this->cst, cg = this->cg,
+              r_slot = this->r_slot;
+    uint32_t a_lane[K16];
+#pragma unroll
+    for (int kt = 0; kt < K16; ++kt) a_lane[kt] = this->a_lane[kt];
+    StageLds& stage = this->stage;
     auto load_block = [&](Block& blk, int32_t v0) __attribute__((always_inline)) {
       if constexpr (kCoal) {
         const int32_t v = v0 + cst;  // this lane's step
@@ -258,7 +278,6 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
         }
       }
     };
-    f32x4 acc[kT];
 #pragma unroll
     for (int i = 0; i < kT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute_block = [&](const Block& blk) __attribute__((always_inline)) {
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
       }
     };
 
-    // Loop positions [0, p.steps) (a multiple of kD kB): a ring of kD blocks
+    // Loop positions [0, steps) (a multiple of kD kB): a ring of kD blocks
     // in registers, block n + kD - 1 issued before block n computes.
     // Scheduling barriers keep each block's loads in issue order, which the
     // in-order vmcnt wait relies on.
@@ -301,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
       load_block(ring[d], d * kB);
       __builtin_amdgcn_sched_barrier(0);
     }
-    for (int32_t s = 0; s < p.steps; s += kD * kB) {
+    for (int32_t s = 0; s < steps; s += kD * kB) {
 #pragma unroll
       for (int d = 0; d < kD; ++d) {
         load_block(ring[(d + kD - 1) % kD], s + (d + kD - 1) * kB);
@@ -310,11 +329,14 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
 
-    // Add the waves' partial sums through LDS, kRound fragments at a time;
-    // wave w finishes fragments w, w + kW, ... of the round.  The first
-    // barrier of a round also orders the previous round's (or unit's) reads
-    // before the writes.
+  // Add the waves' partial sums through LDS, kRound fragments at a time;
+  // wave w finishes fragments w, w + kW, ... of the round.  The first
+  // barrier of a round also orders the previous round's (or unit's) reads
+  // before the writes.
+  template <typename Emit>
+  __device__ __forceinline__ void reduce(const f32x4 (&acc)[kT], Emit&& emit) {
 #pragma unroll
     for (int f0 = 0; f0 < kT; f0 += kRound) {
       __syncthreads();
@@ -328,9 +350,37 @@ __global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p)
         f32x4 v = red[0][q][lane];
 #pragma unroll
         for (int w = 1; w < kW; ++w) v += red[w][q][lane];
-        shrink_store<OD, K16>(p, f0 + q, su.row0, su.rows, 0, j, g, v);
+        emit(f0 + q, v);
       }
     }
+  }
+};
+
+template <int XD, int WD, int OD, int K16, int NS>
+__global__ __launch_bounds__(kThreads) void shrink_split_h(const ShrinkParams p) {
+  using Core = SplitHCore<XD, WD, K16, NS>;
+  prefetch_params(p);
+  extern __shared__ __align__(16) int32_t lds[];  // segment table, 4 * batches + 1 words
+  __shared__ int32_t wave_total[kWaves];
+  __shared__ typename Core::RedLds red;
+  __shared__ typename Core::StageLds stage;
+  const SegTable tab = seg_table(lds, p.batches);
+  const int32_t U = build_tile_table(p, tab, wave_total, kTileRows);
+  if (U == 0) return;
+  uint32_t u, u_end;
+  unit_range(p, (uint32_t)U, &u, &u_end);
+  if (u >= u_end) return;
+
+  Core core(p, red, stage);
+  int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)u);
+  for (; u < u_end; ++u) {
+    while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
+    const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kTileRows);
+    f32x4 acc[Core::kT];
+    core.run(su, acc, p.steps);
+    core.reduce(acc, [&](int i, f32x4 v) __attribute__((always_inline)) {
+      shrink_store<OD, K16>(p, i, su.row0, su.rows, 0, core.j, core.g, v);
+    });
   }
 }
 

@@ -42,12 +42,6 @@ int next_pow2(int v) {
   return p;
 }
 
-// Split-T (64-token units, lora_A shared through LDS) once the batch has at
-// least this many 64-token units; split-H (16-token units) below, where it
-// keeps more compute units busy.
-#ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS
-#define SGMV_SHRINK_SPLIT_T_MIN_UNITS 64
-#endif
 // With a workspace the split-T kernel cuts the units of small batches into
 // hidden parts (limits::part_plan), and for ranks above 64 it then beats
 // split-H from this many units (measured, 16-63 units of 64 tokens, hidden

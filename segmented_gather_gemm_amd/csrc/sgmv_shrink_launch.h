@@ -59,6 +59,15 @@ struct ShrinkParams {
 constexpr int kShrinkMaxSlicesPerLaunch = 3;
 constexpr int kShrinkTokensSplitT = 64;
 
+// Split-T (64-token units, lora_A shared through LDS) once the batch has at
+// least this many 64-token units; split-H (16-token units) below, where it
+// keeps more compute units busy.  The fused shrink-expand call takes the
+// same form by the same rule, so that it reproduces the workspace-free
+// shrink's sums.
+#ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS
+#define SGMV_SHRINK_SPLIT_T_MIN_UNITS 64
+#endif
+
 // Hidden steps (32 wide) per pipeline block.  Split-H: as many as keep about
 // 64 registers of loads in flight per block.  Split-T: the block's lora_A
 // tiles (tiles x steps KiB, two buffers) fit 64 KiB of LDS; the step count

@@ -596,6 +596,35 @@ def fused_gate_up(seed: int = 0) -> FusedWorkload:
                          "bf16", base.start, base.lens, base.idx, 1.0, False, K, L, seed)
 
 
+def fused_q_proj(seed: int = 0) -> FusedWorkload:
+    """Fused q_proj LoRA delta on a short prefill batch: the 8 segments of
+    llama7b_q_proj (lengths uniform in [64, 512], indices uniform in
+    {-1, 0..3}); hidden 4096 -> rank 16 -> one 4096-wide slice; 4 adapters;
+    bf16 throughout; accumulate onto the prior output."""
+    base = llama7b_q_proj(seed)
+    rng = np.random.default_rng(seed + 2000)
+    H, K, L = 4096, 16, 4
+    sl = ((0, 4096),)
+    x, la, lb, out0 = _fused_parts(rng, base.T, H, K, L, sl, 4096, "bf16", "bf16", "bf16")
+    return FusedWorkload("fused_q_proj", x, "bf16", la, lb, "bf16", [o for o, _ in sl], out0,
+                         "bf16", base.start, base.lens, base.idx, 1.0, True, K, L, seed)
+
+
+def fused_decode_qkv(seed: int = 0) -> FusedWorkload:
+    """Fused QKV LoRA delta on a decode step: 256 one-token segments (the
+    per-token layout of bgmv_decode), indices uniform in {-1, 0..31};
+    hidden 4096 -> rank 16 -> Q [0, 4096), K [4096, 5120), V [5120, 6144);
+    32 adapters; bf16 throughout; accumulate onto the prior output."""
+    rng = np.random.default_rng(seed)
+    T, H, K, L = 256, 4096, 16, 32
+    idx = rng.integers(-1, L, size=T).astype(np.int64)
+    lens = np.ones(T, dtype=np.int64)
+    x, la, lb, out0 = _fused_parts(rng, T, H, K, L, QKV_SLICES, 6144, "bf16", "bf16", "bf16")
+    return FusedWorkload("fused_decode_qkv", x, "bf16", la, lb, "bf16",
+                         [o for o, _ in QKV_SLICES], out0, "bf16", exclusive_cumsum(lens), lens,
+                         idx, 1.0, True, K, L, seed)
+
+
 def fused_custom(lens: Sequence[int], idx: Sequence[int], *, H: int, K: int, L: int,
                  slices: Sequence[tuple], H_out: int, x_dtype: str = "bf16",
                  w_dtype: str = "bf16", out_dtype: str = "bf16", add: bool = False,
@@ -620,4 +649,6 @@ def fused_custom(lens: Sequence[int], idx: Sequence[int], *, H: int, K: int, L: 
 FUSED_WORKLOADS: Dict[str, Callable[..., FusedWorkload]] = {
     "fused_qkv": fused_qkv,
     "fused_gate_up": fused_gate_up,
+    "fused_q_proj": fused_q_proj,
+    "fused_decode_qkv": fused_decode_qkv,
 }

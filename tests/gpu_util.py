@@ -321,8 +321,8 @@ def assert_fused_parity(wl, cand_bits, exact=False):
     projection differs from the exact one by at most e_k (summation of H
     exact products in any order and grouping in which no product meets more
     than d = 32 + ceil(H / 32) + 8 roundings -- the fused kernel runs the
-    split-T MFMA contraction, see shrink_sum_depth -- then the scale's
-    rounding), so its
+    split-T or split-H MFMA contraction, see shrink_sum_depth -- then the
+    scale's rounding), so its
     rounding to the weight dtype can land at most delta_k from the oracle's;
     atol and rtol cover the expand's own fp32 sums and final rounding.
     Returns the number of values compared."""

@@ -85,6 +85,55 @@ def test_fused_bit_identical_to_two_calls(K, slices, dts, add):
     assert assert_fused_parity(wl, fused) > 0
 
 
+# Below 64 units of 64 tokens the shrink takes its 16-token (split-H) form,
+# and so does the fused call: its 16-row units, each expanded over one of
+# several column groups, reproduce the workspace-free two calls bit for bit.
+SMALL_CASES = [
+    # few units, 16 column tiles: one column group per tile
+    (16, [(0, 4096)], ("bf16", "bf16", "bf16"), True, [20, 7, 33], [0, 1, -1], 1.0),
+    # QKV-like, 6 column tiles over three slices
+    (32, [(0, 1024), (1024, 256), (1280, 256)], ("bf16", "bf16", "bf16"), True, LENS, IDX, 1.0),
+    (64, [(0, 2048), (2048, 2048)], ("f16", "f16", "f32"), False, LENS, IDX, 0.5),
+    (128, [(0, 520)], ("f32", "bf16", "bf16"), True, LENS, IDX, 1.0),
+    (8, [(0, 40), (40, 40), (80, 40)], ("f16", "f16", "bf16"), True, LENS, IDX, 2.0),
+    (24, [(8, 264)], ("f32", "f16", "f16"), False, LENS, IDX, 1.0),
+    # more units than compute units: one column group each
+    (16, [(0, 512), (512, 256)], ("bf16", "bf16", "bf16"), True, [1000, 1500, 3, 900],
+     [2, 0, 1, -1], 1.0),
+    # a decode step: one-token segments
+    (16, [(0, 1024), (1024, 256)], ("bf16", "bf16", "bf16"), True, [1] * 200,
+     [(i * 7) % 5 - 1 for i in range(200)], 1.0),
+]
+
+
+@pytest.mark.parametrize("K,slices,dts,add,lens,idx,scale", SMALL_CASES)
+def test_fused_small_batches_bit_identical_to_two_calls(K, slices, dts, add, lens, idx, scale):
+    x_dt, w_dt, o_dt = dts
+    H_out = max(o + n for o, n in slices) + 8
+    wl = W.fused_custom(lens, idx, H=1000 if K != 16 else 4096, K=K, L=5, slices=slices,
+                        H_out=H_out, x_dtype=x_dt, w_dtype=w_dt, out_dtype=o_dt, add=add,
+                        scale=scale, seed=K + len(slices) + len(lens))
+    assert -(-wl.T // 64) < 64
+    df = DeviceFused(wl)
+    fused = to_host_bits(df.run())
+    _, two = df.run_two()
+    assert np.array_equal(fused, to_host_bits(two)), "fused call differs from shrink + expand"
+    assert assert_fused_parity(wl, fused) > 0
+
+
+@pytest.mark.parametrize("name", ["fused_q_proj", "fused_decode_qkv"])
+def test_fused_small_named_workloads(name):
+    """The short-prefill and decode workloads: equal to the two-call path bit
+    for bit and within the fused tolerance of the oracle over every
+    element."""
+    wl = W.FUSED_WORKLOADS[name](0)
+    df = DeviceFused(wl)
+    fused = to_host_bits(df.run())
+    _, two = df.run_two()
+    assert np.array_equal(fused, to_host_bits(two)), "fused call differs from shrink + expand"
+    assert assert_fused_parity(wl, fused) > 0
+
+
 def test_fused_edge_layouts():
     # all -1, then fewer tokens than one unit, then a gap-and-order layout
     wl = W.fused_custom([5, 7], [-1, -1], H=64, K=16, L=2, slices=[(0, 64)], H_out=64, seed=1)
