@@ -330,11 +330,10 @@ __global__ __launch_bounds__(kThreads) void fused_shrink_expand(const FusedParam
 // shrink's unit) and a work item is a unit and one of G column groups
 // (contiguous ranges of the 256-column tiles; G from p.item_target and the
 // unit count), so that a batch of few units still spreads its expansion
-// over the chip.  Phase 1 is the
-// split-H contraction (each item of a unit computes it; a workgroup whose
-// consecutive items share a unit computes it once); phase 2 sweeps the
-// item's column group.  Items of one unit are adjacent, so they run on one
-// XCD and share its L2 for the unit's inputs and lora_A rows.
+// over the chip.  Phase 1 is the split-H contraction (each item of a unit
+// computes it); phase 2 sweeps the item's column group.  Items of one unit
+// are adjacent, so they run on one XCD and share its L2 for the unit's
+// inputs and lora_A rows.
 template <int XD, int WD, int OD, bool ADD, int K16, int NS>
 __global__ __launch_bounds__(kThreads) void fused_split_h(const FusedParams p) {
   using Core = SplitHCore<XD, WD, K16, NS>;
@@ -363,22 +362,23 @@ __global__ __launch_bounds__(kThreads) void fused_split_h(const FusedParams p) {
   ex.clear_rank_tail();
   const int32_t tiles = p.total_tiles;
   int b = last_at_most(tab.tile_start, p.batches + 1, (int32_t)(it / G));
-  uint32_t have = 0xFFFFFFFFu;  // unit whose projection y_lds holds
   for (; it < it_end; ++it) {
     const uint32_t u = it / G, cg = it % G;
     while (uniform(tab.tile_start[b + 1]) <= (int32_t)u) ++b;
     const ShrinkUnit<NS> su = shrink_unit<NS>(p, tab, b, u, kTileRows);
-    if (u != have) {
-      // Phase 1: the four waves' partial sums added in wave order (the
-      // reduction's first barrier orders the previous item's reads of
-      // y_lds before these writes), scaled and rounded into y_lds.
+    // Phase 1: the four waves' partial sums added in wave order (the
+    // reduction's first barrier orders the previous item's reads of y_lds
+    // before these writes), scaled and rounded into y_lds.  With several
+    // column groups per unit every workgroup has one item (the host caps
+    // p.item_target at the grid), so no projection is ever recomputed on one
+    // workgroup.
+    {
       f32x4 acc[Core::kT];
       core.run(su, acc, p.steps);
       core.reduce(acc, [&](int i, f32x4 v) __attribute__((always_inline)) {
         ex.put(i / K16, i % K16, core.j, v * p.scale);
       });
       __syncthreads();
-      have = u;
     }
     // Phase 2: column tiles [cg tiles / G, (cg + 1) tiles / G).
     const int32_t lo = (int32_t)(((int64_t)cg * tiles) / G);

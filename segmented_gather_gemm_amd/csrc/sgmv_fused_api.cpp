@@ -214,18 +214,17 @@ sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice*
   // (the device sizes the groups from the actual unit count).
   const int64_t rows = split_h ? kTileRows : kFusedTokens;
   const int64_t units = (x.rows + rows - 1) / rows + (batches < x.rows ? batches : x.rows);
-  int64_t want = units;
-  if (split_h) {
-    // one item per compute unit (measured on fused_q_proj / fused_decode_qkv:
-    // two per compute unit double the projections a compute unit runs and
-    // lose 20-25%; one column group per unit loses 30% on fused_q_proj)
-    p.item_target = cus;
-    if (want < p.item_target) want = p.item_target;
-  }
+  // One item per compute unit (measured on fused_q_proj / fused_decode_qkv:
+  // two per compute unit double the projections a compute unit runs and
+  // lose 20-25%; one column group per unit loses 30% on fused_q_proj).
+  const int64_t want = split_h && units < cus ? cus : units;
   int64_t grid = want < capacity ? want : capacity;
   if (grid > 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   p.grid = (int32_t)grid;
+  // At most the grid: whenever a unit has several column groups, every
+  // workgroup then takes at most one item.
+  p.item_target = (int32_t)(grid < cus ? grid : cus);
   p.cus = cus;
   void* args[] = {&p};
   e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);

@@ -101,13 +101,18 @@ def test_shrink_balanced_graph_replays_match_eager():
             assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("add", [False, True])
-def test_fused_graph_replays_match_eager(add):
-    """sgmv_fused_shrink_expand captured once and replayed."""
+@pytest.mark.parametrize("add,large", [(False, False), (True, False), (True, True)])
+def test_fused_graph_replays_match_eager(add, large):
+    """sgmv_fused_shrink_expand captured once and replayed: a short batch
+    (the 16-row form) and, with ``large``, a batch of more than 64 units of
+    64 tokens (the 64-row form)."""
     import torch
     from gpu_util import DeviceFused, assert_fused_parity
-    wl = W.fused_custom([90, 3, 0, 150, 64, 1], [1, 0, 1, -1, 2, 0], H=512, K=32, L=3,
+    lens = [90, 3, 0, 150, 64, 1] + ([2000, 2100] if large else [])
+    idx = [1, 0, 1, -1, 2, 0] + ([2, 1] if large else [])
+    wl = W.fused_custom(lens, idx, H=512, K=32, L=3,
                         slices=[(0, 256), (256, 128), (384, 128)], H_out=520, add=add, seed=33)
+    assert (-(-wl.T // 64) >= 64) == large
     df = DeviceFused(wl)
     eager = to_host_bits(df.run())
     assert assert_fused_parity(wl, eager) > 0
