@@ -304,7 +304,10 @@ typedef struct {
  * shrink's two forms by the shrink's rule: from 64 units of 64 tokens,
  * 64-row units that each expand over every column; below (short prefill
  * and decode batches), 16-row units, each expanded in column groups over
- * about one work item per compute unit.
+ * about one work item per compute unit.  Measured on MI355X, the call
+ * beats the two calls for ranks up to 32 below 64 units of 64 tokens and
+ * loses elsewhere (each unit reads its adapter's lora_B once per 16 or 64
+ * rows, where the expand reuses it for up to 512): choose it there.
  *
  * inputs        device (total_tokens, hidden) f16/bf16/f32; read only.
  * slices        host array of 1..SGMV_MAX_FUSED_SLICES descriptors, read
