@@ -17,29 +17,34 @@
 // sgmv_shrink_multi_slice into weight-dtype outputs followed by
 // sgmv_expand_multi_slice computes, without storing y.
 //
-// Design (MI355X-first).  A work unit is a 64-row tile of one segment, the
-// split-T shrink's unit.  Phase 1 runs the split-T contraction over the
-// whole hidden dimension (SplitTCore: coalesced input and lora_A loads
-// staged through LDS, MFMAs with lora_A rows as the A operand) and writes
-// the unit's projected rows, scaled and rounded as the shrink stores them,
-// into LDS in the expand's operand layout.  Phase 2 sweeps every 256-column
-// tile of every slice: each wave owns 64 columns, holds their lora_B rows
-// in VGPRs (the A operand, rows permuted as in the expand so that each lane
-// ends with 8 consecutive columns of one token), reads the projected rows
-// from LDS as the B operand for the unit's four 16-token tiles, seeds the
-// accumulators with the prior output (add_inputs) and writes the result
-// row-wise through a per-wave LDS tile with non-temporal device-scope
-// stores -- the expand's epilogue.  The next column tile's lora_B rows and
-// prior output are loaded while the current one computes.  Each accumulator
-// sees the same MFMAs in the same order as in the split-T shrink and the
-// expand kernels, so the result equals, bit for bit, those two calls when
-// the shrink takes its split-T form.
+// Design (MI355X-first).  Two forms, taken by the shrink's own rule so that
+// each reproduces one shrink form's sums:
+//  * split-T (from 64 units of 64 tokens): a work unit is a 64-row tile of
+//    one segment.  Phase 1 runs the split-T contraction over the whole
+//    hidden dimension (SplitTCore: coalesced input and lora_A loads staged
+//    through LDS, MFMAs with lora_A rows as the A operand); phase 2 sweeps
+//    every 256-column tile of every slice;
+//  * split-H (short prefill and decode batches): a unit is a 16-row tile
+//    and a work item is a unit and one column group, about one item per
+//    compute unit.  Phase 1 runs the split-H contraction (SplitHCore: the
+//    four waves split the hidden steps and add their sums through LDS);
+//    phase 2 sweeps the item's column group.
+// Phase 1 writes the unit's projected rows, scaled and rounded as the shrink
+// stores them, into LDS in the expand's operand layout.  Phase 2
+// (FusedExpand) is the expand's: each wave owns 64 columns of a tile, holds
+// their lora_B rows in VGPRs, reads the projected rows from LDS as the B
+// operand, seeds the accumulators with the prior output (add_inputs) and
+// writes the result row-wise through a per-wave LDS tile with non-temporal
+// device-scope stores, the next tiles' lora_B rows and prior output loaded
+// while the current one computes.  Each accumulator sees the same MFMAs in
+// the same order as in the shrink and expand kernels, so the result equals,
+// bit for bit, those two calls (shrink without a workspace).
 //
-// The fused form saves the projection's round trip through memory and a
-// second launch, and lets one workgroup's projection (read-heavy) overlap
-// another's expansion (write-heavy); it re-reads each adapter's lora_B once
-// per 64-row unit (from L2), where the expand keeps a weight tile for up to
-// 512 rows.
+// The fused call saves the projection's round trip through memory and a
+// launch with its segment table and cold start; it re-reads each adapter's
+// lora_B once per unit (16 or 64 rows, from L2), where the expand keeps a
+// weight tile for up to 512 rows -- so it pays for small ranks on small
+// batches and loses where lora_B is large against a unit's output.
 #pragma once
 
 #include "sgmv_device.h"
