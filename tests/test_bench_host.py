@@ -79,3 +79,32 @@ def test_shrink_cpu_baseline():
     cpu = bench.shrink_cpu_baseline(wl, 0.05)
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["single_core_gbs"] > 0
     assert "shrink_tiny" in cpu["sample"]
+
+
+def test_fused_byte_model_hand_count():
+    # segments: 5 rows adapter 1, 7 rows index -1, 2 rows adapter 0; hidden 64
+    # bf16 -> rank 16 -> slices of 32 and 16 columns, bf16 output, accumulate:
+    # 7 active rows, 2 adapters; the projection never leaves the chip.
+    wl = W.fused_custom([5, 7, 2], [1, -1, 0], H=64, K=16, L=2, slices=[(0, 32), (32, 16)],
+                        H_out=48, add=True)
+    total, read, t_act, distinct = bench.fused_byte_model(wl)
+    assert (t_act, distinct) == (7, 2)
+    want_read = 7 * 64 * 2 + 2 * 2 * 16 * 64 * 2 + 2 * 48 * 16 * 2 + 7 * 48 * 2
+    assert read == want_read and total == want_read + 7 * 48 * 2
+
+
+def test_small_fused_workloads_follow_their_recipes():
+    # fused_q_proj: llama7b_q_proj's segments and indices, one 4096-wide slice
+    q, base = W.fused_q_proj(0), W.llama7b_q_proj(0)
+    assert np.array_equal(q.lens, base.lens) and np.array_equal(q.idx, base.idx)
+    assert (q.H, q.K, q.L, q.add, q.offsets) == (4096, 16, 4, True, [0])
+    assert [b.shape for b in q.lora_b] == [(4, 4096, 16)]
+    # fused_decode_qkv: 256 one-token segments in order, indices in -1..31
+    d = W.fused_decode_qkv(0)
+    assert d.batches == 256 and (d.lens == 1).all()
+    assert np.array_equal(d.start, np.arange(256))
+    assert d.idx.min() >= -1 and d.idx.max() <= 31 and (d.idx == -1).any()
+    assert d.offsets == [o for o, _ in W.QKV_SLICES]
+    # both stay below 64 units of 64 tokens (the fused call's 16-row form)
+    for wl in (q, d):
+        assert -(-wl.T // 64) < 64
