@@ -301,8 +301,8 @@ typedef struct {
  * even) to the output dtype; float32 inputs rounded to the weight dtype
  * first.  Rows of index -1 segments, rows outside every segment and
  * columns outside the windows are left untouched.  The call takes the
- * shrink's two forms by the shrink's rule: from 64 units of 64 tokens,
- * 64-row units that each expand over every column; below (short prefill
+ * shrink's two forms by the shrink's rule: from 64 units of 64 tokens
+ * (129 for ranks up to 16), 64-row units that each expand over every column; below (short prefill
  * and decode batches), 16-row units, each expanded in column groups over
  * about one work item per compute unit.  Measured on MI355X, the call
  * beats the two calls for ranks up to 32 below 64 units of 64 tokens and

@@ -176,9 +176,10 @@ sgmv_status sgmv_fused_shrink_expand(sgmv_matrix inputs, const sgmv_fused_slice*
   }
   // The projection's form follows the workspace-free shrink's rule (so the
   // result equals that shrink followed by the expand, bit for bit):
-  // split-T from SGMV_SHRINK_SPLIT_T_MIN_UNITS units of 64 tokens, split-H
+  // split-T from shrink_split_t_min_units(k16) units of 64 tokens, split-H
   // below.
-  const bool split_h = (x.rows + kFusedTokens - 1) / kFusedTokens < SGMV_SHRINK_SPLIT_T_MIN_UNITS;
+  const bool split_h =
+      (x.rows + kFusedTokens - 1) / kFusedTokens < shrink_split_t_min_units((int)k16);
   const void* kernel = pick_fused_kernel(x.dtype, s0.lora_a.dtype, out.dtype, add_inputs != 0,
                                          (int)k16, num_slices, split_h);
   if (!kernel) return fail(SGMV_ERR_UNSUPPORTED, "no fused kernel for this dtype combination");

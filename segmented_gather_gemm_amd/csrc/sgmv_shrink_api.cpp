@@ -292,7 +292,7 @@ sgmv_status shrink_check_and_launch(sgmv_matrix x, const sgmv_shrink_slice* slic
   int fast_per_launch = 16 / k16;
   if (fast_per_launch > kShrinkMaxSlicesPerLaunch) fast_per_launch = kShrinkMaxSlicesPerLaunch;
   const int64_t units64 = (x.rows + kShrinkTokensSplitT - 1) / kShrinkTokensSplitT;
-  const bool split_t = units64 >= SGMV_SHRINK_SPLIT_T_MIN_UNITS ||
+  const bool split_t = units64 >= shrink_split_t_min_units(k16) ||
                        (workspace && k16 >= 8 && units64 >= SGMV_SHRINK_SPLIT_T_MIN_UNITS_WIDE);
   if (clear_counters && workspace) {
     const sgmv_status st = clear_workspace_counters(workspace, stream);

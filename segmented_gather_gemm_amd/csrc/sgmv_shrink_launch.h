@@ -67,6 +67,20 @@ constexpr int kShrinkTokensSplitT = 64;
 #ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS
 #define SGMV_SHRINK_SPLIT_T_MIN_UNITS 64
 #endif
+// Ranks up to 16 (one k tile per slice; lora_A is a small share of split-H's
+// traffic): split-H stays ahead through 128 units of 64 tokens, i.e. two
+// 16-token units per compute unit (measured, hidden 4096, 1-3 slices,
+// workspace-balanced split-T: 66 units 1.06-1.31x, 128 units 1.01-1.19x in
+// favour of split-H; 160-224 units 0.61-0.93x).
+#ifndef SGMV_SHRINK_SPLIT_T_MIN_UNITS_NARROW
+#define SGMV_SHRINK_SPLIT_T_MIN_UNITS_NARROW 129
+#endif
+// Units of 64 tokens from which a batch takes split-T, by 16-row k tiles per
+// slice (a function of the rank alone, so that a multi-slice call takes its
+// single calls' form).
+constexpr int64_t shrink_split_t_min_units(int k16) {
+  return k16 == 1 ? SGMV_SHRINK_SPLIT_T_MIN_UNITS_NARROW : SGMV_SHRINK_SPLIT_T_MIN_UNITS;
+}
 
 // Hidden steps (32 wide) per pipeline block.  Split-H: as many as keep about
 // 64 registers of loads in flight per block.  Split-T: the block's lora_A

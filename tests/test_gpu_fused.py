@@ -59,8 +59,9 @@ def test_fused_integer_data_bit_exact(K, ns, dts, add):
     assert assert_fused_parity(wl, to_host_bits(df.run()), exact=True) > 0
 
 
-# From 64 units of 64 tokens the shrink takes its 64-token (split-T) form,
-# whose sums the fused kernel reproduces: the results are then identical.
+# From 64 units of 64 tokens (129 for ranks up to 16) the shrink takes its
+# 64-token (split-T) form, whose sums the fused kernel reproduces: the
+# results are then identical.
 BIG_LENS = [1500, 3, 2000, 17, 0, 900, 1, 64, 65, 130]
 BIG_IDX = [1, 0, 2, -1, 1, 0, 2, 1, -1, 0]
 
@@ -75,9 +76,10 @@ BIG_IDX = [1, 0, 2, -1, 1, 0, 2, 1, -1, 0]
 def test_fused_bit_identical_to_two_calls(K, slices, dts, add):
     x_dt, w_dt, o_dt = dts
     H_out = max(o + n for o, n in slices)
-    wl = W.fused_custom(BIG_LENS, BIG_IDX, H=512, K=K, L=3, slices=slices, H_out=H_out,
+    lens = [2 * n for n in BIG_LENS] if K <= 16 else BIG_LENS
+    wl = W.fused_custom(lens, BIG_IDX, H=512, K=K, L=3, slices=slices, H_out=H_out,
                         x_dtype=x_dt, w_dtype=w_dt, out_dtype=o_dt, add=add, seed=K)
-    assert -(-wl.T // 64) >= 64
+    assert -(-wl.T // 64) >= (129 if K <= 16 else 64)
     df = DeviceFused(wl)
     fused = to_host_bits(df.run())
     _, two = df.run_two()
@@ -85,9 +87,10 @@ def test_fused_bit_identical_to_two_calls(K, slices, dts, add):
     assert assert_fused_parity(wl, fused) > 0
 
 
-# Below 64 units of 64 tokens the shrink takes its 16-token (split-H) form,
-# and so does the fused call: its 16-row units, each expanded over one of
-# several column groups, reproduce the workspace-free two calls bit for bit.
+# Below 64 units of 64 tokens (129 for ranks up to 16) the shrink takes its
+# 16-token (split-H) form, and so does the fused call: its 16-row units,
+# each expanded over one of several column groups, reproduce the
+# workspace-free two calls bit for bit.
 SMALL_CASES = [
     # few units, 16 column tiles: one column group per tile
     (16, [(0, 4096)], ("bf16", "bf16", "bf16"), True, [20, 7, 33], [0, 1, -1], 1.0),
@@ -103,6 +106,9 @@ SMALL_CASES = [
     # a decode step: one-token segments
     (16, [(0, 1024), (1024, 256)], ("bf16", "bf16", "bf16"), True, [1] * 200,
      [(i * 7) % 5 - 1 for i in range(200)], 1.0),
+    # rank 16 between 64 and 128 units of 64 tokens (split-H up to 128)
+    (16, [(0, 512), (512, 256), (768, 256)], ("bf16", "bf16", "f32"), True,
+     [3000, 2500, 7, 1900], [1, 0, -1, 3], 1.0),
 ]
 
 
@@ -113,7 +119,7 @@ def test_fused_small_batches_bit_identical_to_two_calls(K, slices, dts, add, len
     wl = W.fused_custom(lens, idx, H=1000 if K != 16 else 4096, K=K, L=5, slices=slices,
                         H_out=H_out, x_dtype=x_dt, w_dtype=w_dt, out_dtype=o_dt, add=add,
                         scale=scale, seed=K + len(slices) + len(lens))
-    assert -(-wl.T // 64) < 64
+    assert -(-wl.T // 64) < (129 if K <= 16 else 64)
     df = DeviceFused(wl)
     fused = to_host_bits(df.run())
     _, two = df.run_two()

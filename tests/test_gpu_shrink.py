@@ -242,6 +242,22 @@ def test_shrink_multi_slice_with_a_misaligned_output_equals_single_calls():
     assert assert_shrink_parity(wl, [to_host_bits(o) for o in outs], depth=wl.H) > 0
 
 
+@pytest.mark.parametrize("slices,dts", [(1, ("bf16", "bf16", "f32")), (3, ("f16", "f16", "f16"))])
+def test_shrink_rank16_split_h_up_to_128_units(slices, dts):
+    """Ranks up to 16 keep the 16-token (split-H) form through 128 units of
+    64 tokens: 116 units here, several 16-token units per workgroup; every
+    row compared with the oracle, and integer data bit for bit."""
+    x_dt, a_dt, o_dt = dts
+    lens, idx = [3000, 2500, 7, 1900], [1, 0, -1, 2]
+    wl = W.shrink_custom(lens, idx, H=2048, K=16, L=3, slices=slices, x_dtype=x_dt,
+                         a_dtype=a_dt, out_dtype=o_dt, seed=40 + slices)
+    assert 64 < -(-wl.T // 64) < 129
+    assert run_and_check(wl) > 0
+    wi = W.shrink_custom(lens, idx, H=256, K=16, L=3, slices=slices, x_dtype=x_dt,
+                         a_dtype=a_dt, out_dtype=o_dt, values="int", seed=50 + slices)
+    assert run_and_check(wi, exact=True) > 0
+
+
 @pytest.mark.parametrize("units", [255, 256, 257])
 def test_shrink_unit_assignment_around_the_compute_unit_count(units):
     """`units` segments of 64 tokens, each one split-T unit, in a grid of about
