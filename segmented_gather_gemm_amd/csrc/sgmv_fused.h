@@ -19,11 +19,11 @@
 //
 // Design (MI355X-first).  Two forms, taken by the shrink's own rule so that
 // each reproduces one shrink form's sums:
-//  * split-T (from 64 units of 64 tokens): a work unit is a 64-row tile of
-//    one segment.  Phase 1 runs the split-T contraction over the whole
-//    hidden dimension (SplitTCore: coalesced input and lora_A loads staged
-//    through LDS, MFMAs with lora_A rows as the A operand); phase 2 sweeps
-//    every 256-column tile of every slice;
+//  * split-T (from shrink_split_t_min_units units of 64 tokens): a work
+//    unit is a 64-row tile of one segment.  Phase 1 runs the split-T
+//    contraction over the whole hidden dimension (SplitTCore: coalesced
+//    input and lora_A loads staged through LDS, MFMAs with lora_A rows as
+//    the A operand); phase 2 sweeps every 256-column tile of every slice;
 //  * split-H (short prefill and decode batches): a unit is a 16-row tile
 //    and a work item is a unit and one column group, about one item per
 //    compute unit.  Phase 1 runs the split-H contraction (SplitHCore: the
