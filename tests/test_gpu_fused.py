@@ -100,13 +100,16 @@ SMALL_CASES = [
     (128, [(0, 520)], ("f32", "bf16", "bf16"), True, LENS, IDX, 1.0),
     (8, [(0, 40), (40, 40), (80, 40)], ("f16", "f16", "bf16"), True, LENS, IDX, 2.0),
     (24, [(8, 264)], ("f32", "f16", "f16"), False, LENS, IDX, 1.0),
-    # more units than compute units: one column group each
+    # about 160 active units, more than half the compute units: one column
+    # group each
     (16, [(0, 512), (512, 256)], ("bf16", "bf16", "bf16"), True, [1000, 1500, 3, 900],
      [2, 0, 1, -1], 1.0),
     # a decode step: one-token segments
     (16, [(0, 1024), (1024, 256)], ("bf16", "bf16", "bf16"), True, [1] * 200,
      [(i * 7) % 5 - 1 for i in range(200)], 1.0),
-    # rank 16 between 64 and 128 units of 64 tokens (split-H up to 128)
+    # rank 16 between 64 and 128 units of 64 tokens (split-H up to 128):
+    # about 460 units of 16, more than the compute units, several per
+    # workgroup
     (16, [(0, 512), (512, 256), (768, 256)], ("bf16", "bf16", "f32"), True,
      [3000, 2500, 7, 1900], [1, 0, -1, 3], 1.0),
 ]
