@@ -260,3 +260,29 @@ def test_shrink_sum_depth_follows_the_kernel_choice():
                                             out_pad=4, seed=1)) == 72
     # tiny hidden sizes: never more than H
     assert shrink_sum_depth(W.shrink_custom(lens, idx, H=8, K=8, L=2, seed=1)) == 8
+
+
+FORM_PROBE = r"""
+#include <stdio.h>
+#include "sgmv_shrink_launch.h"
+int main() {
+  for (int k16 = 1; k16 <= 16; k16 *= 2)
+    printf("%d %lld\n", k16, (long long)sgmv::shrink_split_t_min_units(k16));
+  return 0;
+}
+"""
+
+
+def test_shrink_form_threshold_by_rank(tmp_path):
+    """The units of 64 tokens from which the shrink (and the fused call,
+    which follows it) takes its 64-token form: 129 for one 16-row k tile per
+    slice (ranks up to 16), 64 above -- a function of the rank alone."""
+    src = tmp_path / "form.cpp"
+    src.write_text(FORM_PROBE)
+    exe = tmp_path / "form"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    f"-I{CSRC}", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {int(a): int(b) for a, b in (line.split() for line in out.splitlines())}
+    assert got == {1: 129, 2: 64, 4: 64, 8: 64, 16: 64}
